@@ -1,0 +1,103 @@
+"""Layer shapes of the displaced-patch workloads (pure data, no arithmetic).
+
+Each entry is one UNet-layer shape on which one patch's share of a denoising
+step is computed.  The maps are split into ``P`` equal row bands; patch ``i``
+owns rows ``[i*H/P, (i+1)*H/P)``.  The graph is the order of the layer's
+steps:
+
+* ``gn``       corrected asynchronous GroupNorm
+* ``gn_silu``  the same, followed by SiLU
+* ``conv``     3x3 convolution whose halo rows come from the stale map
+* ``attn``     self-attention, queries from the fresh patch, keys/values from
+               the stale map with the fresh patch spliced in
+
+Shapes follow the SDXL-like levels the method is applied to (DistriFusion
+summary on atlas.scime.ai, "Experimental setup"; the 1024px and 3840px
+resolutions of "Key results").
+"""
+
+from dataclasses import dataclass, field
+from typing import Tuple
+
+
+@dataclass(frozen=True)
+class LayerConfig:
+    name: str
+    dtype: str            # "f32" or "bf16": storage type of activations and weights
+    B: int
+    H: int
+    W: int
+    C: int
+    G: int                # GroupNorm groups
+    P: int                # patches (row bands)
+    graph: Tuple[str, ...]
+    heads: int = 0        # attention heads (0: no attention in the graph)
+    head_dim: int = 0
+    eps: float = 1e-5
+    patch: int = 1        # the patch index a benchmark step computes
+    steps: int = 1        # denoising steps the layer test runs (1 warm-up + displaced)
+    note: str = ""
+
+    @property
+    def h(self) -> int:
+        return self.H // self.P
+
+    @property
+    def N(self) -> int:
+        return self.H * self.W
+
+    @property
+    def Nq(self) -> int:
+        return self.h * self.W
+
+    @property
+    def has_attn(self) -> bool:
+        return "attn" in self.graph
+
+    @property
+    def has_conv(self) -> bool:
+        return "conv" in self.graph
+
+    def conv_flops(self) -> float:
+        """Multiply-adds x2 of the patch's 3x3 conv (Cout = Cin = C)."""
+        if not self.has_conv:
+            return 0.0
+        return 2.0 * self.B * self.Nq * self.C * 9 * self.C
+
+    def attn_flops(self) -> float:
+        """QK^T plus PV, 2 flops per multiply-add, every (query, key) pair."""
+        if not self.has_attn:
+            return 0.0
+        return 4.0 * self.B * self.heads * self.Nq * self.N * self.head_dim
+
+    def band_bytes(self) -> int:
+        """Bytes of one activation band [B][h][W][C]."""
+        return self.B * self.Nq * self.C * (4 if self.dtype == "f32" else 2)
+
+
+CONFIGS = {
+    "c0": LayerConfig(
+        "c0", "f32", B=1, H=16, W=16, C=32, G=8, P=2,
+        graph=("gn_silu", "conv", "attn"), heads=1, head_dim=32, steps=2,
+        note="tiny block: GN+SiLU, conv3x3 32->32, 1-head attention over 256 tokens"),
+    "c1": LayerConfig(
+        "c1", "bf16", B=1, H=128, W=128, C=320, G=32, P=4,
+        graph=("gn_silu", "conv"),
+        note="SDXL level-1 conv layer at 1024px: GN+SiLU, conv3x3 320->320"),
+    "c2": LayerConfig(
+        "c2", "bf16", B=1, H=64, W=64, C=640, G=32, P=4,
+        graph=("gn", "attn", "conv"), heads=10, head_dim=64,
+        note="SDXL level-2 attention layer: GN, 10x64 attention over 4096 tokens, conv3x3 640->640"),
+    "c3": LayerConfig(
+        "c3", "bf16", B=1, H=32, W=32, C=1280, G=32, P=8,
+        graph=("gn", "attn", "conv"), heads=20, head_dim=64,
+        note="SDXL level-3 attention layer: GN, 20x64 attention over 1024 tokens, conv3x3 1280->1280"),
+    "c4a": LayerConfig(
+        "c4a", "bf16", B=1, H=480, W=480, C=320, G=32, P=8,
+        graph=("gn_silu", "conv"),
+        note="3840px conv layer: GN+SiLU, conv3x3 320->320, 60x480 bands"),
+    "c4b": LayerConfig(
+        "c4b", "bf16", B=1, H=240, W=240, C=640, G=32, P=8,
+        graph=("gn", "attn"), heads=10, head_dim=64,
+        note="3840px attention layer: GN, 10x64 attention, 7200 queries over 57600 keys"),
+}

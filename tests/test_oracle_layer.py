@@ -1,0 +1,143 @@
+"""Pins of the oracle's band splice, synchronous layer and displaced layer (CPU only).
+
+* The synchronous layer is checked against a torch composition of
+  group_norm, silu, conv2d and scaled_dot_product_attention.
+* Warm-up semantics (DistriFusion summary on atlas.scime.ai, warm-up rows of
+  "Measured effects reported in the paper"): with stale state equal to the
+  current step's, the displaced patch equals the synchronous layer's band.
+* One patch gives the plain layer.
+* With a perturbed previous step the displaced result moves by the order of
+  the perturbation: stale context is read, and only that.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from displaced_patch_parallelism_amd import synth
+from displaced_patch_parallelism_amd.configs import LayerConfig
+from tests.torch_refs import conv2d_nhwc, group_norm_nhwc, sdpa_tokens, t64
+
+GRAPHS = {
+    "gn_silu-conv-attn": ("gn_silu", "conv", "attn"),
+    "gn-attn-conv": ("gn", "attn", "conv"),
+    "gn_silu-conv": ("gn_silu", "conv"),
+    "gn-attn": ("gn", "attn"),
+}
+
+
+def small_cfg(graph, H=8, W=6, C=8, G=4, P=4, heads=2):
+    return LayerConfig("t", "f32", B=1, H=H, W=W, C=C, G=G, P=P, graph=graph,
+                       heads=heads, head_dim=C // heads)
+
+
+def params_of(cfg, inp):
+    return {"G": cfg.G, "eps": cfg.eps, "heads": cfg.heads, "convs": inp.convs}
+
+
+def torch_sync(graph, params, x):
+    h = t64(x)
+    outs = []
+    convs = iter(params["convs"])
+    for step in graph:
+        if step.startswith("gn"):
+            h = group_norm_nhwc(h, params["G"], params["eps"])
+            if step == "gn_silu":
+                h = torch.nn.functional.silu(h)
+        elif step == "conv":
+            w, b = next(convs)
+            h = conv2d_nhwc(h, w, b)
+        else:
+            B, H, W, C = h.shape
+            tok = h.reshape(B, H * W, C)
+            h = sdpa_tokens(tok, tok, tok, params["heads"]).reshape(B, H, W, C)
+        outs.append(h.numpy())
+    return outs
+
+
+def test_stale_update_bytes_and_canaries():
+    rng = np.random.default_rng(0)
+    stale = rng.standard_normal((2, 8, 3, 4)).astype(np.float32)
+    patch = rng.standard_normal((2, 2, 3, 4)).astype(np.float32)
+    out = oracle.stale_update(stale, patch, 4, 2)
+    assert out.dtype == np.float32
+    assert out[:, 4:6].tobytes() == patch.tobytes()
+    assert out[:, :4].tobytes() == stale[:, :4].tobytes()
+    assert out[:, 6:].tobytes() == stale[:, 6:].tobytes()
+    with pytest.raises(ValueError):
+        oracle.stale_update(stale, patch[:, :1], 4, 2)
+
+
+@pytest.mark.parametrize("gname", list(GRAPHS))
+def test_sync_layer_matches_torch(gname):
+    cfg = small_cfg(GRAPHS[gname])
+    inp = synth.layer_inputs(cfg, seed=1)
+    params = params_of(cfg, inp)
+    outs, state = oracle.sync_layer(cfg.graph, params, inp.x, cfg.P)
+    for a, b in zip(outs, torch_sync(cfg.graph, params, inp.x)):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+    # the state holds every band's moments and each consumer's full input map
+    assert state["stats"].shape == (cfg.P, 1, cfg.G, 2)
+    assert set(state["maps"]) == {k for k, s in enumerate(cfg.graph) if s in ("conv", "attn")}
+
+
+@pytest.mark.parametrize("gname", list(GRAPHS))
+def test_warmup_state_gives_sync_layer(gname):
+    """Stale == fresh: every patch's displaced outputs equal the sync layer's band rows."""
+    cfg = small_cfg(GRAPHS[gname])
+    inp = synth.layer_inputs(cfg, seed=2)
+    params = params_of(cfg, inp)
+    sync_outs, state = oracle.sync_layer(cfg.graph, params, inp.x, cfg.P)
+    h = cfg.h
+    for i in range(cfg.P):
+        outs, _ = oracle.displaced_layer(cfg.graph, params, inp.x[:, i * h:(i + 1) * h], state, cfg.P, i)
+        for a, b in zip(outs, sync_outs):
+            np.testing.assert_allclose(a, b[:, i * h:(i + 1) * h], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("gname", list(GRAPHS))
+def test_one_patch_is_plain_layer(gname):
+    cfg = small_cfg(GRAPHS[gname], P=1)
+    inp = synth.layer_inputs(cfg, seed=3)
+    params = params_of(cfg, inp)
+    _, prev_state = oracle.sync_layer(cfg.graph, params, inp.x_prev, 1)
+    outs, _ = oracle.displaced_layer(cfg.graph, params, inp.x, prev_state, 1, 0)
+    for a, b in zip(outs, torch_sync(cfg.graph, params, inp.x)):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("gname", list(GRAPHS))
+def test_displaced_step_reads_stale_context(gname):
+    """Previous step x' = x + 0.05 eps: results differ from sync by O(0.05), not 0 and not O(1)."""
+    cfg = small_cfg(GRAPHS[gname])
+    inp = synth.layer_inputs(cfg, seed=4)
+    params = params_of(cfg, inp)
+    _, prev = oracle.sync_layer(cfg.graph, params, inp.x_prev, cfg.P)
+    sync_outs, _ = oracle.sync_layer(cfg.graph, params, inp.x, cfg.P)
+    i, h = 1, cfg.h
+    outs, new_state = oracle.displaced_layer(cfg.graph, params, inp.x[:, i * h:(i + 1) * h], prev, cfg.P, i)
+    ref = sync_outs[-1][:, i * h:(i + 1) * h]
+    err = np.linalg.norm(outs[-1] - ref) / np.linalg.norm(ref)
+    assert 1e-4 < err < 0.2, err
+    # the new state carries the fresh band and the fresh statistics of patch i
+    np.testing.assert_array_equal(new_state["stats"][i], oracle.gn_band_stats(inp.x[:, i * h:(i + 1) * h], cfg.G))
+    for j in range(cfg.P):
+        if j != i:
+            np.testing.assert_array_equal(new_state["stats"][j], prev["stats"][j])
+    for k, m in new_state["maps"].items():
+        np.testing.assert_array_equal(m[:, :i * h], prev["maps"][k][:, :i * h])
+        np.testing.assert_array_equal(m[:, (i + 1) * h:], prev["maps"][k][:, (i + 1) * h:])
+
+
+def test_all_patches_displaced_converge_to_sync():
+    """Two steps of the c0 graph: a displaced step after a warm-up on x' stays near sync(x)."""
+    cfg = small_cfg(GRAPHS["gn_silu-conv-attn"], H=8, W=8, C=8, G=2, P=2, heads=1)
+    inp = synth.layer_inputs(cfg, seed=5)
+    params = params_of(cfg, inp)
+    _, prev = oracle.sync_layer(cfg.graph, params, inp.x_prev, cfg.P)
+    sync_outs, _ = oracle.sync_layer(cfg.graph, params, inp.x, cfg.P)
+    full = np.concatenate([oracle.displaced_layer(cfg.graph, params, inp.x[:, 4 * i:4 * i + 4], prev, 2, i)[0][-1]
+                           for i in range(2)], axis=1)
+    err = np.linalg.norm(full - sync_outs[-1]) / np.linalg.norm(sync_outs[-1])
+    assert err < 0.1

@@ -1,0 +1,38 @@
+"""The seeded input generator: rounding, determinism, distributions (CPU only)."""
+
+import numpy as np
+import torch
+
+from displaced_patch_parallelism_amd import synth
+from displaced_patch_parallelism_amd.configs import CONFIGS
+
+
+def test_bf16_round_matches_torch_rne():
+    rng = np.random.default_rng(0)
+    a = np.concatenate([rng.standard_normal(10000).astype(np.float32) * 10,
+                        np.array([1.00390625, 1.01171875, -1.00390625, 3.0e-39, 65504.0], np.float32)])
+    ours = synth.bf16_round(a)
+    ref = torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
+    assert ours.tobytes() == ref.tobytes()
+
+
+def test_same_seed_same_inputs():
+    cfg = CONFIGS["c0"]
+    a, b = synth.layer_inputs(cfg, 7), synth.layer_inputs(cfg, 7)
+    assert a.x.tobytes() == b.x.tobytes() and a.x_prev.tobytes() == b.x_prev.tobytes()
+    assert a.convs[0][0].tobytes() == b.convs[0][0].tobytes()
+    c = synth.layer_inputs(cfg, 8)
+    assert a.x.tobytes() != c.x.tobytes()
+
+
+def test_distributions():
+    cfg = CONFIGS["c1"]
+    inp = synth.layer_inputs(cfg, 0)
+    assert inp.x.shape == (1, 128, 128, 320)
+    assert abs(inp.x.mean()) < 0.01 and abs(inp.x.std() - 1) < 0.01
+    d = inp.x_prev - inp.x
+    assert abs(d.std() - 0.05) < 0.002
+    w, b = inp.convs[0]
+    assert w.shape == (320, 3, 3, 320) and b.dtype == np.float32
+    assert abs(w.std() * np.sqrt(9 * 320) - 1) < 0.02
+    assert synth.bf16_round(w).tobytes() == w.tobytes()
