@@ -1,0 +1,258 @@
+"""displaced_patch_parallelism_amd -- the displaced-patch layer hot path on MI355X.
+
+Thin ctypes binding of ``libdp.so`` (C ABI in ``include/dp.h``).  The
+functions take torch tensors on a ROCm device, check device, dtype, shape and
+contiguity, and pass raw pointers plus the current HIP stream to the library.
+Every step of the computation runs in the library's HIP kernels; there is no
+fallback: if the library is not built, or a tensor is not on a GPU, the call
+raises.
+
+Patch geometry: ``Patch(B, H, W, C, P, i)`` -- full NHWC map [B][H][W][C],
+P equal row bands, this call computes band i (rows i*H/P .. (i+1)*H/P).
+"""
+
+import ctypes
+import os
+from typing import NamedTuple, Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdp.so")
+
+DP_OK, DP_ERR_ARG, DP_ERR_UNSUPPORTED, DP_ERR_HIP = 0, 1, 2, 3
+DP_F32, DP_BF16 = 0, 1
+GN_MODES = {"corrected": 0, "local": 1, "stale": 2}
+ACTS = {None: 0, "none": 0, "silu": 1}
+
+
+class DpError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"dp status {status}: {msg}")
+        self.status = status
+
+
+class Patch(NamedTuple):
+    B: int
+    H: int
+    W: int
+    C: int
+    P: int
+    i: int
+
+    @property
+    def h(self):
+        return self.H // self.P
+
+    @property
+    def r0(self):
+        return self.i * (self.H // self.P)
+
+
+class _CPatch(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "H", "W", "C", "P", "i")]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libdp.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                               "or python -m displaced_patch_parallelism_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i32, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_float
+        pp = ctypes.POINTER(_CPatch)
+        psz = ctypes.POINTER(ctypes.c_size_t)
+        sigs = {
+            "dp_groupnorm_async_ws": [pp, i32, i32, psz],
+            "dp_groupnorm_async": [pp, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "dp_conv3x3_halo_ws": [pp, i32, i32, psz],
+            "dp_conv3x3_halo": [pp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp],
+            "dp_attention_splice_ws": [pp, i32, i32, i32, psz],
+            "dp_attention_splice": [pp, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "dp_stale_update": [pp, i32, vp, vp, vp],
+        }
+        for name, args in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        L.dp_last_error.restype = ctypes.c_char_p
+        L.dp_last_error.argtypes = []
+        L.dp_version.restype = ctypes.c_char_p
+        L.dp_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _check(status):
+    if status != DP_OK:
+        raise DpError(status, lib().dp_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return DP_BF16
+    if t.dtype == torch.float32:
+        return DP_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t, name, shape=None, dtype=None, device=None):
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a ROCm GPU device (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream(device):
+    return _torch().cuda.current_stream(device).cuda_stream
+
+
+def _cpatch(p: Patch):
+    return ctypes.byref(_CPatch(*[int(v) for v in p]))
+
+
+_ws_cache = {}
+
+
+def _workspace(nbytes, device, ws):
+    """Caller workspace if given and large enough, else a cached per-device buffer."""
+    torch = _torch()
+    if nbytes == 0:
+        return None, 0
+    if ws is not None:
+        return ws.data_ptr(), ws.numel() * ws.element_size()
+    key = (device.type, device.index)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _ws_cache[key] = buf
+    return buf.data_ptr(), buf.numel()
+
+
+def workspace_bytes(kind, patch: Patch, dtype_code, *args):
+    """Bytes of workspace an entry point needs ("groupnorm", "conv", "attention")."""
+    out = ctypes.c_size_t(0)
+    fn = {"groupnorm": lib().dp_groupnorm_async_ws, "conv": lib().dp_conv3x3_halo_ws,
+          "attention": lib().dp_attention_splice_ws}[kind]
+    _check(fn(_cpatch(patch), dtype_code, *args, ctypes.byref(out)))
+    return out.value
+
+
+def dp_stale_update(patch: Patch, x_patch, stale):
+    """stale[:, r0:r0+h] = x_patch, bit for bit (in place)."""
+    p = Patch(*patch)
+    dt = _dtype_code(stale)
+    _ptr(stale, "stale", (p.B, p.H, p.W, p.C))
+    _ptr(x_patch, "x_patch", (p.B, p.h, p.W, p.C), stale.dtype, stale.device)
+    _check(lib().dp_stale_update(_cpatch(p), dt, x_patch.data_ptr(), stale.data_ptr(), _stream(stale.device)))
+    return stale
+
+
+def dp_stats_update(P, i, fresh_stats, table):
+    """Copy one patch's GroupNorm moments [B][G][2] into slot i of the [P][B][G][2] table."""
+    torch = _torch()
+    if table.dtype != torch.float32 or fresh_stats.dtype != torch.float32:
+        raise TypeError("statistics are float32")
+    n = fresh_stats.numel()
+    if table.numel() != P * n:
+        raise ValueError("table must hold P slots of the statistics shape")
+    p = Patch(1, P, 1, n, P, i)
+    return dp_stale_update(p, fresh_stats.reshape(1, 1, 1, n), table.view(1, P, 1, n))
+
+
+def dp_groupnorm_async(patch: Patch, x_patch, G, stale_stats=None, eps=1e-5, mode="corrected",
+                       act=None, gamma=None, beta=None, fresh_stats_out=None, y_patch=None,
+                       stats_only=False, ws=None):
+    """Corrected asynchronous GroupNorm of patch i; returns (y_patch, fresh_stats_out)."""
+    torch = _torch()
+    p = Patch(*patch)
+    dt = _dtype_code(x_patch)
+    dev = x_patch.device
+    _ptr(x_patch, "x_patch", (p.B, p.h, p.W, p.C))
+    if fresh_stats_out is None:
+        fresh_stats_out = torch.empty((p.B, G, 2), dtype=torch.float32, device=dev)
+    if y_patch is None and not stats_only:
+        y_patch = torch.empty_like(x_patch)
+    _ptr(fresh_stats_out, "fresh_stats_out", (p.B, G, 2), torch.float32, dev)
+    _ptr(y_patch, "y_patch", (p.B, p.h, p.W, p.C), x_patch.dtype, dev)
+    _ptr(stale_stats, "stale_stats", (p.P, p.B, G, 2), torch.float32, dev)
+    _ptr(gamma, "gamma", (p.C,), torch.float32, dev)
+    _ptr(beta, "beta", (p.C,), torch.float32, dev)
+    need = workspace_bytes("groupnorm", p, dt, G)
+    wptr, wbytes = _workspace(need, dev, ws)
+    gp = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    _check(lib().dp_groupnorm_async(
+        _cpatch(p), dt, G, float(eps), GN_MODES[mode], ACTS[act], x_patch.data_ptr(), gp(stale_stats),
+        gp(gamma), gp(beta), fresh_stats_out.data_ptr(), gp(y_patch), wptr, wbytes, _stream(dev)))
+    return y_patch, fresh_stats_out
+
+
+def dp_conv3x3_halo(patch: Patch, x_patch, x_stale, w, bias=None, y_patch=None, ws=None):
+    """3x3 conv of patch i with stale halo rows; returns y_patch [B][h][W][Cout]."""
+    torch = _torch()
+    p = Patch(*patch)
+    dt = _dtype_code(x_patch)
+    dev = x_patch.device
+    cout = int(w.shape[0])
+    _ptr(x_patch, "x_patch", (p.B, p.h, p.W, p.C))
+    _ptr(x_stale, "x_stale", (p.B, p.H, p.W, p.C), x_patch.dtype, dev)
+    _ptr(w, "w", (cout, 3, 3, p.C), x_patch.dtype, dev)
+    _ptr(bias, "bias", (cout,), torch.float32, dev)
+    if y_patch is None:
+        y_patch = torch.empty((p.B, p.h, p.W, cout), dtype=x_patch.dtype, device=dev)
+    _ptr(y_patch, "y_patch", (p.B, p.h, p.W, cout), x_patch.dtype, dev)
+    need = workspace_bytes("conv", p, dt, cout)
+    wptr, wbytes = _workspace(need, dev, ws)
+    _check(lib().dp_conv3x3_halo(_cpatch(p), dt, cout, x_patch.data_ptr(), x_stale.data_ptr(), w.data_ptr(),
+                                 None if bias is None else bias.data_ptr(), y_patch.data_ptr(), wptr, wbytes,
+                                 _stream(dev)))
+    return y_patch
+
+
+def dp_attention_splice(patch: Patch, heads, q_patch, k_patch, v_patch, k_stale, v_stale, o_patch=None,
+                        scale=0.0, ws=None):
+    """Attention of patch i's queries over spliced K/V; tensors are token-major [B][tokens][C]."""
+    torch = _torch()
+    p = Patch(*patch)
+    dt = _dtype_code(q_patch)
+    dev = q_patch.device
+    d = p.C // heads
+    band = (p.B, p.h * p.W, p.C)
+    full = (p.B, p.H * p.W, p.C)
+    for t, n, s in ((q_patch, "q_patch", band), (k_patch, "k_patch", band), (v_patch, "v_patch", band),
+                    (k_stale, "k_stale", full), (v_stale, "v_stale", full)):
+        _ptr(t, n, s, q_patch.dtype, dev)
+    if o_patch is None:
+        o_patch = torch.empty(band, dtype=q_patch.dtype, device=dev)
+    _ptr(o_patch, "o_patch", band, q_patch.dtype, dev)
+    need = workspace_bytes("attention", p, dt, heads, d)
+    wptr, wbytes = _workspace(need, dev, ws)
+    _check(lib().dp_attention_splice(_cpatch(p), dt, heads, d, float(scale), q_patch.data_ptr(),
+                                     k_patch.data_ptr(), v_patch.data_ptr(), k_stale.data_ptr(),
+                                     v_stale.data_ptr(), o_patch.data_ptr(), wptr, wbytes, _stream(dev)))
+    return o_patch
+
+
+def version():
+    return lib().dp_version().decode()

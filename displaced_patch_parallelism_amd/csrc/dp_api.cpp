@@ -1,0 +1,284 @@
+// Host entry points of the C ABI declared in include/dp.h: argument
+// validation, plan selection and kernel dispatch.  Validation touches no HIP
+// API, so a rejected call never initialises the runtime or enqueues work.
+
+#include "dp.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "dp_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+dp_status fail(dp_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+dp_status ok() {
+    g_err.clear();
+    return DP_OK;
+}
+
+dp_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(DP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+size_t elem_size(dp_dtype dt) { return dt == DP_BF16 ? 2 : 4; }
+
+// [a, a+na) and [b, b+nb) intersect
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+// Validates the patch geometry; fills g.
+dp_status check_patch(const dp_patch* p, dp_dtype dt, dp::Geom* g) {
+    if (!p) return fail(DP_ERR_ARG, "patch descriptor is NULL");
+    if (dt != DP_F32 && dt != DP_BF16) return fail(DP_ERR_ARG, "unknown dtype %d", (int)dt);
+    if (p->B < 1 || p->H < 1 || p->W < 1 || p->C < 1 || p->P < 1)
+        return fail(DP_ERR_ARG, "B, H, W, C and P must be >= 1 (got B=%d H=%d W=%d C=%d P=%d)",
+                    p->B, p->H, p->W, p->C, p->P);
+    if (p->H % p->P != 0) return fail(DP_ERR_ARG, "H=%d is not divisible by P=%d", p->H, p->P);
+    if (p->i < 0 || p->i >= p->P) return fail(DP_ERR_ARG, "patch index i=%d not in [0, %d)", p->i, p->P);
+    const int64_t elems = (int64_t)p->B * p->H * p->W * p->C;
+    if (elems > ((int64_t)1 << 40)) return fail(DP_ERR_ARG, "map too large");
+    g->B = p->B; g->H = p->H; g->W = p->W; g->C = p->C; g->P = p->P; g->i = p->i;
+    g->h = p->H / p->P;
+    g->r0 = p->i * g->h;
+    return DP_OK;
+}
+
+#define DP_TRY(expr)                      \
+    do {                                  \
+        dp_status _s = (expr);            \
+        if (_s != DP_OK) return _s;       \
+    } while (0)
+
+#define DP_NEED(ptr, name)                                                  \
+    do {                                                                    \
+        if (!(ptr)) return fail(DP_ERR_ARG, "%s is NULL", name);            \
+        if (!aligned16(ptr)) return fail(DP_ERR_ARG, "%s is not 16-byte aligned", name); \
+    } while (0)
+
+#define DP_OPT(ptr, name)                                                   \
+    do {                                                                    \
+        if ((ptr) && !aligned16(ptr))                                       \
+            return fail(DP_ERR_ARG, "%s is not 16-byte aligned", name);     \
+    } while (0)
+
+// ---- GroupNorm -----------------------------------------------------------
+
+dp_status check_gn(const dp_patch* p, dp_dtype dt, int32_t G, dp::Geom* g) {
+    DP_TRY(check_patch(p, dt, g));
+    if (G < 1 || g->C % G != 0) return fail(DP_ERR_ARG, "C=%d is not divisible by G=%d", g->C, G);
+    const int vec = dt == DP_BF16 ? 8 : 4;
+    if (g->C % vec != 0)
+        return fail(DP_ERR_UNSUPPORTED, "GroupNorm needs C %% %d == 0 for this dtype (C=%d)", vec, g->C);
+    if (g->C > 8192) return fail(DP_ERR_UNSUPPORTED, "GroupNorm supports C <= 8192 (C=%d)", g->C);
+    return DP_OK;
+}
+
+// ---- conv ------------------------------------------------------------------
+
+dp_status check_conv(const dp_patch* p, dp_dtype dt, int32_t Cout, dp::Geom* g) {
+    DP_TRY(check_patch(p, dt, g));
+    if (Cout < 1) return fail(DP_ERR_ARG, "Cout=%d must be >= 1", Cout);
+    if (dt == DP_BF16 && (g->C % 64 != 0 || Cout % 32 != 0))
+        return fail(DP_ERR_UNSUPPORTED, "bf16 conv needs Cin %% 64 == 0 and Cout %% 32 == 0 (Cin=%d Cout=%d)",
+                    g->C, Cout);
+    return DP_OK;
+}
+
+// ---- attention ---------------------------------------------------------------
+
+dp_status check_attn(const dp_patch* p, dp_dtype dt, int32_t heads, int32_t head_dim, dp::Geom* g) {
+    DP_TRY(check_patch(p, dt, g));
+    if (heads < 1 || head_dim < 1) return fail(DP_ERR_ARG, "heads and head_dim must be >= 1");
+    if ((int64_t)heads * head_dim != g->C)
+        return fail(DP_ERR_ARG, "heads*head_dim=%d does not equal C=%d", heads * head_dim, g->C);
+    if (dt == DP_BF16 && head_dim != 64)
+        return fail(DP_ERR_UNSUPPORTED, "bf16 attention is built for head_dim 64 (got %d)", head_dim);
+    if (dt == DP_F32 && !(head_dim == 4 || head_dim == 8 || head_dim == 16 || head_dim == 32 ||
+                          head_dim == 64 || head_dim == 128))
+        return fail(DP_ERR_UNSUPPORTED, "f32 attention is built for head_dim in {4,8,16,32,64,128} (got %d)",
+                    head_dim);
+    return DP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dp_last_error(void) { return g_err.c_str(); }
+
+const char* dp_version(void) { return "dp 0.1 (gfx950)"; }
+
+dp_status dp_stale_update(const dp_patch* p, dp_dtype dtype, const void* x_patch, void* stale,
+                          hipStream_t stream) {
+    dp::Geom g;
+    DP_TRY(check_patch(p, dtype, &g));
+    DP_NEED(x_patch, "x_patch");
+    DP_NEED(stale, "stale");
+    const size_t es = elem_size(dtype);
+    const size_t band_bytes = (size_t)g.B * g.band_tokens() * g.C * es;
+    const size_t map_bytes = (size_t)g.B * g.map_tokens() * g.C * es;
+    const char* band_i = (const char*)stale + (size_t)g.r0 * g.W * g.C * es;
+    if (g.B == 1 && x_patch == (const void*)band_i) return ok();  // already in place
+    if (overlaps(x_patch, band_bytes, stale, map_bytes))
+        return fail(DP_ERR_ARG, "x_patch overlaps the stale map (other than being band i itself)");
+    return hip_status(dp::launch_band_copy(x_patch, stale, g, es, stream), "dp_stale_update launch");
+}
+
+dp_status dp_groupnorm_async_ws(const dp_patch* p, dp_dtype dtype, int32_t G, size_t* ws_bytes) {
+    dp::Geom g;
+    DP_TRY(check_gn(p, dtype, G, &g));
+    if (!ws_bytes) return fail(DP_ERR_ARG, "ws_bytes is NULL");
+    *ws_bytes = dp::plan_groupnorm(g, G, dtype == DP_BF16).ws_bytes;
+    return ok();
+}
+
+dp_status dp_groupnorm_async(const dp_patch* p, dp_dtype dtype, int32_t G, float eps, dp_gn_mode mode,
+                             dp_act act, const void* x_patch, const float* stale_stats,
+                             const float* gamma, const float* beta, float* fresh_stats_out,
+                             void* y_patch, void* ws, size_t ws_bytes, hipStream_t stream) {
+    dp::Geom g;
+    DP_TRY(check_gn(p, dtype, G, &g));
+    if (!(eps > 0.0f) || !std::isfinite(eps)) return fail(DP_ERR_ARG, "eps must be a positive finite number");
+    if (mode != DP_GN_CORRECTED && mode != DP_GN_LOCAL && mode != DP_GN_STALE)
+        return fail(DP_ERR_ARG, "unknown GroupNorm mode %d", (int)mode);
+    if (act != DP_ACT_NONE && act != DP_ACT_SILU) return fail(DP_ERR_ARG, "unknown activation %d", (int)act);
+    DP_NEED(x_patch, "x_patch");
+    DP_OPT(gamma, "gamma");
+    DP_OPT(beta, "beta");
+    DP_OPT(fresh_stats_out, "fresh_stats_out");
+    DP_OPT(y_patch, "y_patch");
+    if (!y_patch && !fresh_stats_out)
+        return fail(DP_ERR_ARG, "nothing to compute: y_patch and fresh_stats_out are both NULL");
+    if (y_patch && mode != DP_GN_LOCAL && !stale_stats)
+        return fail(DP_ERR_ARG, "stale_stats is NULL (needed by this GroupNorm mode)");
+    DP_OPT(stale_stats, "stale_stats");
+    const dp::GnPlan plan = dp::plan_groupnorm(g, G, dtype == DP_BF16);
+    if (ws_bytes < plan.ws_bytes)
+        return fail(DP_ERR_ARG, "workspace too small: %zu < %zu bytes", ws_bytes, plan.ws_bytes);
+    DP_NEED(ws, "ws");
+    const size_t es = elem_size(dtype);
+    const size_t band_bytes = (size_t)g.B * g.band_tokens() * g.C * es;
+    const size_t stats_bytes = (size_t)g.B * G * 2 * sizeof(float);
+    const size_t table_bytes = (size_t)g.P * stats_bytes;
+    if (y_patch && y_patch != x_patch && overlaps(y_patch, band_bytes, x_patch, band_bytes))
+        return fail(DP_ERR_ARG, "y_patch partially overlaps x_patch");
+    if (y_patch && (overlaps(y_patch, band_bytes, stale_stats, table_bytes) ||
+                    overlaps(y_patch, band_bytes, ws, plan.ws_bytes)))
+        return fail(DP_ERR_ARG, "y_patch overlaps the statistics table or the workspace");
+    if (fresh_stats_out && (overlaps(fresh_stats_out, stats_bytes, x_patch, band_bytes) ||
+                            overlaps(fresh_stats_out, stats_bytes, stale_stats, table_bytes) ||
+                            overlaps(fresh_stats_out, stats_bytes, y_patch, band_bytes) ||
+                            overlaps(fresh_stats_out, stats_bytes, ws, plan.ws_bytes)))
+        return fail(DP_ERR_ARG, "fresh_stats_out overlaps an input, y_patch or the workspace");
+    if (overlaps(ws, plan.ws_bytes, x_patch, band_bytes) || overlaps(ws, plan.ws_bytes, stale_stats, table_bytes))
+        return fail(DP_ERR_ARG, "workspace overlaps an input");
+    return hip_status(dp::launch_groupnorm(g, plan, dtype == DP_BF16, G, eps, (int)mode, (int)act, x_patch,
+                                           stale_stats, gamma, beta, fresh_stats_out, y_patch, ws, stream),
+                      "dp_groupnorm_async launch");
+}
+
+dp_status dp_conv3x3_halo_ws(const dp_patch* p, dp_dtype dtype, int32_t Cout, size_t* ws_bytes) {
+    dp::Geom g;
+    DP_TRY(check_conv(p, dtype, Cout, &g));
+    if (!ws_bytes) return fail(DP_ERR_ARG, "ws_bytes is NULL");
+    *ws_bytes = dp::plan_conv(g, Cout, dtype == DP_BF16).ws_bytes;
+    return ok();
+}
+
+dp_status dp_conv3x3_halo(const dp_patch* p, dp_dtype dtype, int32_t Cout, const void* x_patch,
+                          const void* x_stale, const void* w, const float* bias, void* y_patch,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+    dp::Geom g;
+    DP_TRY(check_conv(p, dtype, Cout, &g));
+    DP_NEED(x_patch, "x_patch");
+    DP_NEED(x_stale, "x_stale");
+    DP_NEED(w, "w");
+    DP_OPT(bias, "bias");
+    DP_NEED(y_patch, "y_patch");
+    const dp::ConvPlan plan = dp::plan_conv(g, Cout, dtype == DP_BF16);
+    if (ws_bytes < plan.ws_bytes)
+        return fail(DP_ERR_ARG, "workspace too small: %zu < %zu bytes", ws_bytes, plan.ws_bytes);
+    if (plan.ws_bytes) DP_NEED(ws, "ws");
+    const size_t es = elem_size(dtype);
+    const size_t in_band = (size_t)g.B * g.band_tokens() * g.C * es;
+    const size_t in_map = (size_t)g.B * g.map_tokens() * g.C * es;
+    const size_t out_band = (size_t)g.B * g.band_tokens() * Cout * es;
+    const size_t w_bytes = (size_t)Cout * 9 * g.C * es;
+    if (overlaps(y_patch, out_band, x_patch, in_band) || overlaps(y_patch, out_band, x_stale, in_map) ||
+        overlaps(y_patch, out_band, w, w_bytes) || overlaps(y_patch, out_band, bias, Cout * sizeof(float)) ||
+        overlaps(y_patch, out_band, ws, plan.ws_bytes))
+        return fail(DP_ERR_ARG, "y_patch overlaps an input or the workspace");
+    if (plan.ws_bytes && (overlaps(ws, plan.ws_bytes, x_patch, in_band) || overlaps(ws, plan.ws_bytes, x_stale, in_map) ||
+                          overlaps(ws, plan.ws_bytes, w, w_bytes)))
+        return fail(DP_ERR_ARG, "workspace overlaps an input");
+    return hip_status(dp::launch_conv(g, plan, dtype == DP_BF16, Cout, x_patch, x_stale, w, bias, y_patch, ws,
+                                      stream),
+                      "dp_conv3x3_halo launch");
+}
+
+dp_status dp_attention_splice_ws(const dp_patch* p, dp_dtype dtype, int32_t heads, int32_t head_dim,
+                                 size_t* ws_bytes) {
+    dp::Geom g;
+    DP_TRY(check_attn(p, dtype, heads, head_dim, &g));
+    if (!ws_bytes) return fail(DP_ERR_ARG, "ws_bytes is NULL");
+    *ws_bytes = dp::plan_attention(g, heads, head_dim, dtype == DP_BF16).ws_bytes;
+    return ok();
+}
+
+dp_status dp_attention_splice(const dp_patch* p, dp_dtype dtype, int32_t heads, int32_t head_dim, float scale,
+                              const void* q_patch, const void* k_patch, const void* v_patch,
+                              const void* k_stale, const void* v_stale, void* o_patch, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+    dp::Geom g;
+    DP_TRY(check_attn(p, dtype, heads, head_dim, &g));
+    if (!std::isfinite(scale)) return fail(DP_ERR_ARG, "scale must be finite");
+    if (scale <= 0.0f) scale = 1.0f / std::sqrt((float)head_dim);
+    DP_NEED(q_patch, "q_patch");
+    DP_NEED(k_patch, "k_patch");
+    DP_NEED(v_patch, "v_patch");
+    DP_NEED(k_stale, "k_stale");
+    DP_NEED(v_stale, "v_stale");
+    DP_NEED(o_patch, "o_patch");
+    const dp::AttnPlan plan = dp::plan_attention(g, heads, head_dim, dtype == DP_BF16);
+    if (ws_bytes < plan.ws_bytes)
+        return fail(DP_ERR_ARG, "workspace too small: %zu < %zu bytes", ws_bytes, plan.ws_bytes);
+    if (plan.ws_bytes) DP_NEED(ws, "ws");
+    const size_t es = elem_size(dtype);
+    const size_t band = (size_t)g.B * g.band_tokens() * g.C * es;
+    const size_t map = (size_t)g.B * g.map_tokens() * g.C * es;
+    if (overlaps(o_patch, band, q_patch, band) || overlaps(o_patch, band, k_patch, band) ||
+        overlaps(o_patch, band, v_patch, band) || overlaps(o_patch, band, k_stale, map) ||
+        overlaps(o_patch, band, v_stale, map) || overlaps(o_patch, band, ws, plan.ws_bytes))
+        return fail(DP_ERR_ARG, "o_patch overlaps an input or the workspace");
+    if (plan.ws_bytes && (overlaps(ws, plan.ws_bytes, q_patch, band) || overlaps(ws, plan.ws_bytes, k_patch, band) ||
+                          overlaps(ws, plan.ws_bytes, v_patch, band) || overlaps(ws, plan.ws_bytes, k_stale, map) ||
+                          overlaps(ws, plan.ws_bytes, v_stale, map)))
+        return fail(DP_ERR_ARG, "workspace overlaps an input");
+    return hip_status(dp::launch_attention(g, plan, dtype == DP_BF16, heads, head_dim, scale, q_patch, k_patch,
+                                           v_patch, k_stale, v_stale, o_patch, ws, stream),
+                      "dp_attention_splice launch");
+}
+
+}  // extern "C"

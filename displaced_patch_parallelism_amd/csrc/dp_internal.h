@@ -1,0 +1,69 @@
+// Internal interface between the host entry points (dp_api.cpp) and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dp {
+
+// Geometry of one patch of an NHWC map split into P equal row bands.
+struct Geom {
+    int B, H, W, C, P, i;
+    int h;   // rows per band
+    int r0;  // first row of band i
+    int64_t band_tokens() const { return (int64_t)h * W; }   // per batch
+    int64_t map_tokens() const { return (int64_t)H * W; }    // per batch
+};
+
+// ---- band splice --------------------------------------------------------
+hipError_t launch_band_copy(const void* src, void* dst, const Geom& g, size_t elem_bytes,
+                            hipStream_t stream);
+
+// ---- GroupNorm ---------------------------------------------------------
+struct GnPlan {
+    int vec;          // elements per 16-byte vector
+    int vpt;          // vectors per token (C / vec)
+    int rows;         // tokens a stats block reads in parallel
+    int threads;      // stats block size = vpt * rows
+    int nblk;         // stats blocks per batch
+    int tok_per_blk;  // tokens per stats block
+    size_t partial_floats;  // B * nblk * G * 2
+    size_t ws_bytes;
+};
+GnPlan plan_groupnorm(const Geom& g, int G, bool bf16);
+hipError_t launch_groupnorm(const Geom& g, const GnPlan& plan, bool bf16, int G, float eps, int mode,
+                            int act, const void* x, const float* stale_stats, const float* gamma,
+                            const float* beta, float* fresh_stats_out, void* y, void* ws,
+                            hipStream_t stream);
+
+// ---- conv3x3 with stale halo -------------------------------------------
+struct ConvPlan {
+    int kind;       // 0 = f32 direct, 1 = bf16 MFMA
+    int bm, bn;     // output tile (pixels x output channels)
+    int mtiles, ntiles;
+    int ktiles;     // K tiles of 64 over 9*Cin
+    int ksplit;     // K partitions (>1: fp32 partials + ordered reduction)
+    size_t ws_bytes;
+};
+ConvPlan plan_conv(const Geom& g, int Cout, bool bf16);
+hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout, const void* x_patch,
+                       const void* x_stale, const void* w, const float* bias, void* y, void* ws,
+                       hipStream_t stream);
+
+// ---- attention over spliced K/V ------------------------------------------
+struct AttnPlan {
+    int kind;       // 0 = f32 per-query, 1 = bf16 MFMA flash
+    int qtile;      // queries per workgroup
+    int qtiles;
+    int kvsplit;    // key partitions (>1: partial results + log-sum-exp merge)
+    size_t ws_bytes;
+};
+AttnPlan plan_attention(const Geom& g, int heads, int head_dim, bool bf16);
+hipError_t launch_attention(const Geom& g, const AttnPlan& plan, bool bf16, int heads, int head_dim,
+                            float scale, const void* q, const void* k, const void* v,
+                            const void* k_stale, const void* v_stale, void* o, void* ws,
+                            hipStream_t stream);
+
+}  // namespace dp

@@ -1,0 +1,133 @@
+"""One layer's GPU state and its steps, composed from the four C-ABI calls.
+
+A layer (``configs.LayerConfig``) owns, on the GPU:
+  * the GroupNorm statistics table [P][B][G][2] of the previous step, and
+  * for every conv or attention step of its graph, the previous step's full
+    input map [B][H][W][C] (the stale context; for attention it is the K/V
+    map, since Q = K = V = the step's input).
+
+``warmup(x)`` runs a synchronous step on the full map, patch by patch, and
+leaves the state equal to that step's statistics and maps (warm-up steps are
+synchronous: DistriFusion summary on atlas.scime.ai, warm-up rows of
+"Measured effects reported in the paper").  ``step(x_patch, i)`` runs patch
+i's displaced step against the state and then splices the patch's fresh
+statistics and bands into it (on one GPU this stands for the patch's part of
+the AllGather that refreshes every device's context for the next step).
+"""
+
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import torch
+
+from . import (Patch, dp_attention_splice, dp_conv3x3_halo, dp_groupnorm_async, dp_stale_update,
+               dp_stats_update)
+
+
+def torch_dtype(name):
+    return {"bf16": torch.bfloat16, "f32": torch.float32}[name]
+
+
+class DisplacedLayer:
+    def __init__(self, cfg, convs: Sequence[Tuple["np.ndarray", "np.ndarray"]], device="cuda"):  # noqa: F821
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.dt = torch_dtype(cfg.dtype)
+        self.convs = [(torch.as_tensor(w).to(self.device, self.dt).contiguous(),
+                       torch.as_tensor(b).to(self.device, torch.float32).contiguous()) for w, b in convs]
+        c = cfg
+        self.table = torch.zeros((c.P, c.B, c.G, 2), dtype=torch.float32, device=self.device)
+        self.maps: Dict[int, torch.Tensor] = {
+            k: torch.zeros((c.B, c.H, c.W, c.C), dtype=self.dt, device=self.device)
+            for k, s in enumerate(c.graph) if s in ("conv", "attn")}
+        self.fresh_stats = torch.empty((c.B, c.G, 2), dtype=torch.float32, device=self.device)
+        # patch-sized intermediates, reused by every step
+        band = (c.B, c.h, c.W, c.C)
+        self.bufs = [torch.empty(band, dtype=self.dt, device=self.device) for _ in c.graph]
+
+    def patch(self, i) -> Patch:
+        c = self.cfg
+        return Patch(c.B, c.H, c.W, c.C, c.P, i)
+
+    def band(self, full, j):
+        h = self.cfg.h
+        return full[:, j * h:(j + 1) * h].contiguous()
+
+    def _tok(self, t):
+        return t.reshape(t.shape[0], -1, t.shape[-1])
+
+    # ---- one patch, displaced ------------------------------------------------
+    def step(self, x_patch, i, gn_mode="corrected", update_state=True) -> List[torch.Tensor]:
+        """Patch i's displaced layer step; returns every graph step's patch output."""
+        c = self.cfg
+        p = self.patch(i)
+        h = x_patch
+        outs = []
+        conv_i = 0
+        for k, s in enumerate(c.graph):
+            out = self.bufs[k]
+            if s in ("gn", "gn_silu"):
+                dp_groupnorm_async(p, h, c.G, self.table, c.eps, gn_mode, "silu" if s == "gn_silu" else None,
+                                   fresh_stats_out=self.fresh_stats, y_patch=out)
+            elif s == "conv":
+                w, b = self.convs[conv_i]
+                conv_i += 1
+                dp_conv3x3_halo(p, h, self.maps[k], w, b, y_patch=out)
+            elif s == "attn":
+                tok = self._tok(h)
+                st = self._tok(self.maps[k])
+                dp_attention_splice(p, c.heads, tok, tok, tok, st, st, o_patch=self._tok(out))
+            outs.append(out)
+            h = out
+        if update_state:
+            self.splice_state(i, x_patch, outs)
+        return outs
+
+    def splice_state(self, i, x_patch, outs):
+        """Write patch i's fresh statistics and consumer-input bands into the state."""
+        c = self.cfg
+        p = self.patch(i)
+        inputs = [x_patch] + outs[:-1]
+        for k, s in enumerate(c.graph):
+            if s in ("gn", "gn_silu"):
+                dp_stats_update(c.P, i, self.fresh_stats, self.table)
+            elif k in self.maps:
+                dp_stale_update(p, inputs[k], self.maps[k])
+
+    # ---- all patches, synchronous (warm-up) --------------------------------------
+    def warmup(self, x_full) -> List[torch.Tensor]:
+        """Synchronous full-map step; leaves the state of that step.  Returns full-map outputs."""
+        c = self.cfg
+        h_full = x_full
+        outs = []
+        conv_i = 0
+        for k, s in enumerate(c.graph):
+            out_full = torch.empty((c.B, c.H, c.W, c.C), dtype=self.dt, device=self.device)
+            if s in ("gn", "gn_silu"):
+                for j in range(c.P):
+                    dp_groupnorm_async(self.patch(j), self.band(h_full, j), c.G, None, c.eps, "local",
+                                       fresh_stats_out=self.fresh_stats, stats_only=True)
+                    dp_stats_update(c.P, j, self.fresh_stats, self.table)
+                for j in range(c.P):
+                    y, _ = dp_groupnorm_async(self.patch(j), self.band(h_full, j), c.G, self.table, c.eps,
+                                              "corrected", "silu" if s == "gn_silu" else None,
+                                              fresh_stats_out=self.fresh_stats)
+                    dp_stale_update(self.patch(j), y, out_full)
+            else:
+                for j in range(c.P):
+                    dp_stale_update(self.patch(j), self.band(h_full, j), self.maps[k])
+                if s == "conv":
+                    w, b = self.convs[conv_i]
+                    conv_i += 1
+                for j in range(c.P):
+                    pj = self.patch(j)
+                    xb = self.band(h_full, j)
+                    if s == "conv":
+                        o = dp_conv3x3_halo(pj, xb, self.maps[k], w, b)
+                    else:
+                        tok = self._tok(xb)
+                        st = self._tok(self.maps[k])
+                        o = dp_attention_splice(pj, c.heads, tok, tok, tok, st, st).reshape(xb.shape)
+                    dp_stale_update(pj, o, out_full)
+            outs.append(out_full)
+            h_full = out_full
+        return outs

@@ -1,0 +1,211 @@
+/*
+ * dp.h -- C ABI of the displaced-patch layer hot path on one MI355X (gfx950).
+ *
+ * Displaced patch parallelism (DistriFusion) splits a diffusion model's input
+ * into patches, one per device, and lets every patch use the previous
+ * denoising step's activations as context for the current one ("activation
+ * displacement": "DistriFusion: Distributed Parallel Inference for
+ * High-Resolution Diffusion Models", study.space page, Method; the abstract on
+ * the scholarfeed.org author page).  This library computes one patch's share
+ * of a UNet layer step on one GPU:
+ *
+ *   dp_groupnorm_async   corrected asynchronous GroupNorm (fresh local
+ *                        statistics + stale statistics of the other patches)
+ *   dp_conv3x3_halo      3x3 conv whose rows above/below the patch come from
+ *                        the previous step's (stale) map
+ *   dp_attention_splice  attention: queries from the fresh patch, keys and
+ *                        values from the full stale map with the patch
+ *                        spliced in
+ *   dp_stale_update      writes the fresh patch into the resident stale map
+ *
+ * Geometry.  Maps are NHWC, batch-major: element (b, r, c, ch) of a [B][H][W][C]
+ * map sits at ((b*H + r)*W + c)*C + ch.  The P patches are equal row bands:
+ * patch i owns rows [i*h, (i+1)*h) with h = H/P (H must be divisible by P).
+ * A patch buffer holds just its band, [B][h][W][C].  Token n of a map is row
+ * n / W, column n % W, so a band is one contiguous token range per batch.
+ *
+ * Data types.  DP_F32: activations and weights are float.  DP_BF16:
+ * activations and weights are bfloat16 (raw 16-bit patterns), arithmetic is
+ * fp32 (MFMA accumulates in fp32), outputs are rounded to nearest even.
+ * Statistics, bias, gamma and beta are always float.
+ *
+ * Ownership.  Every pointer argument except `p` and size outputs is device
+ * memory owned by the caller (e.g. a torch tensor's storage).  The library
+ * allocates nothing, keeps no state between calls and never synchronises the
+ * host: each call only enqueues kernels on `stream` (0 = legacy default
+ * stream) and returns.  Pointers must be 16-byte aligned.  A workspace `ws`
+ * is caller-provided scratch of at least the size the matching *_ws query
+ * returns (may be NULL when that size is 0); its contents on entry do not
+ * matter and are undefined on return.  Calls that share a workspace or an
+ * output must be ordered on one stream.
+ *
+ * Errors.  All arguments are validated on the host before anything is
+ * enqueued; a rejected call enqueues nothing.  Return codes:
+ *   DP_OK               enqueued
+ *   DP_ERR_ARG          invalid argument (shape, index, NULL, alignment,
+ *                       workspace too small, output overlapping an input)
+ *   DP_ERR_UNSUPPORTED  valid but not built (e.g. bf16 attention with a
+ *                       head_dim other than 64)
+ *   DP_ERR_HIP          a HIP launch failed
+ * dp_last_error() then describes the failure.  No C++ exception or abort
+ * crosses the ABI.  Results are deterministic: repeated calls with the same
+ * inputs give bitwise identical outputs (fixed reduction orders, no atomics
+ * on data).
+ */
+#ifndef DP_H
+#define DP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DP_OK = 0, DP_ERR_ARG = 1, DP_ERR_UNSUPPORTED = 2, DP_ERR_HIP = 3 } dp_status;
+
+typedef enum { DP_F32 = 0, DP_BF16 = 1 } dp_dtype;
+
+/* GroupNorm statistics a patch normalises with.  The three alternatives to
+ * the corrected form are the ablations of the DistriFusion summary on
+ * atlas.scime.ai, table "Measured effects reported in the paper"
+ * (on-device patch statistics only; stale statistics reused).  The
+ * synchronised exact form is DP_GN_CORRECTED with a table that holds the
+ * current step's statistics of every band (warm-up). */
+typedef enum {
+    DP_GN_CORRECTED = 0, /* fresh moments of patch i + stale moments of the other bands */
+    DP_GN_LOCAL = 1,     /* fresh moments of patch i only                              */
+    DP_GN_STALE = 2      /* previous step's moments of all bands                       */
+} dp_gn_mode;
+
+typedef enum { DP_ACT_NONE = 0, DP_ACT_SILU = 1 } dp_act;
+
+/* Full-map geometry and the patch this call computes: map [B][H][W][C],
+ * P row bands, patch index i in [0, P). */
+typedef struct {
+    int32_t B, H, W, C, P, i;
+} dp_patch;
+
+/* ------------------------------------------------------------------------
+ * dp_groupnorm_async -- corrected asynchronous GroupNorm of patch i.
+ *
+ * Source: DistriFusion summary (atlas.scime.ai), Approach: a corrected
+ * asynchronous GroupNorm fixes the statistics that stale activations would
+ * otherwise give; same page, "Measured effects" table: on-device-only and
+ * stale-only statistics are the worse ablations, synchronised statistics the
+ * slower exact one.  Reading: the patch normalises with the moments of the
+ * spliced map (previous step's map with its own band fresh), per (b, group g):
+ *   m_i, q_i   = mean of x and of x*x over the band's h*W*(C/G) elements
+ *   CORRECTED: E = (m_i + sum_{j!=i} m'_j) / P,  Q = (q_i + sum_{j!=i} q'_j) / P
+ *   LOCAL:     E = m_i,                          Q = q_i
+ *   STALE:     E = sum_j m'_j / P,               Q = sum_j q'_j / P
+ *   var = max(Q - E*E, 0),  y = (x - E) / sqrt(var + eps) * gamma[c] + beta[c]
+ *   then y = y * sigmoid(y) if act == DP_ACT_SILU.
+ *
+ *   x_patch         [B][h][W][C] dtype, the fresh band
+ *   stale_stats     [P][B][G][2] float, (m'_j, q'_j) of every band from the
+ *                   previous step; may be NULL for DP_GN_LOCAL
+ *   gamma, beta     [C] float or NULL (1 and 0)
+ *   fresh_stats_out [B][G][2] float, receives (m_i, q_i); may be NULL
+ *   y_patch         [B][h][W][C] dtype, or NULL to compute statistics only
+ *                   (the first pass of a synchronous warm-up step); may equal
+ *                   x_patch (in place) but must not otherwise overlap it
+ *   ws              >= dp_groupnorm_async_ws bytes
+ * Requires C % G == 0, C % 8 == 0 (bf16) or C % 4 == 0 (f32), eps > 0.
+ * After the call, fresh_stats_out is what dp_stale_update copies into slot i
+ * of the table for the next step (see dp_stale_update).
+ * ---------------------------------------------------------------------- */
+dp_status dp_groupnorm_async_ws(const dp_patch* p, dp_dtype dtype, int32_t G, size_t* ws_bytes);
+
+dp_status dp_groupnorm_async(const dp_patch* p, dp_dtype dtype, int32_t G, float eps,
+                             dp_gn_mode mode, dp_act act, const void* x_patch,
+                             const float* stale_stats, const float* gamma, const float* beta,
+                             float* fresh_stats_out, void* y_patch, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * dp_conv3x3_halo -- 3x3 convolution of patch i with stale halo rows.
+ *
+ * Source: study.space page, Method (previous-step activations give each
+ * patch its context; each device computes only its patch).  Reading: the
+ * conv is the zero-padded, stride-1 3x3 cross-correlation of the spliced
+ * map, evaluated on the band's rows:
+ *   y[b,y,x,o] = bias[o] + sum_{ky,kx,c} w[o,ky,kx,c] * src(b, r0+y+ky-1, x+kx-1, c)
+ * where src is x_patch inside rows [r0, r0+h), x_stale at other rows of the
+ * image (only rows r0-1 and r0+h are ever read) and 0 outside the image.
+ *
+ *   x_patch  [B][h][W][Cin] dtype (Cin = p->C)
+ *   x_stale  [B][H][W][Cin] dtype, previous step's map
+ *   w        [Cout][3][3][Cin] dtype
+ *   bias     [Cout] float or NULL
+ *   y_patch  [B][h][W][Cout] dtype; must not overlap any input
+ *   ws       >= dp_conv3x3_halo_ws bytes
+ * bf16 requires Cin % 64 == 0 and Cout % 32 == 0 (MFMA path); f32 takes any
+ * Cin, Cout >= 1.
+ * ---------------------------------------------------------------------- */
+dp_status dp_conv3x3_halo_ws(const dp_patch* p, dp_dtype dtype, int32_t Cout, size_t* ws_bytes);
+
+dp_status dp_conv3x3_halo(const dp_patch* p, dp_dtype dtype, int32_t Cout, const void* x_patch,
+                          const void* x_stale, const void* w, const float* bias, void* y_patch,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * dp_attention_splice -- self-attention of patch i over spliced K/V.
+ *
+ * Source: PipeFusion explainer (gist.science), Problem Statement and Memory
+ * Efficiency: DistriFusion keeps the full spatial K and V of every layer on
+ * every device; with the study.space Method (stale context, fresh patch).
+ * Reading: for head e (channels [e*d, (e+1)*d)) and query token q of the band,
+ *   O[q] = sum_n softmax_n(scale * <Q[q], K[n]>) V[n]
+ * with K[n] = k_patch[n - r0*W] for tokens n of the band [r0*W, (r0+h)*W) and
+ * k_stale[n] elsewhere; likewise V.  No mask.  scale <= 0 selects d^-1/2.
+ *
+ *   q_patch, k_patch, v_patch  [B][h*W][heads*head_dim] dtype
+ *   k_stale, v_stale           [B][H*W][heads*head_dim] dtype
+ *   o_patch                    [B][h*W][heads*head_dim] dtype; must not
+ *                              overlap any input
+ * k_patch / v_patch may point into band i of k_stale / v_stale (an in-place
+ * splice done before the call); the result is the same.
+ * Requires heads*head_dim == p->C.  bf16: head_dim == 64.  f32:
+ * head_dim <= 128 and head_dim % 4 == 0.
+ * ---------------------------------------------------------------------- */
+dp_status dp_attention_splice_ws(const dp_patch* p, dp_dtype dtype, int32_t heads,
+                                 int32_t head_dim, size_t* ws_bytes);
+
+dp_status dp_attention_splice(const dp_patch* p, dp_dtype dtype, int32_t heads, int32_t head_dim,
+                              float scale, const void* q_patch, const void* k_patch,
+                              const void* v_patch, const void* k_stale, const void* v_stale,
+                              void* o_patch, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * dp_stale_update -- write the fresh patch into the resident stale map.
+ *
+ * Source: DistriFusion summary (atlas.scime.ai), Approach (the AllGather of
+ * fresh activations that becomes the next step's context); study.space page,
+ * Method.  On one GPU this is the own-band part of what the gather delivers:
+ *   stale[b, r0:r0+h, :, :] = x_patch[b]   bit for bit; other rows untouched.
+ *
+ *   x_patch  [B][h][W][C] dtype
+ *   stale    [B][H][W][C] dtype, updated in place
+ * x_patch may be band i of stale itself (then nothing is done); any other
+ * overlap is an error.  The GroupNorm statistics table [P][B][G][2] is updated
+ * with the same call viewed as a map: dtype DP_F32, B=1, H=P, W=1,
+ * C=B*G*2, P=P, i=i, x_patch = fresh_stats_out.
+ * ---------------------------------------------------------------------- */
+dp_status dp_stale_update(const dp_patch* p, dp_dtype dtype, const void* x_patch, void* stale,
+                          hipStream_t stream);
+
+/* Description of the last error on the calling thread (empty if none). The
+ * string stays valid until the thread's next dp_* call. */
+const char* dp_last_error(void);
+
+/* Library version string. */
+const char* dp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DP_H */

@@ -1,0 +1,150 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+rejects invalid arguments on the host before touching the GPU runtime.
+
+No call here reaches a kernel launch: every case fails validation first.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import displaced_patch_parallelism_amd as dp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dp.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(dp.LIB_PATH), reason="libdp.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert {"dp_groupnorm_async", "dp_conv3x3_halo", "dp_attention_splice", "dp_stale_update"} <= set(names)
+    lib = dp.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert dp.version().startswith("dp ")
+
+
+P_OK = dp.Patch(1, 16, 8, 64, 4, 1)
+FAKE = 0x10000          # 16-byte aligned, never dereferenced: validation fails first
+FAKE2 = 0x20000000
+
+
+def call_stale(p, dtype=dp.DP_BF16, x=FAKE, s=FAKE2):
+    return dp.lib().dp_stale_update(dp._cpatch(p), dtype, x, s, None)
+
+
+@pytest.mark.parametrize("p,msg", [
+    (dp.Patch(1, 10, 8, 64, 4, 0), "divisible"),
+    (dp.Patch(1, 16, 8, 64, 4, 4), "patch index"),
+    (dp.Patch(1, 16, 8, 64, 4, -1), "patch index"),
+    (dp.Patch(0, 16, 8, 64, 4, 0), ">= 1"),
+    (dp.Patch(1, 16, 0, 64, 4, 0), ">= 1"),
+])
+def test_bad_geometry(p, msg):
+    assert call_stale(p) == dp.DP_ERR_ARG
+    assert msg in dp.lib().dp_last_error().decode()
+
+
+def test_null_and_misaligned_pointers():
+    assert call_stale(P_OK, x=0) == dp.DP_ERR_ARG
+    assert "NULL" in dp.lib().dp_last_error().decode()
+    assert call_stale(P_OK, x=FAKE + 2) == dp.DP_ERR_ARG
+    assert "aligned" in dp.lib().dp_last_error().decode()
+    assert call_stale(P_OK, dtype=7) == dp.DP_ERR_ARG
+
+
+def test_stale_update_overlap_rejected():
+    # x_patch inside the map but not band i
+    assert call_stale(P_OK, x=FAKE2 + 16, s=FAKE2) == dp.DP_ERR_ARG
+    assert "overlap" in dp.lib().dp_last_error().decode()
+
+
+def test_stale_update_in_place_is_noop():
+    # x_patch == band i of stale: nothing to do, succeeds without touching memory
+    band_off = P_OK.r0 * P_OK.W * P_OK.C * 2
+    assert call_stale(P_OK, x=FAKE2 + band_off, s=FAKE2) == dp.DP_OK
+
+
+def ws_query(kind, p, dtype, *args):
+    out = ctypes.c_size_t(123)
+    fn = {"gn": dp.lib().dp_groupnorm_async_ws, "conv": dp.lib().dp_conv3x3_halo_ws,
+          "attn": dp.lib().dp_attention_splice_ws}[kind]
+    st = fn(dp._cpatch(p), dtype, *args, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_queries():
+    st, n = ws_query("gn", dp.Patch(1, 128, 128, 320, 4, 1), dp.DP_BF16, 32)
+    assert st == dp.DP_OK and n > 0
+    st, n = ws_query("conv", dp.Patch(1, 480, 480, 320, 8, 1), dp.DP_BF16, 320)
+    assert st == dp.DP_OK
+    st, n = ws_query("conv", dp.Patch(1, 32, 32, 1280, 8, 1), dp.DP_BF16, 1280)
+    assert st == dp.DP_OK and n > 0          # small M: split along K
+    st, n = ws_query("attn", dp.Patch(1, 64, 64, 640, 4, 1), dp.DP_BF16, 10, 64)
+    assert st == dp.DP_OK and n > 0          # few query tiles: split along keys
+    st, n = ws_query("attn", dp.Patch(1, 16, 16, 32, 2, 1), dp.DP_F32, 1, 32)
+    assert st == dp.DP_OK and n == 0
+
+
+def test_unsupported_shapes():
+    assert ws_query("gn", dp.Patch(1, 8, 8, 30, 2, 0), dp.DP_BF16, 3)[0] == dp.DP_ERR_UNSUPPORTED
+    assert ws_query("gn", dp.Patch(1, 8, 8, 32, 2, 0), dp.DP_BF16, 5)[0] == dp.DP_ERR_ARG
+    assert ws_query("conv", dp.Patch(1, 8, 8, 32, 2, 0), dp.DP_BF16, 64)[0] == dp.DP_ERR_UNSUPPORTED
+    assert ws_query("attn", dp.Patch(1, 8, 8, 256, 2, 0), dp.DP_BF16, 2, 128)[0] == dp.DP_ERR_UNSUPPORTED
+    assert ws_query("attn", dp.Patch(1, 8, 8, 64, 2, 0), dp.DP_BF16, 2, 64)[0] == dp.DP_ERR_ARG
+    assert ws_query("attn", dp.Patch(1, 8, 8, 24, 2, 0), dp.DP_F32, 1, 24)[0] == dp.DP_ERR_UNSUPPORTED
+
+
+def test_groupnorm_argument_errors():
+    L = dp.lib()
+    p = dp._cpatch(dp.Patch(1, 8, 8, 64, 2, 0))
+    # eps must be positive
+    assert L.dp_groupnorm_async(p, dp.DP_BF16, 8, 0.0, 0, 0, FAKE, FAKE2, None, None, None, FAKE2 * 2,
+                                FAKE2 * 4, 1 << 20, None) == dp.DP_ERR_ARG
+    # corrected mode needs the stale table when normalising
+    assert L.dp_groupnorm_async(p, dp.DP_BF16, 8, 1e-5, 0, 0, FAKE, None, None, None, None, FAKE2 * 2,
+                                FAKE2 * 4, 1 << 20, None) == dp.DP_ERR_ARG
+    assert "stale_stats" in L.dp_last_error().decode()
+    # workspace too small
+    assert L.dp_groupnorm_async(p, dp.DP_BF16, 8, 1e-5, 0, 0, FAKE, FAKE2, None, None, None, FAKE2 * 2,
+                                FAKE2 * 4, 16, None) == dp.DP_ERR_ARG
+    assert "workspace" in L.dp_last_error().decode()
+    # nothing requested
+    assert L.dp_groupnorm_async(p, dp.DP_BF16, 8, 1e-5, 1, 0, FAKE, None, None, None, None, None,
+                                FAKE2 * 4, 1 << 20, None) == dp.DP_ERR_ARG
+    # unknown mode / activation
+    assert L.dp_groupnorm_async(p, dp.DP_BF16, 8, 1e-5, 9, 0, FAKE, FAKE2, None, None, None, FAKE2 * 2,
+                                FAKE2 * 4, 1 << 20, None) == dp.DP_ERR_ARG
+    assert L.dp_groupnorm_async(p, dp.DP_BF16, 8, 1e-5, 0, 5, FAKE, FAKE2, None, None, None, FAKE2 * 2,
+                                FAKE2 * 4, 1 << 20, None) == dp.DP_ERR_ARG
+
+
+def test_conv_and_attention_overlap_errors():
+    L = dp.lib()
+    p = dp._cpatch(dp.Patch(1, 8, 8, 64, 2, 0))
+    # output overlaps the stale map
+    assert L.dp_conv3x3_halo(p, dp.DP_BF16, 64, FAKE, FAKE2, FAKE2 * 2, None, FAKE2 + 64, FAKE2 * 4,
+                             1 << 24, None) == dp.DP_ERR_ARG
+    assert "overlap" in L.dp_last_error().decode()
+    pa = dp._cpatch(dp.Patch(1, 8, 8, 64, 2, 0))
+    assert L.dp_attention_splice(pa, dp.DP_BF16, 1, 64, 0.0, FAKE, FAKE, FAKE, FAKE2, FAKE2, FAKE,
+                                 FAKE2 * 4, 1 << 24, None) == dp.DP_ERR_ARG
+    assert L.dp_attention_splice(pa, dp.DP_BF16, 1, 64, float("nan"), FAKE, FAKE, FAKE, FAKE2, FAKE2,
+                                 FAKE2 * 2, FAKE2 * 4, 1 << 24, None) == dp.DP_ERR_ARG
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    s = torch.zeros(1, 8, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        dp.dp_stale_update(dp.Patch(1, 8, 8, 64, 4, 1), x, s)

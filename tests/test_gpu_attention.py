@@ -1,0 +1,126 @@
+"""dp_attention_splice on the GPU against the oracle, per call, on identical inputs."""
+
+import numpy as np
+import pytest
+import torch
+
+import displaced_patch_parallelism_amd as dp
+import oracle
+from displaced_patch_parallelism_amd import synth
+from displaced_patch_parallelism_amd.configs import CONFIGS
+from tests.gpu_util import announce, assert_parity, gpu, host
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(B, H, W, heads, d, P, i, dtype, seed=0, rows=None, q_scale=1.0):
+    C = heads * d
+    case = synth.attn_case(B, H * W, C, dtype, seed, q_scale=q_scale)
+    nq = (H // P) * W
+    t0 = i * nq
+    q, k, v = (a[:, t0:t0 + nq] for a in (case.q, case.k, case.v))
+    ref = oracle.attention_splice(q, k, v, case.k_stale, case.v_stale, H, W, P, i, heads, rows=rows)
+    o = dp.dp_attention_splice(dp.Patch(B, H, W, C, P, i), heads, gpu(q, dtype), gpu(k, dtype), gpu(v, dtype),
+                               gpu(case.k_stale, dtype), gpu(case.v_stale, dtype))
+    torch.cuda.synchronize()
+    got = host(o)
+    if rows is not None:
+        got = got[:, rows]
+    assert_parity(got, ref, dtype, f"attn {dtype} B{B} {H}x{W} {heads}x{d} P{P} i{i}")
+    return o
+
+
+@pytest.mark.parametrize("name", ["c0", "c2", "c3"])
+def test_config_shapes(name):
+    c = CONFIGS[name]
+    patches = [0, c.patch, c.P - 1] if c.P > 2 else list(range(c.P))
+    for i in patches:
+        announce("attention", name, "patch", i)
+        run_case(c.B, c.H, c.W, c.heads, c.head_dim, c.P, i, c.dtype, seed=20 + i)
+
+
+def test_c4b_sampled_rows():
+    """3840px layer: the oracle computes a seeded sample of query rows plus every band-edge row."""
+    c = CONFIGS["c4b"]
+    rng = np.random.default_rng(0)
+    nq = c.Nq
+    edges = list(range(c.W)) + list(range(nq - c.W, nq))
+    rows = sorted(set(rng.choice(nq, 256, replace=False).tolist()) | set(edges))
+    announce("attention c4b sampled", len(rows), "rows")
+    run_case(c.B, c.H, c.W, c.heads, c.head_dim, c.P, c.patch, c.dtype, seed=5, rows=rows)
+
+
+@pytest.mark.parametrize("B,H,W,heads,P,i", [
+    (1, 5, 13, 2, 5, 2),     # N = 65: ragged last key tile; Nq = 13
+    (2, 6, 30, 3, 3, 1),     # batch 2, Nq = 60, N = 180, band straddles key tiles
+    (1, 40, 10, 1, 2, 1),    # Nq = 200: ragged query tile
+    (1, 8, 24, 4, 1, 0),     # one patch: plain self-attention
+])
+def test_ragged_bf16(B, H, W, heads, P, i):
+    announce("attention ragged", B, H, W, heads, P, i)
+    run_case(B, H, W, heads, 64, P, i, "bf16", seed=i)
+
+
+def test_peaked_softmax_bf16():
+    """Large scores (queries scaled x4) exercise the running-max rescaling."""
+    announce("attention peaked")
+    run_case(1, 16, 32, 2, 64, 4, 2, "bf16", seed=9, q_scale=4.0)
+
+
+@pytest.mark.parametrize("d", [4, 16, 32, 64, 128])
+def test_f32_head_dims(d):
+    announce("attention f32 d", d)
+    run_case(1, 8, 8, 2, d, 2, 1, "f32", seed=d)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f32", 32)])
+def test_onehot_splice_indexing_bit_exact(dtype, d):
+    """Each query selects one key by a margin of 1000 (every other softmax weight is
+    exactly 0); the output row is then that key's V row: fresh (negative values)
+    inside the band, stale (positive) outside."""
+    N = 2 * d                                  # keys n = +-e_{n mod d}: all distinct
+    W, P = 16, 4
+    H = N // W
+    nq = (H // P) * W
+    rng = np.random.default_rng(3)
+    sign = np.where(np.arange(N) < d, 1.0, -1.0).astype(np.float32)
+    kdir = np.zeros((N, d), np.float32)
+    kdir[np.arange(N), np.arange(N) % d] = sign
+    v_fresh = -rng.integers(1, 101, size=(1, N, d)).astype(np.float32)
+    v_stale = rng.integers(1, 101, size=(1, N, d)).astype(np.float32)
+    k = kdir[None]
+    for i in range(P):
+        announce("attention one-hot", dtype, d, "patch", i)
+        t0 = i * nq
+        targets = rng.integers(0, N, size=nq)
+        q = 1000.0 * kdir[targets][None]
+        ref = oracle.attention_splice(q, k[:, t0:t0 + nq], v_fresh[:, t0:t0 + nq], k, v_stale, H, W, P, i, 1,
+                                      scale=1.0)
+        inband = ((targets >= t0) & (targets < t0 + nq))[None, :, None]
+        assert np.array_equal(ref, np.where(inband, v_fresh[:, targets], v_stale[:, targets]))
+        o = dp.dp_attention_splice(dp.Patch(1, H, W, d, P, i), 1, gpu(q, dtype), gpu(k[:, t0:t0 + nq], dtype),
+                                   gpu(v_fresh[:, t0:t0 + nq], dtype), gpu(k, dtype), gpu(v_stale, dtype),
+                                   scale=1.0)
+        assert np.array_equal(host(o), ref), f"patch {i}"
+
+
+def test_in_place_splice_alias_and_determinism():
+    """k_patch/v_patch pointing into band i of the stale maps gives the same result."""
+    c = CONFIGS["c2"]
+    announce("attention alias c2")
+    case = synth.attn_case(1, c.N, c.C, "bf16", 4)
+    i, nq = 1, c.Nq
+    p = dp.Patch(1, c.H, c.W, c.C, c.P, i)
+    q = gpu(case.q[:, i * nq:(i + 1) * nq], "bf16")
+    k = gpu(case.k[:, i * nq:(i + 1) * nq], "bf16")
+    v = gpu(case.v[:, i * nq:(i + 1) * nq], "bf16")
+    ks, vs = gpu(case.k_stale, "bf16"), gpu(case.v_stale, "bf16")
+    o1 = dp.dp_attention_splice(p, c.heads, q, k, v, ks, vs)
+    o2 = dp.dp_attention_splice(p, c.heads, q, k, v, ks, vs)
+    ks2, vs2 = ks.clone(), vs.clone()
+    ks2[:, i * nq:(i + 1) * nq] = k
+    vs2[:, i * nq:(i + 1) * nq] = v
+    o3 = dp.dp_attention_splice(p, c.heads, q, ks2[:, i * nq:(i + 1) * nq], vs2[:, i * nq:(i + 1) * nq], ks2, vs2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))

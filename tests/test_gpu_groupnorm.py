@@ -1,0 +1,88 @@
+"""dp_groupnorm_async on the GPU against the oracle, per call, on identical inputs."""
+
+import numpy as np
+import pytest
+import torch
+
+import displaced_patch_parallelism_amd as dp
+import oracle
+from displaced_patch_parallelism_amd import synth
+from displaced_patch_parallelism_amd.configs import CONFIGS
+from tests.gpu_util import announce, assert_parity, gpu, host
+
+pytestmark = pytest.mark.gpu
+
+MODES = {"corrected": oracle.GN_CORRECTED, "local": oracle.GN_LOCAL, "stale": oracle.GN_STALE}
+
+
+def run_case(B, H, W, C, G, P, i, dtype, mode="corrected", act=None, affine=False, seed=0, mean=0.0):
+    fresh, stale, gamma, beta = synth.gn_case(B, H, W, C, dtype, seed, mean=mean, affine=affine)
+    table = oracle.band_moments(stale, G, P).astype(np.float32)   # previous step's moments
+    h = H // P
+    xb = fresh[:, i * h:(i + 1) * h]
+    ref_y, ref_st = oracle.gn_async(xb, table, P, i, G, 1e-5, MODES[mode], gamma, beta, act)
+    y, st = dp.dp_groupnorm_async(dp.Patch(B, H, W, C, P, i), gpu(xb, dtype), G, gpu(table, "f32"), 1e-5, mode,
+                                  act, None if gamma is None else gpu(gamma, "f32"),
+                                  None if beta is None else gpu(beta, "f32"))
+    torch.cuda.synchronize()
+    assert_parity(host(y), ref_y, dtype, f"y {dtype} {mode} {act}")
+    # fresh moments: fp32 sums over the band
+    np.testing.assert_allclose(host(st), ref_st, rtol=1e-4, atol=1e-5)
+    return y, st
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_config_shapes(name):
+    c = CONFIGS[name]
+    act = "silu" if "gn_silu" in c.graph else None
+    for i in ([0, c.patch, c.P - 1] if c.P > 2 else range(c.P)):
+        announce("groupnorm", name, "patch", i)
+        run_case(c.B, c.H, c.W, c.C, c.G, c.P, i, c.dtype, act=act, seed=i)
+
+
+@pytest.mark.parametrize("mode", ["corrected", "local", "stale"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_modes_affine_batched(mode, dtype):
+    announce("groupnorm modes", mode, dtype)
+    run_case(2, 12, 10, 48, 6, 3, 1, dtype, mode=mode, act="silu", affine=True, seed=3)
+
+
+def test_nonzero_mean_and_ragged_tokens():
+    announce("groupnorm mean 3, 7x13 map")
+    run_case(1, 14, 13, 64, 8, 2, 1, "bf16", mean=3.0, seed=4)
+    run_case(1, 14, 13, 64, 8, 2, 0, "f32", mean=3.0, seed=4)
+
+
+def test_stats_only_and_in_place_and_determinism():
+    c = CONFIGS["c1"]
+    announce("groupnorm stats-only / in-place / determinism")
+    fresh, stale, _, _ = synth.gn_case(1, c.H, c.W, c.C, "bf16", 5)
+    table = gpu(oracle.band_moments(stale, c.G, c.P).astype(np.float32), "f32")
+    p = dp.Patch(1, c.H, c.W, c.C, c.P, 1)
+    xb = gpu(fresh[:, c.h:2 * c.h], "bf16")
+    _, st_only = dp.dp_groupnorm_async(p, xb, c.G, None, stats_only=True)
+    y1, st1 = dp.dp_groupnorm_async(p, xb, c.G, table, act="silu")
+    y2, st2 = dp.dp_groupnorm_async(p, xb, c.G, table, act="silu")
+    x_inplace = xb.clone()
+    dp.dp_groupnorm_async(p, x_inplace, c.G, table, act="silu", y_patch=x_inplace)
+    torch.cuda.synchronize()
+    assert torch.equal(st_only, st1) and torch.equal(st1, st2)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(y1.view(torch.int16), x_inplace.view(torch.int16))
+
+
+def test_warmup_table_gives_exact_group_norm():
+    """Stats pass over every band, then corrected normalisation = full-map GroupNorm."""
+    c = CONFIGS["c2"]
+    announce("groupnorm warm-up identity c2")
+    fresh, _, _, _ = synth.gn_case(1, c.H, c.W, c.C, "bf16", 6)
+    table = torch.empty((c.P, 1, c.G, 2), device="cuda")
+    for j in range(c.P):
+        _, st = dp.dp_groupnorm_async(dp.Patch(1, c.H, c.W, c.C, c.P, j), gpu(fresh[:, j * c.h:(j + 1) * c.h], "bf16"),
+                                      c.G, None, stats_only=True)
+        dp.dp_stats_update(c.P, j, st, table)
+    ref = oracle.group_norm(fresh, c.G)
+    for j in range(c.P):
+        y, _ = dp.dp_groupnorm_async(dp.Patch(1, c.H, c.W, c.C, c.P, j), gpu(fresh[:, j * c.h:(j + 1) * c.h], "bf16"),
+                                     c.G, table)
+        assert_parity(host(y), ref[:, j * c.h:(j + 1) * c.h], "bf16", f"warm-up band {j}")
