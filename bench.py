@@ -1,0 +1,208 @@
+#!/usr/bin/env python
+"""Benchmark of one displaced-patch layer step on one MI355X.
+
+A step is patch i's share of one UNet-layer denoising step, every call of the
+hot path in order: corrected asynchronous GroupNorm (statistics, combine,
+normalise + SiLU), the 3x3 conv with stale halo rows and/or the attention over
+spliced K/V, then the splice of the fresh band and statistics into the
+resident stale state.  The default workload is the SDXL level-1 conv layer at
+1024px (latent 128x128, C=320, 4 row patches, patch 1).  Inputs are seeded
+synthetic tensors already resident in HBM; the stale state comes from a
+synchronous warm-up step run by the same library.
+
+Prints one JSON line: whole-step TFLOP/s (algorithmic conv + attention flops
+over the step's wall time between two device synchronisations), per-call
+times from HIP events recorded on the library's stream during the timed
+steps, the roofline of the dominant kernel, and the CPU oracle's rate on a
+bounded sample of the same step.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "displaced-patch layer TFLOP/s (% bf16 MFMA peak) + GroupNorm/splice HBM GB/s"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA bf16; fp32 vector
+PEAK_HBM_GBS = 8000.0
+
+# source file of each call's main kernel (for the counter file's staleness check)
+KERNEL_SOURCES = {"conv": "k_conv.hip", "attn": "k_attention.hip", "gn": "k_groupnorm.hip",
+                  "gn_silu": "k_groupnorm.hip", "stale_update": "k_splice.hip"}
+KERNEL_NAMES = {"conv": "conv3x3_bf16_mfma_kernel", "attn": "attn_bf16_d64_kernel"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(name):
+    path = os.path.join(ROOT, "displaced_patch_parallelism_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if taken on the current source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = table.get(f"{kernel}/{workload}")
+    if not ent or ent.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, i, seconds):
+    """The oracle's displaced step of the same patch, repeated for about `seconds`."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    params = {"G": cfg.G, "eps": cfg.eps, "heads": cfg.heads, "convs": inp.convs}
+    _, state = oracle.sync_layer(cfg.graph, params, inp.x_prev, cfg.P)
+    xb = inp.x[:, i * cfg.h:(i + 1) * cfg.h]
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.displaced_layer(cfg.graph, params, xb, state, cfg.P, i)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    flops = (cfg.conv_flops() + cfg.attn_flops()) * reps
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} x oracle displaced step of {cfg.name} patch {i} "
+                      f"({'+'.join(cfg.graph)}, float64 numpy) in {el:.1f} s",
+            "seconds_per_step": el / reps}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c1", help="layer shape: c1 (default), c2, c3, c4a, c4b, c0")
+    ap.add_argument("--patch", type=int, default=None, help="patch index (default: the config's)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample length; 0 skips it")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one patch's layer step on ONE GPU; runs on more than one GPU "
+              "are not part of this build (--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import displaced_patch_parallelism_amd as dp
+    from displaced_patch_parallelism_amd import synth
+    from displaced_patch_parallelism_amd.configs import CONFIGS
+    from displaced_patch_parallelism_amd.layers import DisplacedLayer
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    dp.lib()  # fail loudly if the library is not built
+    cfg = CONFIGS[args.config]
+    i = cfg.patch if args.patch is None else args.patch
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device {props.name} ({getattr(props, 'gcnArchName', '?')}), {props.multi_processor_count} CUs; "
+        f"config {cfg.name}: {cfg.note}; patch {i}")
+
+    inp = synth.layer_inputs(cfg, args.seed)
+    layer = DisplacedLayer(cfg, inp.convs, dev)
+    to = lambda a: torch.from_numpy(a).to(dev, layer.dt).contiguous()  # noqa: E731
+    layer.warmup(to(inp.x_prev))                 # previous step: synchronous, builds the stale state
+    x_patch = to(inp.x[:, i * cfg.h:(i + 1) * cfg.h])
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        layer.step(x_patch, i)
+    torch.cuda.synchronize()
+
+    # timed steps, wall clock between device synchronisations
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer.step(x_patch, i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # the same steps again with every call bracketed by HIP events on the library's stream
+    events = {}
+    for _ in range(args.steps):
+        layer.step(x_patch, i, events=events)
+    torch.cuda.synchronize()
+    per_call_us = {k: 1e3 * sum(s.elapsed_time(e) for s, e in v) / len(v) for k, v in events.items()}
+
+    ms_per_step = 1e3 * wall / args.steps
+    flops = cfg.conv_flops() + cfg.attn_flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[cfg.dtype]
+
+    band = cfg.band_bytes()
+    kernels = {}
+    for k, us in per_call_us.items():
+        ent = {"us": round(us, 3)}
+        if k == "conv":
+            ent["tflops"] = round(cfg.conv_flops() / (us * 1e-6) / 1e12, 2)
+            ent["frac_mfma_peak"] = round(ent["tflops"] / peak, 4)
+        elif k == "attn":
+            ent["tflops"] = round(cfg.attn_flops() / (us * 1e-6) / 1e12, 2)
+            ent["frac_mfma_peak"] = round(ent["tflops"] / peak, 4)
+        elif k in ("gn", "gn_silu", "stale_update"):
+            gbs = 2 * band / (us * 1e-6) / 1e9       # one read + one write of the band
+            ent["gbs"] = round(gbs, 1)
+            ent["frac_hbm_peak"] = round(gbs / PEAK_HBM_GBS, 4)
+        kernels[k] = ent
+
+    compute = [k for k in ("conv", "attn") if k in per_call_us]
+    dom = max(compute, key=lambda k: per_call_us[k])
+    dom_flops = cfg.conv_flops() if dom == "conv" else cfg.attn_flops()
+    achieved = dom_flops / (per_call_us[dom] * 1e-6) / 1e12
+    roofline = {"bound": "mfma", "kernel": KERNEL_NAMES.get(dom, dom), "achieved": round(achieved, 2),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": traffic_for(dom, cfg.name),
+                "algorithmic_flops_per_launch": dom_flops}
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) activations, previous step x+0.05*N(0,1), N(0,1/fan_in) weights)",
+        "config": {"workload": f"{cfg.name}: {cfg.note}", "map": [cfg.B, cfg.H, cfg.W, cfg.C],
+                   "groups": cfg.G, "patches": cfg.P, "patch": i, "graph": list(cfg.graph),
+                   "parallelism": "one patch on one GPU"},
+        "frac_mfma_peak": round(value / peak, 4),
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+    if args.cpu_seconds > 0:
+        log("timing the CPU oracle ...")
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, i, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -27,6 +27,20 @@ def torch_dtype(name):
     return {"bf16": torch.bfloat16, "f32": torch.float32}[name]
 
 
+def _mark(events, name):
+    if events is None:
+        return None
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    events.setdefault(name, []).append((start, end))
+    return end
+
+
+def _done(end):
+    if end is not None:
+        end.record()
+
+
 class DisplacedLayer:
     def __init__(self, cfg, convs: Sequence[Tuple["np.ndarray", "np.ndarray"]], device="cuda"):  # noqa: F821
         self.cfg = cfg
@@ -56,8 +70,13 @@ class DisplacedLayer:
         return t.reshape(t.shape[0], -1, t.shape[-1])
 
     # ---- one patch, displaced ------------------------------------------------
-    def step(self, x_patch, i, gn_mode="corrected", update_state=True) -> List[torch.Tensor]:
-        """Patch i's displaced layer step; returns every graph step's patch output."""
+    def step(self, x_patch, i, gn_mode="corrected", update_state=True, events=None) -> List[torch.Tensor]:
+        """Patch i's displaced layer step; returns every graph step's patch output.
+
+        ``events``: optional dict; when given, each call is bracketed by a pair of
+        torch.cuda.Event recorded on the current stream (the stream the library
+        launches on), appended to events[name] as (start, end).
+        """
         c = self.cfg
         p = self.patch(i)
         h = x_patch
@@ -65,6 +84,7 @@ class DisplacedLayer:
         conv_i = 0
         for k, s in enumerate(c.graph):
             out = self.bufs[k]
+            ev = _mark(events, s)
             if s in ("gn", "gn_silu"):
                 dp_groupnorm_async(p, h, c.G, self.table, c.eps, gn_mode, "silu" if s == "gn_silu" else None,
                                    fresh_stats_out=self.fresh_stats, y_patch=out)
@@ -76,22 +96,28 @@ class DisplacedLayer:
                 tok = self._tok(h)
                 st = self._tok(self.maps[k])
                 dp_attention_splice(p, c.heads, tok, tok, tok, st, st, o_patch=self._tok(out))
+            _done(ev)
             outs.append(out)
             h = out
         if update_state:
-            self.splice_state(i, x_patch, outs)
+            self.splice_state(i, x_patch, outs, events)
         return outs
 
-    def splice_state(self, i, x_patch, outs):
+    def splice_state(self, i, x_patch, outs, events=None):
         """Write patch i's fresh statistics and consumer-input bands into the state."""
         c = self.cfg
         p = self.patch(i)
         inputs = [x_patch] + outs[:-1]
         for k, s in enumerate(c.graph):
             if s in ("gn", "gn_silu"):
+                ev = _mark(events, "stats_update")
                 dp_stats_update(c.P, i, self.fresh_stats, self.table)
             elif k in self.maps:
+                ev = _mark(events, "stale_update")
                 dp_stale_update(p, inputs[k], self.maps[k])
+            else:
+                continue
+            _done(ev)
 
     # ---- all patches, synchronous (warm-up) --------------------------------------
     def warmup(self, x_full) -> List[torch.Tensor]:
