@@ -8,15 +8,16 @@
 //   y[b,y,x,o] = bias[o] + sum_{ky,kx,c} w[o,ky,kx,c] * src(b, r0+y+ky-1, x+kx-1, c)
 // src = fresh patch inside the band, stale map at other image rows, 0 outside.
 //
-// bf16 path: implicit GEMM on MFMA (v_mfma_f32_32x32x16_bf16).
+// bf16 path: implicit GEMM on MFMA (v_mfma_f32_16x16x32_bf16).
 //   M = B*h*W output pixels, N = Cout, K = 9*Cin with k = tap*Cin + c, so a
-//   K tile of 64 lies inside one tap.  Weights [Cout][3][3][Cin] are the GEMM's
-//   B^T, row-contiguous in K.  The A loader resolves each pixel's source row
-//   once per tap (fresh band / stale map / zero) and then streams 128-byte
-//   channel runs; rows are staged through LDS with a 16-byte pad per row.
-//   Tile 128 pixels x 160 channels, 4 waves, each wave 32 pixels x 160
-//   channels (5 MFMA blocks).  Small M is split along K; the fp32 partials
-//   are summed in split order by a second kernel (deterministic).
+//   K tile of 64 channels lies inside one tap.  Weights [Cout][3][3][Cin] are
+//   the GEMM's B^T, row-contiguous in K.  The A loader resolves each pixel's
+//   source row once per tap (fresh band / stale map / zero) and streams its
+//   128-byte channel runs straight into LDS with direct-to-LDS loads.  Tile
+//   128 pixels x 160 channels, 4 waves of 64x80; a 2-stage LDS ring of 36 KB
+//   per stage lets two workgroups share a CU so one's waits overlap the
+//   other's MFMAs.  Small M is split along K; the fp32 partials are summed in
+//   split order by a second kernel (deterministic).
 // f32 path: one thread per output element (correctness path for small maps).
 
 #include "dp_device.h"
@@ -28,8 +29,7 @@ namespace {
 constexpr int BM = 128;
 constexpr int BN = 160;
 constexpr int BK = 64;
-constexpr int LDK = BK + 8;  // padded LDS row (bf16 elements)
-constexpr int NB = BN / 32;  // MFMA n-blocks per wave
+constexpr int kStages = 2;   // LDS ring depth: 2 x 36 KB, so two workgroups share a CU
 constexpr int kThreads = 256;
 
 struct ConvArgs {
@@ -45,29 +45,71 @@ struct ConvArgs {
     int ntiles;
 };
 
-__global__ __launch_bounds__(kThreads) void conv3x3_bf16_mfma_kernel(ConvArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDK];
+// ---------------------------------------------------------------------------
+// bf16 implicit GEMM, pipelined through LDS with direct-to-LDS loads.
+//
+// Tile BM=128 pixels x BN output channels, 4 waves in a 2x2 grid, each wave
+// 64 pixels x BN/2 channels as 16x16 blocks of v_mfma_f32_16x16x32_bf16.
+// Every K tile (64 input channels of one tap) of A (128 rows) and B (BN rows)
+// is 128 bytes per row, fetched by global_load_lds_dwordx4 straight into an
+// LDS stage (lane l of a load writes the l-th 16-byte slot of a 1 KB chunk).
+// The 16-byte chunk c of row r sits at slot c ^ (r & 7) so the MFMA operand
+// reads (16 rows x one chunk) spread over the banks.  STAGES stages form a
+// ring: while stage k is multiplied, stages k+1.. are in flight.  A rows
+// whose source is outside the image (or past the last pixel) read a static
+// zero line instead.
+// ---------------------------------------------------------------------------
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __attribute__((aligned(64))) uint4 g_zero_line[8];   // never written: reads as zero
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int BN, int STAGES>
+__global__ __launch_bounds__(256) void conv3x3_bf16_lds_dma_kernel(ConvArgs a) {
+    constexpr int BM2 = 128;
+    constexpr int A_CH = BM2 * 128 / 1024;      // 1 KB chunks per A stage (16)
+    constexpr int B_CH = BN * 128 / 1024;       // per B stage (BN/8)
+    static_assert(A_CH % 4 == 0 && B_CH % 4 == 0, "chunks split over 4 waves");
+    constexpr int A_PW = A_CH / 4;
+    constexpr int B_PW = B_CH / 4;
+    constexpr int LOADS = A_PW + B_PW;          // DMA loads per wave per stage
+    constexpr int STAGE = (A_CH + B_CH) * 1024;
+    constexpr int WN = BN / 2;                  // channels per wave
+    constexpr int NBK = WN / 16;                // 16-wide blocks per wave
+    constexpr int SMEM = STAGES * STAGE > BM2 * BN * 4 ? STAGES * STAGE : BM2 * BN * 4;
+    __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
     const int mt = blockIdx.x / a.ntiles;
-    const int nt = blockIdx.x % a.ntiles;
-    const int m0 = mt * BM;
+    const int nt = blockIdx.x - mt * a.ntiles;
+    const int m0 = mt * BM2;
     const int n0 = nt * BN;
     const int split = blockIdx.y;
     const int kt0 = (int)((int64_t)a.ktiles * split / a.ksplit);
     const int kt1 = (int)((int64_t)a.ktiles * (split + 1) / a.ksplit);
-    const int cpt = a.Cin / BK;  // K tiles per tap
+    const int nkt = kt1 - kt0;
+    const int cpt = a.Cin / 64;
+    const int64_t wrow = 9 * (int64_t)a.Cin;
+    const uint16_t* zero = (const uint16_t*)g_zero_line;
 
-    // ---- per-thread loader state ----
-    const int chunk = tid & 7;   // 16-byte chunk within a 128-byte K row
-    const int lrow = tid >> 3;   // 0..31
-    int pb[4], py[4], px[4];
+    // ---- loader state: this lane's A rows (pixels) and B rows (channels) ----
+    const int sub = lane >> 3;          // row within a 1 KB chunk (8 rows of 128 B)
+    const int slot = lane & 7;          // physical 16-byte slot in the row
+    int pb[A_PW], py[A_PW], px[A_PW], achunk[A_PW];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int m = m0 + lrow + 32 * j;
+    for (int j = 0; j < A_PW; ++j) {
+        const int row = (wave * A_PW + j) * 8 + sub;
+        achunk[j] = slot ^ (row & 7);
+        const int m = m0 + row;
         if (m < a.M) {
             const int hw = a.h * a.W;
             pb[j] = m / hw;
@@ -79,101 +121,138 @@ __global__ __launch_bounds__(kThreads) void conv3x3_bf16_mfma_kernel(ConvArgs a)
             py[j] = px[j] = 0;
         }
     }
-    const uint16_t* asrc[4];
-    bool aval[4];
+    const uint16_t* bsrc[B_PW];
+#pragma unroll
+    for (int j = 0; j < B_PW; ++j) {
+        const int row = (wave * B_PW + j) * 8 + sub;
+        const int co = n0 + row;
+        const int ch = slot ^ (row & 7);
+        bsrc[j] = co < a.Cout ? a.w + co * wrow + ch * 8 : nullptr;
+    }
+    const uint16_t* asrc[A_PW];
     int cur_tap = -1;
 
-    auto set_tap = [&](int tap) {
-        const int ky = tap / 3, kx = tap - 3 * (tap / 3);
+    f32x4 acc[4][NBK];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = a.r0 + py[j] + ky - 1;
-            const int xx = px[j] + kx - 1;
-            aval[j] = pb[j] >= 0 && r >= 0 && r < a.H && xx >= 0 && xx < a.W;
-            const bool fresh = r >= a.r0 && r < a.r0 + a.h;
-            const int64_t fo = (((int64_t)pb[j] * a.h + (r - a.r0)) * a.W + xx) * a.Cin;
-            const int64_t so = (((int64_t)pb[j] * a.H + r) * a.W + xx) * a.Cin;
-            asrc[j] = aval[j] ? (fresh ? a.xp + fo : a.xs + so) : a.xp;
-        }
-    };
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int n = 0; n < NBK; ++n) acc[i][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    uint4 ra[4], rb[NB];
-    auto load_tile = [&](int kt) {
-        const int tap = kt / cpt;
-        const int c0 = (kt - tap * cpt) * BK + chunk * 8;
-        if (tap != cur_tap) {
-            set_tap(tap);
-            cur_tap = tap;
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            ra[j] = aval[j] ? *(const uint4*)(asrc[j] + c0) : make_uint4(0, 0, 0, 0);
-        const int64_t kofs = (int64_t)kt * BK + chunk * 8;
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int co = n0 + lrow + 32 * j;
-            rb[j] = co < a.Cout ? *(const uint4*)(a.w + (int64_t)co * 9 * a.Cin + kofs) : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) *(uint4*)(As + (lrow + 32 * j) * LDK + chunk * 8) = ra[j];
-#pragma unroll
-        for (int j = 0; j < NB; ++j) *(uint4*)(Bs + (lrow + 32 * j) * LDK + chunk * 8) = rb[j];
-    };
+#define DP_ISSUE_STAGE(KT, BUF)                                                                     \
+    do {                                                                                            \
+        const int kt_ = (KT);                                                                       \
+        const int tap_ = kt_ / cpt;                                                                 \
+        const int cc_ = kt_ - tap_ * cpt;                                                           \
+        const int coff_ = cc_ * 64;                                                                 \
+        const int64_t kofs_ = (int64_t)tap_ * a.Cin + coff_;                                        \
+        if (tap_ != cur_tap) {                                                                      \
+            cur_tap = tap_;                                                                         \
+            const int ky_ = tap_ / 3, kx_ = tap_ - 3 * (tap_ / 3);                                  \
+            _Pragma("unroll") for (int j = 0; j < A_PW; ++j) {                                      \
+                const int r_ = a.r0 + py[j] + ky_ - 1;                                              \
+                const int x_ = px[j] + kx_ - 1;                                                     \
+                const bool ok_ = pb[j] >= 0 && r_ >= 0 && r_ < a.H && x_ >= 0 && x_ < a.W;          \
+                const bool fr_ = r_ >= a.r0 && r_ < a.r0 + a.h;                                     \
+                const int64_t fo_ = (((int64_t)pb[j] * a.h + (r_ - a.r0)) * a.W + x_) * a.Cin;      \
+                const int64_t so_ = (((int64_t)pb[j] * a.H + r_) * a.W + x_) * a.Cin;               \
+                asrc[j] = ok_ ? (fr_ ? a.xp + fo_ : a.xs + so_) + achunk[j] * 8 : nullptr;          \
+            }                                                                                       \
+        }                                                                                           \
+        char* st_ = smem + (BUF) * STAGE;                                                           \
+        _Pragma("unroll") for (int j = 0; j < A_PW; ++j) {                                          \
+            const uint16_t* g_ = asrc[j] ? asrc[j] + coff_ : zero;                                  \
+            __builtin_amdgcn_global_load_lds((const void*)g_, (lds_void*)(st_ + (wave * A_PW + j) * 1024), \
+                                             16, 0, 0);                                            \
+        }                                                                                           \
+        _Pragma("unroll") for (int j = 0; j < B_PW; ++j) {                                          \
+            const uint16_t* g_ = bsrc[j] ? bsrc[j] + kofs_ : zero;                                  \
+            __builtin_amdgcn_global_load_lds((const void*)g_,                                      \
+                                             (lds_void*)(st_ + A_CH * 1024 + (wave * B_PW + j) * 1024), \
+                                             16, 0, 0);                                            \
+        }                                                                                           \
+    } while (0)
 
-    f32x16 acc[NB];
-#pragma unroll
-    for (int n = 0; n < NB; ++n)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[n][e] = 0.f;
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nkt) DP_ISSUE_STAGE(kt0 + s, s);
 
-    if (kt0 < kt1) {
-        load_tile(kt0);
-        store_tile();
+    // operand read offsets: row (l & 15) of a 16-row block, chunk (ks*4 + l/16) swizzled by (l & 7)
+    const int frow = lane & 15;
+    const int aoff = (wm * 64 + frow) * 128;
+    const int boff = A_CH * 1024 + (wn * WN + frow) * 128;
+    const int p0 = ((0 * 4 + (lane >> 4)) ^ (lane & 7)) * 16;
+    const int p1 = ((1 * 4 + (lane >> 4)) ^ (lane & 7)) * 16;
+
+    for (int it = 0; it < nkt; ++it) {
+        const int ahead = nkt - 1 - it;     // stages issued after this one, capped
+        if (ahead >= STAGES - 2)
+            wait_vmcnt<(STAGES - 2) * LOADS>();
+        else if (STAGES > 3 && ahead == 1)
+            wait_vmcnt<LOADS>();
+        else
+            wait_vmcnt<0>();
         __syncthreads();
-    }
-    const int arow = wave * 32 + (lane & 31);
-    const int kl = (lane >> 5) * 8;
-    for (int kt = kt0; kt < kt1; ++kt) {
-        const bool more = kt + 1 < kt1;
-        if (more) load_tile(kt + 1);
+        if (it + STAGES - 1 < nkt) DP_ISSUE_STAGE(kt0 + it + STAGES - 1, (it + STAGES - 1) % STAGES);
+        const char* st = smem + (it % STAGES) * STAGE;
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const bf16x8 af = *(const bf16x8*)(As + arow * LDK + ks * 16 + kl);
+        for (int ks = 0; ks < 2; ++ks) {
+            const int po = ks ? p1 : p0;
+            bf16x8 af[4];
 #pragma unroll
-            for (int n = 0; n < NB; ++n) {
-                const bf16x8 bfr = *(const bf16x8*)(Bs + (n * 32 + (lane & 31)) * LDK + ks * 16 + kl);
-                acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc[n], 0, 0, 0);
+            for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8*)(st + aoff + i * 16 * 128 + po);
+#pragma unroll
+            for (int n = 0; n < NBK; ++n) {
+                const bf16x8 bfr = *(const bf16x8*)(st + boff + n * 16 * 128 + po);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr, acc[i][n], 0, 0, 0);
             }
         }
-        __syncthreads();
-        if (more) {
-            store_tile();
-            __syncthreads();
-        }
     }
+#undef DP_ISSUE_STAGE
+    __syncthreads();   // all waves done with the ring; reuse it for the output tile
 
-    // ---- epilogue: lane holds column (l & 31) of each n-block, rows 8q + 4(l>>5) + r ----
-    const int col = lane & 31;
-    const int rbase = wave * 32 + 4 * (lane >> 5);
+    // ---- epilogue through LDS: lane holds pixel 4*(l/16)+r, channel l%16 of each block ----
+    const int ecol = lane & 15;
+    const int erow = 4 * (lane >> 4);
+    if (a.ksplit == 1) {
+        uint16_t* tile = (uint16_t*)smem;   // [BM2][BN] bf16
 #pragma unroll
-    for (int n = 0; n < NB; ++n) {
-        const int co = n0 + n * 32 + col;
-        if (co >= a.Cout) continue;
-        const float bv = (a.ksplit == 1 && a.bias) ? a.bias[co] : 0.f;
+        for (int n = 0; n < NBK; ++n) {
+            const int ch = wn * WN + n * 16 + ecol;
+            const float bv = (a.bias && n0 + ch < a.Cout) ? a.bias[n0 + ch] : 0.f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m0 + rbase + 8 * q + r;
-                if (m >= a.M) continue;
-                const float v = acc[n][4 * q + r];
-                if (a.ksplit == 1)
-                    a.y[(int64_t)m * a.Cout + co] = f32_to_bf16(v + bv);
-                else
-                    a.part[((int64_t)split * a.M + m) * a.Cout + co] = v;
-            }
+                for (int r = 0; r < 4; ++r)
+                    tile[(wm * 64 + i * 16 + erow + r) * BN + ch] = f32_to_bf16(acc[i][n][r] + bv);
+        }
+        __syncthreads();
+        constexpr int CPR = BN * 2 / 16;    // 16-byte chunks per output row
+        for (int q = tid; q < BM2 * CPR; q += 256) {
+            const int row = q / CPR, c16 = q - (q / CPR) * CPR;
+            const int m = m0 + row, co = n0 + c16 * 8;
+            if (m < a.M && co < a.Cout)
+                *(uint4*)(a.y + (int64_t)m * a.Cout + co) = *(const uint4*)(tile + row * BN + c16 * 8);
+        }
+    } else {
+        float* tile = (float*)smem;         // [BM2][BN] fp32
+#pragma unroll
+        for (int n = 0; n < NBK; ++n) {
+            const int ch = wn * WN + n * 16 + ecol;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) tile[(wm * 64 + i * 16 + erow + r) * BN + ch] = acc[i][n][r];
+        }
+        __syncthreads();
+        constexpr int CPR = BN * 4 / 16;
+        float* part = a.part + (int64_t)split * a.M * a.Cout;
+        for (int q = tid; q < BM2 * CPR; q += 256) {
+            const int row = q / CPR, c16 = q - (q / CPR) * CPR;
+            const int m = m0 + row, co = n0 + c16 * 4;
+            if (m < a.M && co < a.Cout)
+                *(float4*)(part + (int64_t)m * a.Cout + co) = *(const float4*)(tile + row * BN + c16 * 4);
+        }
     }
 }
 
@@ -254,8 +333,9 @@ ConvPlan plan_conv(const Geom& g, int Cout, bool bf16) {
     const int tiles = p.mtiles * p.ntiles;
     int ks = 1;
     if (tiles < 256) {
+        // split K until about 256 workgroups, keeping >= 4 K tiles per split
         ks = (256 + tiles - 1) / tiles;
-        const int maxk = p.ktiles / 4 > 0 ? p.ktiles / 4 : 1;  // keep >= 4 K tiles per split
+        const int maxk = p.ktiles / 4 > 0 ? p.ktiles / 4 : 1;
         if (ks > maxk) ks = maxk;
         if (ks > 32) ks = 32;
     }
@@ -294,7 +374,7 @@ hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout,
     a.ksplit = plan.ksplit;
     a.ntiles = plan.ntiles;
     dim3 grid((unsigned)(plan.mtiles * plan.ntiles), (unsigned)plan.ksplit);
-    conv3x3_bf16_mfma_kernel<<<grid, kThreads, 0, stream>>>(a);
+    conv3x3_bf16_lds_dma_kernel<BN, kStages><<<grid, kThreads, 0, stream>>>(a);
     if (plan.ksplit > 1) {
         const int64_t total4 = (int64_t)a.M * Cout / 4;
         conv_splitk_reduce_kernel<<<(unsigned)((total4 + 255) / 256), 256, 0, stream>>>(
