@@ -29,10 +29,8 @@ namespace dp {
 namespace {
 
 constexpr int D = 64;
-constexpr int QT = 128;         // queries per workgroup
 constexpr int KT = 64;          // keys per tile
-constexpr int LDKS = D + 8;     // K tile row stride (bf16)
-constexpr int LDVT = KT + 8;    // V^T tile row stride (bf16)
+constexpr int kStages = 4;      // LDS ring depth (16 KB per stage)
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;
@@ -69,52 +67,53 @@ __device__ __forceinline__ bf16x8 pack_probs(const f32x16& p) {
     return __builtin_bit_cast(bf16x8, raw);
 }
 
-__device__ __forceinline__ bf16x8 load_vt(const uint16_t* vrow) {
-    const uint2 lo = *(const uint2*)vrow;
-    const uint2 hi = *(const uint2*)(vrow + 8);
-    return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((vector_size(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __attribute__((aligned(64))) uint4 g_attn_zero[8];   // never written: a zero key/value row
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-__device__ __forceinline__ void stage_kv(uint16_t* Ks, uint16_t* Vt, int kr, int chunk, const uint4& k4,
-                                         const uint4& v4) {
-    *(uint4*)(Ks + kr * LDKS + chunk * 8) = k4;
-    uint16_t* vt = Vt + chunk * 8 * LDVT + kr;
-    vt[0 * LDVT] = (uint16_t)(v4.x & 0xffffu);
-    vt[1 * LDVT] = (uint16_t)(v4.x >> 16);
-    vt[2 * LDVT] = (uint16_t)(v4.y & 0xffffu);
-    vt[3 * LDVT] = (uint16_t)(v4.y >> 16);
-    vt[4 * LDVT] = (uint16_t)(v4.z & 0xffffu);
-    vt[5 * LDVT] = (uint16_t)(v4.z >> 16);
-    vt[6 * LDVT] = (uint16_t)(v4.w & 0xffffu);
-    vt[7 * LDVT] = (uint16_t)(v4.w >> 16);
+// 4 bf16 of V^T for the PV operand via the transposing LDS read (see the lane map below).
+__device__ __forceinline__ s16x4 tr_read(const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
 }
 
-__device__ __forceinline__ void fetch_kv(const AttnArgs& a, int b, int n, int col, uint4& k4, uint4& v4) {
-    if (n < a.N) {
-        k4 = *(const uint4*)kv_row(a.k, a.ks, b, n, a, col);
-        v4 = *(const uint4*)kv_row(a.v, a.vs, b, n, a, col);
-    } else {
-        k4 = v4 = make_uint4(0, 0, 0, 0);
-    }
-}
-
-__global__ __launch_bounds__(kThreads) void attn_bf16_d64_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * LDKS];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * LDVT];
+// ---------------------------------------------------------------------------
+// bf16 flash attention, d = 64.  K and V tiles of 64 keys arrive by
+// global_load_lds_dwordx4 in a STAGES-deep LDS ring (16 KB per stage, rows of
+// 128 bytes, 16-byte chunk c of row r at slot c ^ (r & 7)); the loader picks
+// the fresh patch or the stale map per key row.  S^T = K Q^T per wave (lane
+// = query).  The PV operand V^T is read with ds_read_b64_tr_b16: within a
+// 16-lane group, lane c receives element c%4 of the 8-byte reads of lanes
+// c/4, c/4+4, c/4+8, c/4+12, so lane j reads key (j/4) of a 4-key group at
+// dims 4*(j%4)..+3 and each lane ends up holding one dim for 4 keys -- V
+// stays row-major in LDS.
+// ---------------------------------------------------------------------------
+template <int STAGES, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void attn_bf16_d64_kernel(AttnArgs a) {
+    constexpr int STAGE = 16 * 1024;          // K tile 8 KB + V tile 8 KB
+    constexpr int LOADS = 16 / WAVES;         // DMA loads (1 KB chunks) per wave per stage
+    constexpr int QTW = 32 * WAVES;           // queries per workgroup
+    __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int hsel = lane >> 5;          // which half of the wave
+    const int hsel = lane >> 5;
     const int bh = blockIdx.y;
     const int b = bh / a.heads;
     const int e = bh - b * a.heads;
     const int split = blockIdx.z;
-    const int myq = blockIdx.x * QT + wave * 32 + (lane & 31);
+    const int myq = blockIdx.x * QTW + wave * 32 + (lane & 31);
     const bool qvalid = myq < a.Nq;
     const int col0 = e * D;
 
-    // Q^T fragments (B operand): lane gives query myq, dims ks*16 + 8*hsel .. +7
     bf16x8 q0, q1, q2, q3;
     {
         uint4 r0 = make_uint4(0, 0, 0, 0), r1 = r0, r2 = r0, r3 = r0;
@@ -133,95 +132,144 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_d64_kernel(AttnArgs a) {
 
     const int t0 = (int)((int64_t)a.kv_tiles * split / a.kvsplit);
     const int t1 = (int)((int64_t)a.kv_tiles * (split + 1) / a.kvsplit);
+    const int nt = t1 - t0;
 
-    // loader: thread -> key rows lrow, lrow+32; 16-byte chunk `chunk` of the 128-byte head slice
-    const int chunk = tid & 7;
-    const int lrow = tid >> 3;
-    const int lcol = col0 + chunk * 8;
-    uint4 k4a, v4a, k4b, v4b;
+    // DMA lanes: wave w issues chunks w*LOADS+j (0..7 K rows, 8..15 V rows), 8 rows of 128 B per chunk
+    const int sub = lane >> 3;
+    const int slot = lane & 7;
+    const uint16_t* zero = (const uint16_t*)g_attn_zero;
+#define DPA_ISSUE(T, BUF)                                                                           \
+    do {                                                                                            \
+        char* st_ = smem + (BUF) * STAGE;                                                           \
+        _Pragma("unroll") for (int j = 0; j < LOADS; ++j) {                                         \
+            const int q_ = wave * LOADS + j;                                                        \
+            const int row_ = (q_ & 7) * 8 + sub;                                                    \
+            const int n_ = (T) * KT + row_;                                                         \
+            const int ch_ = (slot ^ (row_ & 7)) * 8;                                                \
+            const uint16_t* fr_ = q_ < 8 ? a.k : a.v;                                               \
+            const uint16_t* sl_ = q_ < 8 ? a.ks : a.vs;                                             \
+            const uint16_t* g_ = n_ < a.N ? kv_row(fr_, sl_, b, n_, a, col0 + ch_) : zero;          \
+            __builtin_amdgcn_global_load_lds((const void*)g_, (lds_void*)(st_ + q_ * 1024), 16, 0, 0); \
+        }                                                                                           \
+    } while (0)
+
+    // K operand reads (A of S^T): key row kb*32 + (l & 31), 16-byte chunk 2*ks + hsel
+    const int krow = lane & 31;
+    int koff[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) koff[ks] = krow * 128 + (((2 * ks + hsel) ^ (krow & 7)) * 16);
+    // V^T operand reads via tr reads: lane l = 16g + j; key 16u + 4*(g>>1) + 8h + (j>>2),
+    // dims 32*db + 16*(g&1) + 4*(j&3) .. +3
+    const int gq = lane >> 4, jl = lane & 15;
+    int voff[2][2];   // [h][db] byte offsets inside the V tile for u = 0
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+            const int row = 4 * (gq >> 1) + 8 * h + (jl >> 2);          // + 16u (u*16 rows keeps row & 7)
+            const int d = 32 * db + 16 * (gq & 1) + 4 * (jl & 3);
+            voff[h][db] = 8192 + row * 128 + (((d >> 3) ^ (row & 7)) * 16) + (d & 7) * 2;
+        }
 
     f32x16 o0, o1;
 #pragma unroll
     for (int i = 0; i < 16; ++i) o0[i] = o1[i] = 0.f;
     float m_run = kNegBig;
     float l_run = 0.f;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    if (t0 < t1) {
-        fetch_kv(a, b, t0 * KT + lrow, lcol, k4a, v4a);
-        fetch_kv(a, b, t0 * KT + lrow + 32, lcol, k4b, v4b);
-        stage_kv(Ks, Vt, lrow, chunk, k4a, v4a);
-        stage_kv(Ks, Vt, lrow + 32, chunk, k4b, v4b);
-        __syncthreads();
+    if (nt > 0) {
+        for (int s = 0; s < STAGES - 1; ++s)
+            if (s < nt) DPA_ISSUE(t0 + s, s);
     }
-    const uint16_t* krow0 = Ks + (lane & 31) * LDKS + hsel * 8;
-    const uint16_t* krow1 = krow0 + 32 * LDKS;
-    const uint16_t* vrow0 = Vt + (lane & 31) * LDVT + 4 * hsel;
-    const uint16_t* vrow1 = vrow0 + 32 * LDVT;
-    for (int t = t0; t < t1; ++t) {
-        const bool more = t + 1 < t1;
-        if (more) {
-            fetch_kv(a, b, (t + 1) * KT + lrow, lcol, k4a, v4a);
-            fetch_kv(a, b, (t + 1) * KT + lrow + 32, lcol, k4b, v4b);
-        }
+    for (int it = 0; it < nt; ++it) {
+        const int t = t0 + it;
+        const int ahead = nt - 1 - it;
+        if (STAGES >= 4 && ahead >= 2) wait_vmcnt<2 * LOADS>();
+        else if (STAGES >= 3 && ahead >= 1) wait_vmcnt<LOADS>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (it + STAGES - 1 < nt) DPA_ISSUE(t + STAGES - 1, (it + STAGES - 1) % STAGES);
+        const char* st = smem + (it % STAGES) * STAGE;
+
         // S^T[key][query], keys kb*32 + 8q + 4*hsel + r in s_kb[4q + r]
         f32x16 s0, s1;
 #pragma unroll
         for (int i = 0; i < 16; ++i) s0[i] = s1[i] = 0.f;
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(krow0 + 0), q0, s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(krow1 + 0), q0, s1, 0, 0, 0);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(krow0 + 16), q1, s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(krow1 + 16), q1, s1, 0, 0, 0);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(krow0 + 32), q2, s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(krow1 + 32), q2, s1, 0, 0, 0);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(krow0 + 48), q3, s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(krow1 + 48), q3, s1, 0, 0, 0);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + koff[0]), q0, s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + 4096 + koff[0]), q0, s1, 0, 0, 0);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + koff[1]), q1, s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + 4096 + koff[1]), q1, s1, 0, 0, 0);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + koff[2]), q2, s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + 4096 + koff[2]), q2, s1, 0, 0, 0);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + koff[3]), q3, s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + 4096 + koff[3]), q3, s1, 0, 0, 0);
 
-        // keys >= N (ragged last tile) are excluded from the max and get p = 0
-        const int kvalid = a.N - (t * KT + 4 * hsel);  // element at block offset off is valid iff off < kvalid
-        float mx = kNegBig;
+        // keys >= N occur only in a ragged last tile: excluded from the max, p = 0
+        if ((t + 1) * KT > a.N) {
+            const int kvalid = a.N - (t * KT + 4 * hsel);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int off = 8 * (i >> 2) + (i & 3);
-            mx = fmaxf(mx, off < kvalid ? s0[i] : kNegBig);
-            mx = fmaxf(mx, off + 32 < kvalid ? s1[i] : kNegBig);
+            for (int i = 0; i < 16; ++i) {
+                const int off = 8 * (i >> 2) + (i & 3);
+                if (off >= kvalid) s0[i] = -INFINITY;
+                if (off + 32 >= kvalid) s1[i] = -INFINITY;
+            }
         }
+        float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // rescale the running sum and O only when some query's max grew
         const float m_new = fmaxf(m_run, mx * a.sc);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        float psum = 0.f;
+        if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            l_run *= alpha;
+            o0 *= alpha;
+            o1 *= alpha;
+            m_run = m_new;
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int off = 8 * (i >> 2) + (i & 3);
-            const float p0 = off < kvalid ? __builtin_amdgcn_exp2f(fmaf(s0[i], a.sc, -m_new)) : 0.f;
-            const float p1 = off + 32 < kvalid ? __builtin_amdgcn_exp2f(fmaf(s1[i], a.sc, -m_new)) : 0.f;
-            psum += p0 + p1;
-            s0[i] = p0;
-            s1[i] = p1;
+            s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], a.sc, -m_run));
+            s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], a.sc, -m_run));
         }
-        l_run = fmaf(l_run, alpha, psum);
-        o0 *= alpha;
-        o1 *= alpha;
-        // O^T[d][query] += V^T P^T over 4 steps of 16 keys (keys 16u + 4*hsel + {0..3, 8..11})
+        // P^T operands (keys 16u + 4*hsel + {0..3, 8..11}); the row sum adds the same bf16 values
         const bf16x8 p0 = pack_probs<0>(s0);
         const bf16x8 p1 = pack_probs<2>(s0);
         const bf16x8 p2 = pack_probs<0>(s1);
         const bf16x8 p3 = pack_probs<2>(s1);
-        o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_vt(vrow0 + 0), p0, o0, 0, 0, 0);
-        o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_vt(vrow1 + 0), p0, o1, 0, 0, 0);
-        o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_vt(vrow0 + 16), p1, o0, 0, 0, 0);
-        o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_vt(vrow1 + 16), p1, o1, 0, 0, 0);
-        o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_vt(vrow0 + 32), p2, o0, 0, 0, 0);
-        o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_vt(vrow1 + 32), p2, o1, 0, 0, 0);
-        o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_vt(vrow0 + 48), p3, o0, 0, 0, 0);
-        o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(load_vt(vrow1 + 48), p3, o1, 0, 0, 0);
-        __syncthreads();
-        if (more) {
-            stage_kv(Ks, Vt, lrow, chunk, k4a, v4a);
-            stage_kv(Ks, Vt, lrow + 32, chunk, k4b, v4b);
-            __syncthreads();
-        }
+#define DPA_SUM(PV)                                                                                 \
+    do {                                                                                            \
+        const uint4 w_ = __builtin_bit_cast(uint4, PV);                                             \
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w_.x), ones, l_run, false); \
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w_.y), ones, l_run, false); \
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w_.z), ones, l_run, false); \
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w_.w), ones, l_run, false); \
+    } while (0)
+        DPA_SUM(p0);
+        DPA_SUM(p1);
+        DPA_SUM(p2);
+        DPA_SUM(p3);
+#undef DPA_SUM
+#define DPA_PV(U, PU)                                                                               \
+    do {                                                                                            \
+        const char* vb_ = st + (U) * 16 * 128;                                                      \
+        const s16x4 a0_ = tr_read(vb_ + voff[0][0]);                                                \
+        const s16x4 b0_ = tr_read(vb_ + voff[1][0]);                                                \
+        const s16x4 a1_ = tr_read(vb_ + voff[0][1]);                                                \
+        const s16x4 b1_ = tr_read(vb_ + voff[1][1]);                                                \
+        const bf16x8 v0_ = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0_, b0_, 0, 1, 2, 3, 4, 5, 6, 7)); \
+        const bf16x8 v1_ = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a1_, b1_, 0, 1, 2, 3, 4, 5, 6, 7)); \
+        o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0_, PU, o0, 0, 0, 0);                          \
+        o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1_, PU, o1, 0, 0, 0);                          \
+    } while (0)
+        DPA_PV(0, p0);
+        DPA_PV(1, p1);
+        DPA_PV(2, p2);
+        DPA_PV(3, p3);
+#undef DPA_PV
     }
+#undef DPA_ISSUE
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     if (!qvalid) return;
@@ -342,13 +390,28 @@ AttnPlan plan_attention(const Geom& g, int heads, int head_dim, bool bf16) {
         return p;
     }
     p.kind = 1;
-    p.qtile = QT;
     const int64_t Nq = g.band_tokens();
-    p.qtiles = (int)((Nq + QT - 1) / QT);
+    // 8 waves (256 queries) share each K/V tile when the band is large; 4 waves otherwise
+    p.qtile = Nq >= 2048 ? 256 : 128;
+    p.qtiles = (int)((Nq + p.qtile - 1) / p.qtile);
     const int kv_tiles = (int)((g.map_tokens() + KT - 1) / KT);
     const int64_t units = (int64_t)p.qtiles * g.B * heads;
+    // Resident workgroups (register-limited): 2 of 4 waves or 1 of 8 waves per CU, 256 CUs.
+    // Pick the key split that fills whole rounds of workgroups best (>= 2 key tiles per
+    // split), preferring fewer splits.
+    const int64_t slots = p.qtile == 256 ? 256 : 512;
     int ks = 1;
-    while (units * ks * 2 <= 512 && kv_tiles / (ks * 2) >= 2) ks *= 2;
+    double best = 0.0;
+    for (int k = 1; k <= 16; ++k) {
+        if (k > 1 && kv_tiles / k < 2) break;
+        const int64_t wgs = units * k;
+        const int64_t rounds = (wgs + slots - 1) / slots;
+        const double eff = (double)wgs / (double)(rounds * slots);
+        if (eff > best + 0.04) {
+            best = eff;
+            ks = k;
+        }
+    }
     p.kvsplit = ks;
     p.ws_bytes = ks > 1 ? (size_t)ks * g.B * heads * Nq * (D * sizeof(float) + sizeof(float2)) : 0;
     (void)head_dim;
@@ -401,7 +464,10 @@ hipError_t launch_attention(const Geom& g, const AttnPlan& plan, bool bf16, int 
     a.kvsplit = plan.kvsplit;
     a.sc = scale * kLog2e;
     dim3 grid((unsigned)plan.qtiles, (unsigned)(g.B * heads), (unsigned)plan.kvsplit);
-    attn_bf16_d64_kernel<<<grid, kThreads, 0, stream>>>(a);
+    if (plan.qtile == 256)
+        attn_bf16_d64_kernel<kStages, 8><<<grid, 512, 0, stream>>>(a);
+    else
+        attn_bf16_d64_kernel<kStages, 4><<<grid, 256, 0, stream>>>(a);
     if (plan.kvsplit > 1) {
         const int64_t threads = (int64_t)g.B * heads * Nq * (D / 4);
         attn_merge_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(

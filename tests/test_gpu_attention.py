@@ -55,6 +55,7 @@ def test_c4b_sampled_rows():
     (2, 6, 30, 3, 3, 1),     # batch 2, Nq = 60, N = 180, band straddles key tiles
     (1, 40, 10, 1, 2, 1),    # Nq = 200: ragged query tile
     (1, 8, 24, 4, 1, 0),     # one patch: plain self-attention
+    (2, 48, 90, 1, 2, 1),    # Nq = 2160 (8-wave tiles, ragged), N = 4320 (ragged key tiles), batch 2
 ])
 def test_ragged_bf16(B, H, W, heads, P, i):
     announce("attention ragged", B, H, W, heads, P, i)
