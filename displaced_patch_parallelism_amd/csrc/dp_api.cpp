@@ -187,8 +187,11 @@ dp_status dp_groupnorm_async(const dp_patch* p, dp_dtype dtype, int32_t G, float
     if (y_patch && (overlaps(y_patch, band_bytes, stale_stats, table_bytes) ||
                     overlaps(y_patch, band_bytes, ws, plan.ws_bytes)))
         return fail(DP_ERR_ARG, "y_patch overlaps the statistics table or the workspace");
+    // fresh_stats_out may be slot i of the table in CORRECTED mode, which never reads slot i
+    const bool stats_in_slot_i = stale_stats && mode == DP_GN_CORRECTED &&
+                                 fresh_stats_out == stale_stats + (size_t)g.i * g.B * G * 2;
     if (fresh_stats_out && (overlaps(fresh_stats_out, stats_bytes, x_patch, band_bytes) ||
-                            overlaps(fresh_stats_out, stats_bytes, stale_stats, table_bytes) ||
+                            (!stats_in_slot_i && overlaps(fresh_stats_out, stats_bytes, stale_stats, table_bytes)) ||
                             overlaps(fresh_stats_out, stats_bytes, y_patch, band_bytes) ||
                             overlaps(fresh_stats_out, stats_bytes, ws, plan.ws_bytes)))
         return fail(DP_ERR_ARG, "fresh_stats_out overlaps an input, y_patch or the workspace");

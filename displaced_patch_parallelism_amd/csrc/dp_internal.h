@@ -27,8 +27,9 @@ struct GnPlan {
     int vpt;          // vectors per token (C / vec)
     int rows;         // tokens a stats block reads in parallel
     int threads;      // stats block size = vpt * rows
-    int nblk;         // stats blocks per batch
-    int tok_per_blk;  // tokens per stats block
+    int nblk;         // statistics blocks per batch
+    int tok_per_blk;  // tokens per statistics block (the same split for every path, so the
+                      // fresh moments are bitwise identical however they are computed)
     size_t partial_floats;  // B * nblk * G * 2
     size_t ws_bytes;
 };

@@ -9,19 +9,19 @@
 // (m_i, q_i) plus the previous step's moments of every other band, each
 // band weighted 1/P; variance = E[x^2] - E[x]^2 clamped at 0.
 //
-// Three launches, all streaming over the band [B][h*W][C] with 16-byte
-// vectors:
-//   1. gn_stats:    each block owns a token range; thread (cv, r) owns
-//                   channel vector cv and walks tokens r, r+R, ...; fp32
-//                   per-channel sums, reduced through LDS in a fixed order to
-//                   per-group partial (sum, sum of squares) per block.
-//   2. gn_finalize: one wave per (b, g) adds the block partials in a fixed
-//                   order, emits (m_i, q_i), combines with the stale table
-//                   and stores (mean, rstd).
-//   3. gn_apply:    y = x * a[c] + b'[c] with a = rstd*gamma,
-//                   b' = beta - mean*a, optional SiLU, rounded to the
-//                   storage type.
+// Two launches, both streaming the band [B][h*W][C] with 16-byte vectors.
+// A block is vpt x R threads: thread (cv, r) owns channel vector cv (8 bf16
+// or 4 f32 channels) and walks token rows r, r+R, ... of the block's range
+// with four loads in flight, so per-channel state stays in registers.
+//   1. gn_stats: fp32 per-channel sums, reduced through LDS in a fixed order
+//      to per-group (sum, sum of squares) partials [block][B][G].
+//   2. gn_apply: every block first adds the partials of its batch in a fixed
+//      order, forms the fresh moments (block 0 stores them), combines them
+//      with the stale table into (mean, rstd) and per-channel (scale, shift),
+//      then writes y = x*scale + shift (+ SiLU) rounded to the storage type.
+// Both kernels use the same token split (about one block per CU).
 // No atomics: results are bitwise reproducible.
+
 
 #include "dp_device.h"
 #include "dp_internal.h"
@@ -29,12 +29,9 @@
 namespace dp {
 namespace {
 
-constexpr int kApplyThreads = 256;
-constexpr int kApplyUnroll = 4;
 
 template <bool BF16>
-__device__ __forceinline__ void load_vec(const void* base, int64_t vec_index, float* f) {
-    const uint4 v = ((const uint4*)base)[vec_index];
+__device__ __forceinline__ void to_f32(const uint4& v, float* f) {
     if (BF16) {
         unpack8(v, f);
     } else {
@@ -45,7 +42,7 @@ __device__ __forceinline__ void load_vec(const void* base, int64_t vec_index, fl
     }
 }
 
-// partial[(b*nblk + blk)*G + g] = (sum x, sum x^2) over the block's tokens.
+// partial[(blk*B + b)*G + g] = (sum x, sum x^2) over the block's tokens.
 template <bool BF16>
 __global__ void gn_stats_kernel(const void* __restrict__ x, int64_t tokens, int C, int G, int vpt, int rows,
                                 int tok_per_blk, float2* __restrict__ partial) {
@@ -62,10 +59,26 @@ __global__ void gn_stats_kernel(const void* __restrict__ x, int64_t tokens, int 
     float s[VEC], q[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) s[e] = q[e] = 0.f;
-    const int64_t batch_vec0 = (int64_t)b * tokens * vpt;
-    for (int64_t t = t0 + r; t < t1; t += rows) {
+    const uint4* xb = (const uint4*)x + (int64_t)b * tokens * vpt + cv;
+    int64_t t = t0 + r;
+    for (; t + 3 * rows < t1; t += 4 * rows) {
+        uint4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = xb[(t + u * rows) * vpt];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            float f[VEC];
+            to_f32<BF16>(v[u], f);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                s[e] += f[e];
+                q[e] = fmaf(f[e], f[e], q[e]);
+            }
+        }
+    }
+    for (; t < t1; t += rows) {
         float f[VEC];
-        load_vec<BF16>(x, batch_vec0 + t * vpt + cv, f);
+        to_f32<BF16>(xb[t * vpt], f);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             s[e] += f[e];
@@ -98,116 +111,143 @@ __global__ void gn_stats_kernel(const void* __restrict__ x, int64_t tokens, int 
             a += sh_s[c];
             aq += sh_q[c];
         }
-        partial[((int64_t)b * gridDim.x + blockIdx.x) * G + g] = make_float2(a, aq);
+        partial[((int64_t)blockIdx.x * gridDim.y + b) * G + g] = make_float2(a, aq);
     }
 }
 
-// One wave per (b, g).  meanrstd[b*G + g] = (mean, rstd).
-__global__ __launch_bounds__(256) void gn_finalize_kernel(const float2* __restrict__ partial, int nblk, int B,
-                                                          int G, int P, int i, int mode, float inv_count,
-                                                          float eps, const float* __restrict__ stale,
-                                                          float* __restrict__ fresh_out,
-                                                          float2* __restrict__ meanrstd, int need_norm) {
-    const int lane = threadIdx.x & 63;
-    const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
-    if (wave >= B * G) return;
-    const int b = wave / G, g = wave % G;
-    float a = 0.f, aq = 0.f;
-    for (int j = lane; j < nblk; j += 64) {
-        const float2 v = partial[((int64_t)b * nblk + j) * G + g];
-        a += v.x;
-        aq += v.y;
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        a += __shfl_xor(a, off);
-        aq += __shfl_xor(aq, off);
-    }
-    if (lane != 0) return;
-    const float m = a * inv_count, qm = aq * inv_count;
-    if (fresh_out) {
-        fresh_out[(b * G + g) * 2 + 0] = m;
-        fresh_out[(b * G + g) * 2 + 1] = qm;
-    }
-    if (!need_norm) return;
-    float E = m, Q = qm;
-    if (mode != 1) {  // corrected (0) or stale (2): sum the table in band order
-        float se = 0.f, sq = 0.f;
-        for (int j = 0; j < P; ++j) {
-            if (mode == 0 && j == i) {
-                se += m;
-                sq += qm;
-            } else {
-                se += stale[((int64_t)j * B + b) * G * 2 + g * 2 + 0];
-                sq += stale[((int64_t)j * B + b) * G * 2 + g * 2 + 1];
-            }
+struct GnApplyArgs {
+    const void* x;
+    void* y;                 // null: moments only
+    const float2* partial;   // [nblk][B][G]
+    int nblk;
+    int64_t tokens;          // per batch
+    int B, C, G, P, i, mode, vpt, rows, tok_per_blk;
+    float inv_count, eps;
+    const float* stale;      // [P][B][G][2]
+    const float* gamma;
+    const float* beta;
+    float* fresh_out;        // [B][G][2] or null
+};
+
+// Every block: (1) adds the stats partials of its batch in a fixed order and
+// forms each group's fresh moments (block 0 of the batch stores them); (2)
+// combines them with the stale table per mode into (mean, rstd) and this
+// thread's per-channel (scale, shift); (3) normalises its token range.
+template <bool BF16, bool SILU>
+__global__ void gn_apply_kernel(GnApplyArgs a) {
+    constexpr int VEC = BF16 ? 8 : 4;
+    extern __shared__ float2 gsh[];          // [lanes_per_g][G] partial sums, then [G] (mean, rstd)
+    const int tid = threadIdx.x;
+    const int b = blockIdx.y;
+    const int G = a.G;
+    const int lanes_per_g = blockDim.x / G;  // >= 1: the plan gives blocks of >= G threads
+    if (tid < lanes_per_g * G) {
+        const int g = tid % G, j0 = tid / G;
+        float sa = 0.f, sq = 0.f;
+        for (int j = j0; j < a.nblk; j += lanes_per_g) {
+            const float2 v = a.partial[((int64_t)j * a.B + b) * G + g];
+            sa += v.x;
+            sq += v.y;
         }
-        E = se / (float)P;
-        Q = sq / (float)P;
+        gsh[j0 * G + g] = make_float2(sa, sq);
     }
-    const float var = fmaxf(Q - E * E, 0.f);
-    meanrstd[b * G + g] = make_float2(E, 1.0f / sqrtf(var + eps));
+    __syncthreads();
+    float2* mr = gsh + lanes_per_g * G;
+    for (int g = tid; g < G; g += blockDim.x) {
+        float sa = 0.f, sq = 0.f;
+        for (int j = 0; j < lanes_per_g; ++j) {
+            sa += gsh[j * G + g].x;
+            sq += gsh[j * G + g].y;
+        }
+        const float m = sa * a.inv_count, qm = sq * a.inv_count;
+        if (a.fresh_out && blockIdx.x == 0) {
+            a.fresh_out[(b * G + g) * 2 + 0] = m;
+            a.fresh_out[(b * G + g) * 2 + 1] = qm;
+        }
+        float E = m, Q = qm;
+        if (a.mode != 1) {  // corrected (0) or stale (2): the table in band order
+            float se = 0.f, sqq = 0.f;
+            for (int j = 0; j < a.P; ++j) {
+                if (a.mode == 0 && j == a.i) {
+                    se += m;
+                    sqq += qm;
+                } else {
+                    se += a.stale[((int64_t)j * a.B + b) * G * 2 + g * 2 + 0];
+                    sqq += a.stale[((int64_t)j * a.B + b) * G * 2 + g * 2 + 1];
+                }
+            }
+            E = se / (float)a.P;
+            Q = sqq / (float)a.P;
+        }
+        const float var = fmaxf(Q - E * E, 0.f);
+        mr[g] = make_float2(E, 1.0f / sqrtf(var + a.eps));
+    }
+    if (!a.y) return;
+    __syncthreads();
+    const int cv = tid % a.vpt;
+    const int r = tid / a.vpt;
+    if (r >= a.rows) return;
+    const int cg = a.C / G;
+    float sc[VEC], sf[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        const int c = cv * VEC + e;
+        const float2 m = mr[c / cg];
+        const float ga = a.gamma ? a.gamma[c] : 1.f;
+        const float be = a.beta ? a.beta[c] : 0.f;
+        sc[e] = m.y * ga;
+        sf[e] = be - m.x * sc[e];
+    }
+    const int64_t t0 = (int64_t)blockIdx.x * a.tok_per_blk;
+    int64_t t1 = t0 + a.tok_per_blk;
+    if (t1 > a.tokens) t1 = a.tokens;
+    const int64_t base = (int64_t)b * a.tokens * a.vpt + cv;
+    const uint4* xv = (const uint4*)a.x + base;
+    uint4* yv = (uint4*)a.y + base;
+    int64_t t = t0 + r;
+    for (; t < t1; t += 4 * a.rows) {
+        uint4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (t + u * a.rows < t1) v[u] = xv[(t + u * a.rows) * a.vpt];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (t + u * a.rows >= t1) continue;
+            float f[VEC];
+            to_f32<BF16>(v[u], f);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                float z = fmaf(f[e], sc[e], sf[e]);
+                if (SILU) z = silu(z);
+                f[e] = z;
+            }
+            uint4 o;
+            if (BF16) o = pack8(f);
+            else o = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+            yv[(t + u * a.rows) * a.vpt] = o;
+        }
+    }
 }
 
 template <bool BF16, bool SILU>
-__global__ __launch_bounds__(kApplyThreads) void gn_apply_kernel(const void* __restrict__ x, void* __restrict__ y,
-                                                                 int64_t nvec, int vpt, int C, int G,
-                                                                 const float2* __restrict__ meanrstd,
-                                                                 const float* __restrict__ gamma,
-                                                                 const float* __restrict__ beta) {
-    constexpr int VEC = BF16 ? 8 : 4;
-    extern __shared__ float2 ab[];  // [C] (scale, shift)
-    const int b = blockIdx.y;
-    const int cg = C / G;
-    for (int c = threadIdx.x; c < C; c += blockDim.x) {
-        const float2 mr = meanrstd[b * G + c / cg];
-        const float ga = gamma ? gamma[c] : 1.f;
-        const float be = beta ? beta[c] : 0.f;
-        const float sc = mr.y * ga;
-        ab[c] = make_float2(sc, be - mr.x * sc);
+hipError_t launch_gn_typed(const Geom& g, const GnPlan& plan, GnApplyArgs a, float2* partial, hipStream_t stream) {
+    // statistics over the plan's token split
+    {
+        dim3 grid((unsigned)plan.nblk, (unsigned)g.B);
+        const size_t shmem = (size_t)2 * plan.rows * g.C * sizeof(float);
+        gn_stats_kernel<BF16><<<grid, plan.threads, shmem, stream>>>(a.x, a.tokens, g.C, a.G, plan.vpt, plan.rows,
+                                                                    plan.tok_per_blk, partial);
     }
-    __syncthreads();
-    const int64_t batch0 = (int64_t)b * nvec;
-    const int64_t stride = (int64_t)gridDim.x * kApplyThreads * kApplyUnroll;
-    for (int64_t base = (int64_t)blockIdx.x * kApplyThreads * kApplyUnroll + threadIdx.x; base < nvec;
-         base += stride) {
-        uint4 raw[kApplyUnroll];
-#pragma unroll
-        for (int u = 0; u < kApplyUnroll; ++u) {
-            const int64_t v = base + u * kApplyThreads;
-            if (v < nvec) raw[u] = ((const uint4*)x)[batch0 + v];
-        }
-#pragma unroll
-        for (int u = 0; u < kApplyUnroll; ++u) {
-            const int64_t v = base + u * kApplyThreads;
-            if (v >= nvec) continue;
-            const int c0 = (int)(v % vpt) * VEC;
-            float f[VEC];
-            if (BF16) {
-                unpack8(raw[u], f);
-            } else {
-                f[0] = __uint_as_float(raw[u].x);
-                f[1] = __uint_as_float(raw[u].y);
-                f[2] = __uint_as_float(raw[u].z);
-                f[3] = __uint_as_float(raw[u].w);
-            }
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                const float2 k = ab[c0 + e];
-                float t = fmaf(f[e], k.x, k.y);
-                if (SILU) t = silu(t);
-                f[e] = t;
-            }
-            uint4 out;
-            if (BF16) {
-                out = pack8(f);
-            } else {
-                out = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
-                                 __float_as_uint(f[3]));
-            }
-            ((uint4*)y)[batch0 + v] = out;
-        }
+    // apply: the same token split (<= 256 blocks); a moments-only call runs one block per batch
+    int64_t nb = 1;
+    a.tok_per_blk = (int)a.tokens;
+    if (a.y) {
+        nb = plan.nblk;
+        a.tok_per_blk = plan.tok_per_blk;
     }
+    const size_t shmem = ((size_t)(plan.threads / a.G) * a.G + a.G) * sizeof(float2);
+    gn_apply_kernel<BF16, SILU><<<dim3((unsigned)nb, (unsigned)g.B), plan.threads, shmem, stream>>>(a);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -216,72 +256,54 @@ GnPlan plan_groupnorm(const Geom& g, int G, bool bf16) {
     GnPlan p{};
     p.vec = bf16 ? 8 : 4;
     p.vpt = g.C / p.vec;
+    // R token rows per block; block = vpt * R threads (<= 512 when vpt <= 512)
     p.rows = p.vpt >= 512 ? 1 : 512 / p.vpt;
     p.threads = p.vpt * p.rows;
+    if (p.threads < G) {          // the reduction uses at least one thread per group
+        p.rows = (G + p.vpt - 1) / p.vpt;
+        p.threads = p.vpt * p.rows;
+    }
     const int64_t tokens = g.band_tokens();
-    // about 512 blocks over the whole band, at least ~2 token rows per thread row
-    int64_t want = 512 / g.B;
-    if (want < 1) want = 1;
-    int64_t per = (tokens + want - 1) / want;
-    const int64_t min_per = 2 * (int64_t)p.rows;
-    if (per < min_per) per = min_per;
-    p.tok_per_blk = (int)per;
-    p.nblk = (int)((tokens + per - 1) / per);
-    if (p.nblk < 1) p.nblk = 1;
-    p.partial_floats = (size_t)g.B * p.nblk * G * 2;
-    const size_t partial_bytes = (p.partial_floats * sizeof(float) + 255) & ~(size_t)255;
-    p.ws_bytes = partial_bytes + (size_t)g.B * G * 2 * sizeof(float);
+    // Token split shared by both kernels (so the fresh moments never depend on the call's
+    // other arguments): about one block per CU over the whole batch, 256 blocks.
+    int64_t per_batch = 256 / g.B;
+    if (per_batch < 1) per_batch = 1;
+    p.tok_per_blk = (int)((tokens + per_batch - 1) / per_batch);
+    p.nblk = (int)((tokens + p.tok_per_blk - 1) / p.tok_per_blk);
+    p.partial_floats = (size_t)p.nblk * g.B * G * 2;
+    p.ws_bytes = p.partial_floats * sizeof(float);
     return p;
 }
 
 hipError_t launch_groupnorm(const Geom& g, const GnPlan& plan, bool bf16, int G, float eps, int mode, int act,
                             const void* x, const float* stale_stats, const float* gamma, const float* beta,
                             float* fresh_stats_out, void* y, void* ws, hipStream_t stream) {
+    GnApplyArgs a;
+    a.x = x;
+    a.y = y;
+    a.partial = (const float2*)ws;
+    a.nblk = plan.nblk;
+    a.tokens = g.band_tokens();
+    a.B = g.B;
+    a.C = g.C;
+    a.G = G;
+    a.P = g.P;
+    a.i = g.i;
+    a.mode = y ? mode : 1;   // moments only: the table is not read
+    a.vpt = plan.vpt;
+    a.rows = plan.rows;
+    a.tok_per_blk = 0;
+    a.inv_count = 1.0f / (float)((double)a.tokens * (g.C / G));
+    a.eps = eps;
+    a.stale = stale_stats;
+    a.gamma = gamma;
+    a.beta = beta;
+    a.fresh_out = fresh_stats_out;
     float2* partial = (float2*)ws;
-    const size_t partial_bytes = (plan.partial_floats * sizeof(float) + 255) & ~(size_t)255;
-    float2* meanrstd = (float2*)((char*)ws + partial_bytes);
-    const int64_t tokens = g.band_tokens();
-    {
-        dim3 grid((unsigned)plan.nblk, (unsigned)g.B);
-        const size_t shmem = (size_t)2 * plan.rows * g.C * sizeof(float);
-        if (bf16)
-            gn_stats_kernel<true><<<grid, plan.threads, shmem, stream>>>(x, tokens, g.C, G, plan.vpt, plan.rows,
-                                                                        plan.tok_per_blk, partial);
-        else
-            gn_stats_kernel<false><<<grid, plan.threads, shmem, stream>>>(x, tokens, g.C, G, plan.vpt, plan.rows,
-                                                                         plan.tok_per_blk, partial);
-    }
-    {
-        const int waves = g.B * G;
-        const int blocks = (waves * 64 + 255) / 256;
-        const float inv_count = 1.0f / (float)((double)tokens * (g.C / G));
-        gn_finalize_kernel<<<blocks, 256, 0, stream>>>(partial, plan.nblk, g.B, G, g.P, g.i, mode, inv_count, eps,
-                                                       stale_stats, fresh_stats_out, meanrstd, y != nullptr);
-    }
-    if (y) {
-        const int64_t nvec = tokens * plan.vpt;
-        int64_t blocks = (nvec + kApplyThreads * kApplyUnroll - 1) / (kApplyThreads * kApplyUnroll);
-        if (blocks > 2048) blocks = 2048;
-        dim3 grid((unsigned)blocks, (unsigned)g.B);
-        const size_t shmem = (size_t)g.C * sizeof(float2);
-        const bool silu_on = act == 1;
-        if (bf16) {
-            if (silu_on)
-                gn_apply_kernel<true, true><<<grid, kApplyThreads, shmem, stream>>>(x, y, nvec, plan.vpt, g.C, G,
-                                                                                   meanrstd, gamma, beta);
-            else
-                gn_apply_kernel<true, false><<<grid, kApplyThreads, shmem, stream>>>(x, y, nvec, plan.vpt, g.C, G,
-                                                                                    meanrstd, gamma, beta);
-        } else {
-            if (silu_on)
-                gn_apply_kernel<false, true><<<grid, kApplyThreads, shmem, stream>>>(x, y, nvec, plan.vpt, g.C, G,
-                                                                                    meanrstd, gamma, beta);
-            else
-                gn_apply_kernel<false, false><<<grid, kApplyThreads, shmem, stream>>>(x, y, nvec, plan.vpt, g.C,
-                                                                                     G, meanrstd, gamma, beta);
-        }
-    }
-    return hipGetLastError();
+    if (bf16) return act == 1 ? launch_gn_typed<true, true>(g, plan, a, partial, stream)
+                              : launch_gn_typed<true, false>(g, plan, a, partial, stream);
+    return act == 1 ? launch_gn_typed<false, true>(g, plan, a, partial, stream)
+                    : launch_gn_typed<false, false>(g, plan, a, partial, stream);
 }
 
 }  // namespace dp

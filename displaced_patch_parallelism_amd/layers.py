@@ -73,21 +73,36 @@ class DisplacedLayer:
     def step(self, x_patch, i, gn_mode="corrected", update_state=True, events=None) -> List[torch.Tensor]:
         """Patch i's displaced layer step; returns every graph step's patch output.
 
+        With ``update_state`` (and B == 1, CORRECTED GroupNorm) each step that
+        feeds a conv or attention writes its output straight into band i of that
+        consumer's resident stale map, and the fresh moments go straight into
+        slot i of the table: the state is refreshed with no separate splice.
+        A patch never reads its own band of a stale map (the conv reads only the
+        rows next to the band, the attention splices its fresh band in), so the
+        in-place write is safe within the step.  Otherwise the outputs go to
+        scratch buffers and, with ``update_state``, are spliced in afterwards.
+
         ``events``: optional dict; when given, each call is bracketed by a pair of
         torch.cuda.Event recorded on the current stream (the stream the library
         launches on), appended to events[name] as (start, end).
         """
         c = self.cfg
         p = self.patch(i)
+        in_place = update_state and c.B == 1 and gn_mode == "corrected"
         h = x_patch
         outs = []
         conv_i = 0
         for k, s in enumerate(c.graph):
-            out = self.bufs[k]
+            nxt = k + 1
+            if in_place and nxt < len(c.graph) and nxt in self.maps:
+                out = self.maps[nxt][:, i * c.h:(i + 1) * c.h]      # contiguous for B == 1
+            else:
+                out = self.bufs[k]
             ev = _mark(events, s)
             if s in ("gn", "gn_silu"):
+                stats = self.table[i] if in_place else self.fresh_stats
                 dp_groupnorm_async(p, h, c.G, self.table, c.eps, gn_mode, "silu" if s == "gn_silu" else None,
-                                   fresh_stats_out=self.fresh_stats, y_patch=out)
+                                   fresh_stats_out=stats, y_patch=out)
             elif s == "conv":
                 w, b = self.convs[conv_i]
                 conv_i += 1
@@ -99,7 +114,7 @@ class DisplacedLayer:
             _done(ev)
             outs.append(out)
             h = out
-        if update_state:
+        if update_state and not in_place:
             self.splice_state(i, x_patch, outs, events)
         return outs
 

@@ -108,7 +108,10 @@ typedef struct {
  *   stale_stats     [P][B][G][2] float, (m'_j, q'_j) of every band from the
  *                   previous step; may be NULL for DP_GN_LOCAL
  *   gamma, beta     [C] float or NULL (1 and 0)
- *   fresh_stats_out [B][G][2] float, receives (m_i, q_i); may be NULL
+ *   fresh_stats_out [B][G][2] float, receives (m_i, q_i); may be NULL; in
+ *                   DP_GN_CORRECTED mode it may be slot i of stale_stats
+ *                   (that mode never reads slot i), which splices the fresh
+ *                   moments into the table without a separate copy
  *   y_patch         [B][h][W][C] dtype, or NULL to compute statistics only
  *                   (the first pass of a synchronous warm-up step); may equal
  *                   x_patch (in place) but must not otherwise overlap it

@@ -86,3 +86,4 @@ def test_warmup_table_gives_exact_group_norm():
         y, _ = dp.dp_groupnorm_async(dp.Patch(1, c.H, c.W, c.C, c.P, j), gpu(fresh[:, j * c.h:(j + 1) * c.h], "bf16"),
                                      c.G, table)
         assert_parity(host(y), ref[:, j * c.h:(j + 1) * c.h], "bf16", f"warm-up band {j}")
+
