@@ -23,6 +23,8 @@
 #include "dp_device.h"
 #include "dp_internal.h"
 
+#include <cstdlib>
+
 namespace dp {
 namespace {
 
@@ -256,6 +258,196 @@ __global__ __launch_bounds__(256) void conv3x3_bf16_lds_dma_kernel(ConvArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 implicit GEMM for small M: each wave owns a K range.
+//
+// A workgroup computes one 64-pixel x 80-channel tile; its 4 waves split the
+// workgroup's K range into 4 consecutive parts and each wave accumulates the
+// whole 64x80 tile (4x5 blocks of v_mfma_f32_16x16x32_bf16) over its part,
+// streaming its own A (64 rows) and B (80 rows) K tiles through a private
+// 2-stage LDS ring with direct-to-LDS loads -- no barrier in the main loop.
+// At the end the four accumulators are added through LDS in wave order
+// (deterministic) and the tile is written with coalesced 16-byte stores, as
+// bf16 output (+bias) or, when K is also split across workgroups, as fp32
+// partials for the ordered reduce kernel.
+// ---------------------------------------------------------------------------
+constexpr int KS_BM = 64;
+constexpr int KS_BN = 80;
+constexpr int KS_A_CH = KS_BM / 8;                        // 1 KB chunks of A per stage (8)
+constexpr int KS_B_CH = KS_BN / 8;                        // (10)
+constexpr int KS_STAGE = (KS_A_CH + KS_B_CH) * 1024;      // 18 KB
+constexpr int KS_STAGES = 2;
+constexpr int KS_WAVE_LDS = KS_STAGES * KS_STAGE;         // 36 KB per wave
+
+__global__ __launch_bounds__(256) void conv3x3_bf16_wave_ksplit_kernel(ConvArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[4 * KS_WAVE_LDS];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int mt = blockIdx.x / a.ntiles;
+    const int nt = blockIdx.x - mt * a.ntiles;
+    const int m0 = mt * KS_BM;
+    const int n0 = nt * KS_BN;
+    const int split = blockIdx.y;
+    const int kw0 = (int)((int64_t)a.ktiles * split / a.ksplit);
+    const int kw1 = (int)((int64_t)a.ktiles * (split + 1) / a.ksplit);
+    const int kt0 = kw0 + (kw1 - kw0) * wave / 4;
+    const int kt1 = kw0 + (kw1 - kw0) * (wave + 1) / 4;
+    const int nkt = kt1 - kt0;
+    const int cpt = a.Cin / 64;
+    const int wrow = 9 * a.Cin;
+    const uint16_t* zero = (const uint16_t*)g_zero_line;
+    char* ring = smem + wave * KS_WAVE_LDS;
+
+    const int sub = lane >> 3;
+    const int slot = lane & 7;
+    // A rows of this lane: j*8 + sub (j = 0..7); B rows: j*8 + sub (j = 0..9)
+    int pb[KS_A_CH], py[KS_A_CH], px[KS_A_CH], achunk[KS_A_CH];
+#pragma unroll
+    for (int j = 0; j < KS_A_CH; ++j) {
+        const int row = j * 8 + sub;
+        achunk[j] = (slot ^ (row & 7)) * 8;
+        const int m = m0 + row;
+        if (m < a.M) {
+            const int hw = a.h * a.W;
+            pb[j] = m / hw;
+            const int rem = m - pb[j] * hw;
+            py[j] = rem / a.W;
+            px[j] = rem - py[j] * a.W;
+        } else {
+            pb[j] = -1;
+            py[j] = px[j] = 0;
+        }
+    }
+    uint32_t boff[KS_B_CH];
+#pragma unroll
+    for (int j = 0; j < KS_B_CH; ++j) {
+        const int row = j * 8 + sub;
+        int co = n0 + row;
+        if (co >= a.Cout) co = a.Cout - 1;       // clamped rows feed columns that are never stored
+        boff[j] = (uint32_t)(((co - n0) * wrow + (slot ^ (row & 7)) * 8) * 2);
+    }
+    const char* wbase = (const char*)(a.w + (int64_t)n0 * wrow);
+    const uint16_t* asrc[KS_A_CH];
+    int cur_tap = -1;
+
+#define DPK_ISSUE(KT, BUF)                                                                          \
+    do {                                                                                            \
+        const int kt_ = (KT);                                                                       \
+        const int tap_ = kt_ / cpt;                                                                 \
+        const int coff_ = (kt_ - tap_ * cpt) * 64;                                                  \
+        if (tap_ != cur_tap) {                                                                      \
+            cur_tap = tap_;                                                                         \
+            const int ky_ = tap_ / 3, kx_ = tap_ - 3 * (tap_ / 3);                                  \
+            _Pragma("unroll") for (int j = 0; j < KS_A_CH; ++j) {                                   \
+                const int r_ = a.r0 + py[j] + ky_ - 1;                                              \
+                const int x_ = px[j] + kx_ - 1;                                                     \
+                const bool ok_ = pb[j] >= 0 && r_ >= 0 && r_ < a.H && x_ >= 0 && x_ < a.W;          \
+                const bool fr_ = r_ >= a.r0 && r_ < a.r0 + a.h;                                     \
+                const int64_t fo_ = (((int64_t)pb[j] * a.h + (r_ - a.r0)) * a.W + x_) * a.Cin;      \
+                const int64_t so_ = (((int64_t)pb[j] * a.H + r_) * a.W + x_) * a.Cin;               \
+                asrc[j] = ok_ ? (fr_ ? a.xp + fo_ : a.xs + so_) + achunk[j] : nullptr;              \
+            }                                                                                       \
+        }                                                                                           \
+        char* st_ = ring + (BUF) * KS_STAGE;                                                        \
+        _Pragma("unroll") for (int j = 0; j < KS_A_CH; ++j) {                                       \
+            const uint16_t* g_ = asrc[j] ? asrc[j] + coff_ : zero;   /* padding rows: zero line */ \
+            __builtin_amdgcn_global_load_lds((const void*)g_, (lds_void*)(st_ + j * 1024), 16, 0, 0); \
+        }                                                                                           \
+        const char* wk_ = wbase + ((int64_t)tap_ * a.Cin + coff_) * 2;                              \
+        _Pragma("unroll") for (int j = 0; j < KS_B_CH; ++j)                                         \
+            __builtin_amdgcn_global_load_lds((const void*)(wk_ + boff[j]),                         \
+                                             (lds_void*)(st_ + (KS_A_CH + j) * 1024), 16, 0, 0);   \
+    } while (0)
+
+    f32x4 acc[4][5];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int n = 0; n < 5; ++n) acc[i][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int frow = lane & 15;
+    const int p0 = ((0 + (lane >> 4)) ^ (lane & 7)) * 16;
+    const int p1 = ((4 + (lane >> 4)) ^ (lane & 7)) * 16;
+    if (nkt > 0) DPK_ISSUE(kt0, 0);
+    for (int it = 0; it < nkt; ++it) {
+        wait_vmcnt<0>();                         // this wave's stage `it` has landed
+        if (it + 1 < nkt) DPK_ISSUE(kt0 + it + 1, (it + 1) & 1);
+        const char* st = ring + (it & 1) * KS_STAGE;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int po = ks ? p1 : p0;
+            bf16x8 af[4], bfr[5];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8*)(st + (i * 16 + frow) * 128 + po);
+#pragma unroll
+            for (int n = 0; n < 5; ++n) bfr[n] = *(const bf16x8*)(st + KS_A_CH * 1024 + (n * 16 + frow) * 128 + po);
+#pragma unroll
+            for (int n = 0; n < 5; ++n)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[n], acc[i][n], 0, 0, 0);
+        }
+    }
+#undef DPK_ISSUE
+    __syncthreads();   // every wave is done with its ring: reuse the LDS for the reduction
+
+    // acc[i][n][r] = C[pixel i*16 + 4*(l>>4) + r][channel n*16 + (l&15)]
+    float* red = (float*)smem;                   // [4 waves][64][80] fp32 (80 KB)
+    const int ecol = lane & 15;
+    const int erow = 4 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int n = 0; n < 5; ++n)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                red[(wave * KS_BM + i * 16 + erow + r) * KS_BN + n * 16 + ecol] = acc[i][n][r];
+    __syncthreads();
+    // each thread: 4 consecutive channels of 5 (pixel, 4-channel) groups; sum waves in order
+    if (a.ksplit == 1) {
+        uint16_t* tile = (uint16_t*)(smem + 4 * KS_BM * KS_BN * 4);   // [64][80] bf16 after the fp32 area
+        for (int q = tid; q < KS_BM * KS_BN / 4; q += 256) {
+            const int row = q / (KS_BN / 4), c4 = (q - row * (KS_BN / 4)) * 4;
+            float4 v = *(const float4*)(red + row * KS_BN + c4);
+#pragma unroll
+            for (int w = 1; w < 4; ++w) {
+                const float4 u = *(const float4*)(red + (w * KS_BM + row) * KS_BN + c4);
+                v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+            }
+            const int co = n0 + c4;
+            if (a.bias && co < a.Cout) {
+                v.x += a.bias[co]; v.y += a.bias[co + 1]; v.z += a.bias[co + 2]; v.w += a.bias[co + 3];
+            }
+            uint2 o;
+            o.x = pack_bf16x2(v.x, v.y);
+            o.y = pack_bf16x2(v.z, v.w);
+            *(uint2*)(tile + row * KS_BN + c4) = o;
+        }
+        __syncthreads();
+        constexpr int CPR = KS_BN * 2 / 16;       // 10 chunks of 16 bytes per row
+        for (int q = tid; q < KS_BM * CPR; q += 256) {
+            const int row = q / CPR, c16 = q - (q / CPR) * CPR;
+            const int m = m0 + row, co = n0 + c16 * 8;
+            if (m < a.M && co < a.Cout)
+                *(uint4*)(a.y + (int64_t)m * a.Cout + co) = *(const uint4*)(tile + row * KS_BN + c16 * 8);
+        }
+    } else {
+        float* part = a.part + (int64_t)split * a.M * a.Cout;
+        for (int q = tid; q < KS_BM * KS_BN / 4; q += 256) {
+            const int row = q / (KS_BN / 4), c4 = (q - row * (KS_BN / 4)) * 4;
+            float4 v = *(const float4*)(red + row * KS_BN + c4);
+#pragma unroll
+            for (int w = 1; w < 4; ++w) {
+                const float4 u = *(const float4*)(red + (w * KS_BM + row) * KS_BN + c4);
+                v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+            }
+            const int m = m0 + row, co = n0 + c4;
+            if (m < a.M && co < a.Cout) *(float4*)(part + (int64_t)m * a.Cout + co) = v;
+        }
+    }
+}
+
 // y[m][co] = bf16(bias[co] + sum_s part[s][m][co]), summed in split order.
 __global__ __launch_bounds__(256) void conv_splitk_reduce_kernel(const float* __restrict__ part,
                                                                  const float* __restrict__ bias,
@@ -323,22 +515,41 @@ ConvPlan plan_conv(const Geom& g, int Cout, bool bf16) {
         p.kind = 0;
         return p;
     }
-    p.kind = 1;
-    p.bm = BM;
-    p.bn = BN;
     const int64_t M = (int64_t)g.B * g.h * g.W;
-    p.mtiles = (int)((M + BM - 1) / BM);
-    p.ntiles = (Cout + BN - 1) / BN;
     p.ktiles = 9 * g.C / BK;
-    const int tiles = p.mtiles * p.ntiles;
+    const int64_t big_tiles = ((M + BM - 1) / BM) * ((Cout + BN - 1) / BN);
     int ks = 1;
-    if (tiles < 256) {
-        // split K until about 256 workgroups, keeping >= 4 K tiles per split
-        ks = (256 + tiles - 1) / tiles;
-        const int maxk = p.ktiles / 4 > 0 ? p.ktiles / 4 : 1;
-        if (ks > maxk) ks = maxk;
-        if (ks > 32) ks = 32;
+    if (big_tiles >= 128) {
+        // enough 128x160 tiles: waves share A and B through LDS; split K if < 256 tiles
+        p.kind = 1;
+        p.bm = BM;
+        p.bn = BN;
+        p.mtiles = (int)((M + BM - 1) / BM);
+        p.ntiles = (Cout + BN - 1) / BN;
+        const int tiles = p.mtiles * p.ntiles;
+        if (tiles < 256) {
+            ks = (256 + tiles - 1) / tiles;
+            const int maxk = p.ktiles / 4 > 0 ? p.ktiles / 4 : 1;
+            if (ks > maxk) ks = maxk;
+        }
+    } else {
+        // small M: 64x80 tiles, K split over the 4 waves of a workgroup (and across
+        // workgroups until about 256 workgroups, keeping >= 2 K tiles per wave)
+        p.kind = 2;
+        p.bm = KS_BM;
+        p.bn = KS_BN;
+        p.mtiles = (int)((M + KS_BM - 1) / KS_BM);
+        p.ntiles = (Cout + KS_BN - 1) / KS_BN;
+        const int tiles = p.mtiles * p.ntiles;
+        if (tiles < 256) {
+            ks = (256 + tiles / 2) / tiles;
+            const int maxk = p.ktiles / 8 > 0 ? p.ktiles / 8 : 1;
+            if (ks > maxk) ks = maxk;
+            if (ks < 1) ks = 1;
+        }
     }
+    if (ks > 32) ks = 32;
+    if (const char* e = getenv("DP_CONV_KSPLIT")) ks = atoi(e) > 0 ? (atoi(e) < p.ktiles ? atoi(e) : p.ktiles) : ks;
     p.ksplit = ks;
     p.ws_bytes = ks > 1 ? (size_t)ks * M * Cout * sizeof(float) : 0;
     return p;
@@ -374,7 +585,10 @@ hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout,
     a.ksplit = plan.ksplit;
     a.ntiles = plan.ntiles;
     dim3 grid((unsigned)(plan.mtiles * plan.ntiles), (unsigned)plan.ksplit);
-    conv3x3_bf16_lds_dma_kernel<BN, kStages><<<grid, kThreads, 0, stream>>>(a);
+    if (plan.kind == 2)
+        conv3x3_bf16_wave_ksplit_kernel<<<grid, kThreads, 0, stream>>>(a);
+    else
+        conv3x3_bf16_lds_dma_kernel<BN, kStages><<<grid, kThreads, 0, stream>>>(a);
     if (plan.ksplit > 1) {
         const int64_t total4 = (int64_t)a.M * Cout / 4;
         conv_splitk_reduce_kernel<<<(unsigned)((total4 + 255) / 256), 256, 0, stream>>>(
