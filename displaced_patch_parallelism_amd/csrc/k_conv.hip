@@ -23,7 +23,6 @@
 #include "dp_device.h"
 #include "dp_internal.h"
 
-#include <cstdlib>
 
 namespace dp {
 namespace {
@@ -32,6 +31,7 @@ constexpr int BM = 128;
 constexpr int BN = 160;
 constexpr int BK = 64;
 constexpr int kStages = 2;   // LDS ring depth: 2 x 36 KB, so two workgroups share a CU
+constexpr int kWaveKB = 64;  // K tile of the wave-split kernel: 2 stages of 18 KB per wave
 constexpr int kThreads = 256;
 
 struct ConvArgs {
@@ -273,13 +273,24 @@ __global__ __launch_bounds__(256) void conv3x3_bf16_lds_dma_kernel(ConvArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int KS_BM = 64;
 constexpr int KS_BN = 80;
-constexpr int KS_A_CH = KS_BM / 8;                        // 1 KB chunks of A per stage (8)
-constexpr int KS_B_CH = KS_BN / 8;                        // (10)
-constexpr int KS_STAGE = (KS_A_CH + KS_B_CH) * 1024;      // 18 KB
-constexpr int KS_STAGES = 2;
-constexpr int KS_WAVE_LDS = KS_STAGES * KS_STAGE;         // 36 KB per wave
+constexpr int KS_WAVE_LDS = 36 * 1024;                    // per wave; 4 waves = 144 KB
 
+// KB = K tile width (64: 2 stages of 18 KB; 32: 4 stages of 9 KB per wave).
+// Rows of a stage are KB*2 bytes; 16-byte chunk c of row r sits at slot
+// c ^ swz(r) (swz = r & 7 for 128-byte rows, (r >> 2) & 3 for 64-byte rows)
+// so the 16 rows x 16 bytes of an operand read spread over the LDS banks.
+template <int KB>
 __global__ __launch_bounds__(256) void conv3x3_bf16_wave_ksplit_kernel(ConvArgs a) {
+    constexpr int RB = KB * 2;                          // bytes per row
+    constexpr int SLOTS = RB / 16;                      // 16-byte chunks per row
+    constexpr int RPC = 1024 / RB;                      // rows per 1 KB DMA chunk
+    constexpr int A_CH = KS_BM * RB / 1024;             // DMA chunks per stage for A
+    constexpr int B_CH = KS_BN * RB / 1024;             // ... for B
+    constexpr int LOADS = A_CH + B_CH;
+    constexpr int STAGE = LOADS * 1024;
+    constexpr int STAGES = KS_WAVE_LDS / STAGE;         // 2 (KB=64) or 4 (KB=32)
+    constexpr int KSTEPS = KB / 32;
+    static_assert(STAGES >= 2, "ring depth");
     __shared__ __attribute__((aligned(1024))) char smem[4 * KS_WAVE_LDS];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -294,19 +305,19 @@ __global__ __launch_bounds__(256) void conv3x3_bf16_wave_ksplit_kernel(ConvArgs 
     const int kt0 = kw0 + (kw1 - kw0) * wave / 4;
     const int kt1 = kw0 + (kw1 - kw0) * (wave + 1) / 4;
     const int nkt = kt1 - kt0;
-    const int cpt = a.Cin / 64;
+    const int cpt = a.Cin / KB;
     const int wrow = 9 * a.Cin;
     const uint16_t* zero = (const uint16_t*)g_zero_line;
     char* ring = smem + wave * KS_WAVE_LDS;
 
-    const int sub = lane >> 3;
-    const int slot = lane & 7;
-    // A rows of this lane: j*8 + sub (j = 0..7); B rows: j*8 + sub (j = 0..9)
-    int pb[KS_A_CH], py[KS_A_CH], px[KS_A_CH], achunk[KS_A_CH];
+    auto swz = [](int row) { return SLOTS == 8 ? (row & 7) : ((row >> 2) & 3); };
+    const int sub = lane / SLOTS;
+    const int slot = lane % SLOTS;
+    int pb[A_CH], py[A_CH], px[A_CH], achunk[A_CH];
 #pragma unroll
-    for (int j = 0; j < KS_A_CH; ++j) {
-        const int row = j * 8 + sub;
-        achunk[j] = (slot ^ (row & 7)) * 8;
+    for (int j = 0; j < A_CH; ++j) {
+        const int row = j * RPC + sub;
+        achunk[j] = (slot ^ swz(row)) * 8;
         const int m = m0 + row;
         if (m < a.M) {
             const int hw = a.h * a.W;
@@ -319,27 +330,27 @@ __global__ __launch_bounds__(256) void conv3x3_bf16_wave_ksplit_kernel(ConvArgs 
             py[j] = px[j] = 0;
         }
     }
-    uint32_t boff[KS_B_CH];
+    uint32_t boff[B_CH];
 #pragma unroll
-    for (int j = 0; j < KS_B_CH; ++j) {
-        const int row = j * 8 + sub;
+    for (int j = 0; j < B_CH; ++j) {
+        const int row = j * RPC + sub;
         int co = n0 + row;
         if (co >= a.Cout) co = a.Cout - 1;       // clamped rows feed columns that are never stored
-        boff[j] = (uint32_t)(((co - n0) * wrow + (slot ^ (row & 7)) * 8) * 2);
+        boff[j] = (uint32_t)(((co - n0) * wrow + (slot ^ swz(row)) * 8) * 2);
     }
     const char* wbase = (const char*)(a.w + (int64_t)n0 * wrow);
-    const uint16_t* asrc[KS_A_CH];
+    const uint16_t* asrc[A_CH];
     int cur_tap = -1;
 
 #define DPK_ISSUE(KT, BUF)                                                                          \
     do {                                                                                            \
         const int kt_ = (KT);                                                                       \
         const int tap_ = kt_ / cpt;                                                                 \
-        const int coff_ = (kt_ - tap_ * cpt) * 64;                                                  \
+        const int coff_ = (kt_ - tap_ * cpt) * KB;                                                  \
         if (tap_ != cur_tap) {                                                                      \
             cur_tap = tap_;                                                                         \
             const int ky_ = tap_ / 3, kx_ = tap_ - 3 * (tap_ / 3);                                  \
-            _Pragma("unroll") for (int j = 0; j < KS_A_CH; ++j) {                                   \
+            _Pragma("unroll") for (int j = 0; j < A_CH; ++j) {                                      \
                 const int r_ = a.r0 + py[j] + ky_ - 1;                                              \
                 const int x_ = px[j] + kx_ - 1;                                                     \
                 const bool ok_ = pb[j] >= 0 && r_ >= 0 && r_ < a.H && x_ >= 0 && x_ < a.W;          \
@@ -349,15 +360,15 @@ __global__ __launch_bounds__(256) void conv3x3_bf16_wave_ksplit_kernel(ConvArgs 
                 asrc[j] = ok_ ? (fr_ ? a.xp + fo_ : a.xs + so_) + achunk[j] : nullptr;              \
             }                                                                                       \
         }                                                                                           \
-        char* st_ = ring + (BUF) * KS_STAGE;                                                        \
-        _Pragma("unroll") for (int j = 0; j < KS_A_CH; ++j) {                                       \
+        char* st_ = ring + (BUF) * STAGE;                                                           \
+        _Pragma("unroll") for (int j = 0; j < A_CH; ++j) {                                          \
             const uint16_t* g_ = asrc[j] ? asrc[j] + coff_ : zero;   /* padding rows: zero line */ \
             __builtin_amdgcn_global_load_lds((const void*)g_, (lds_void*)(st_ + j * 1024), 16, 0, 0); \
         }                                                                                           \
         const char* wk_ = wbase + ((int64_t)tap_ * a.Cin + coff_) * 2;                              \
-        _Pragma("unroll") for (int j = 0; j < KS_B_CH; ++j)                                         \
+        _Pragma("unroll") for (int j = 0; j < B_CH; ++j)                                            \
             __builtin_amdgcn_global_load_lds((const void*)(wk_ + boff[j]),                         \
-                                             (lds_void*)(st_ + (KS_A_CH + j) * 1024), 16, 0, 0);   \
+                                             (lds_void*)(st_ + (A_CH + j) * 1024), 16, 0, 0);      \
     } while (0)
 
     f32x4 acc[4][5];
@@ -367,21 +378,26 @@ __global__ __launch_bounds__(256) void conv3x3_bf16_wave_ksplit_kernel(ConvArgs 
         for (int n = 0; n < 5; ++n) acc[i][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int frow = lane & 15;
-    const int p0 = ((0 + (lane >> 4)) ^ (lane & 7)) * 16;
-    const int p1 = ((4 + (lane >> 4)) ^ (lane & 7)) * 16;
-    if (nkt > 0) DPK_ISSUE(kt0, 0);
-    for (int it = 0; it < nkt; ++it) {
-        wait_vmcnt<0>();                         // this wave's stage `it` has landed
-        if (it + 1 < nkt) DPK_ISSUE(kt0 + it + 1, (it + 1) & 1);
-        const char* st = ring + (it & 1) * KS_STAGE;
+    int po[KSTEPS];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int po = ks ? p1 : p0;
+    for (int ks = 0; ks < KSTEPS; ++ks) po[ks] = ((ks * 4 + (lane >> 4)) ^ swz(frow)) * 16;
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nkt) DPK_ISSUE(kt0 + s, s);
+    for (int it = 0; it < nkt; ++it) {
+        // this wave's stage `it` has landed; later stages may still be in flight
+        const int ahead = nkt - 1 - it;
+        if (STAGES >= 4 && ahead >= 2) wait_vmcnt<(STAGES >= 4 ? 2 : 0) * LOADS>();
+        else if (STAGES >= 3 && ahead >= 1) wait_vmcnt<(STAGES >= 3 ? 1 : 0) * LOADS>();
+        else wait_vmcnt<0>();
+        if (it + STAGES - 1 < nkt) DPK_ISSUE(kt0 + it + STAGES - 1, (it + STAGES - 1) % STAGES);
+        const char* st = ring + (it % STAGES) * STAGE;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
             bf16x8 af[4], bfr[5];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8*)(st + (i * 16 + frow) * 128 + po);
+            for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8*)(st + (i * 16 + frow) * RB + po[ks]);
 #pragma unroll
-            for (int n = 0; n < 5; ++n) bfr[n] = *(const bf16x8*)(st + KS_A_CH * 1024 + (n * 16 + frow) * 128 + po);
+            for (int n = 0; n < 5; ++n) bfr[n] = *(const bf16x8*)(st + A_CH * 1024 + (n * 16 + frow) * RB + po[ks]);
 #pragma unroll
             for (int n = 0; n < 5; ++n)
 #pragma unroll
@@ -538,6 +554,7 @@ ConvPlan plan_conv(const Geom& g, int Cout, bool bf16) {
         p.kind = 2;
         p.bm = KS_BM;
         p.bn = KS_BN;
+        p.ktiles = 9 * g.C / kWaveKB;
         p.mtiles = (int)((M + KS_BM - 1) / KS_BM);
         p.ntiles = (Cout + KS_BN - 1) / KS_BN;
         const int tiles = p.mtiles * p.ntiles;
@@ -549,7 +566,6 @@ ConvPlan plan_conv(const Geom& g, int Cout, bool bf16) {
         }
     }
     if (ks > 32) ks = 32;
-    if (const char* e = getenv("DP_CONV_KSPLIT")) ks = atoi(e) > 0 ? (atoi(e) < p.ktiles ? atoi(e) : p.ktiles) : ks;
     p.ksplit = ks;
     p.ws_bytes = ks > 1 ? (size_t)ks * M * Cout * sizeof(float) : 0;
     return p;
@@ -585,8 +601,9 @@ hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout,
     a.ksplit = plan.ksplit;
     a.ntiles = plan.ntiles;
     dim3 grid((unsigned)(plan.mtiles * plan.ntiles), (unsigned)plan.ksplit);
-    if (plan.kind == 2)
-        conv3x3_bf16_wave_ksplit_kernel<<<grid, kThreads, 0, stream>>>(a);
+    if (plan.kind == 2) {
+        conv3x3_bf16_wave_ksplit_kernel<kWaveKB><<<grid, kThreads, 0, stream>>>(a);
+    }
     else
         conv3x3_bf16_lds_dma_kernel<BN, kStages><<<grid, kThreads, 0, stream>>>(a);
     if (plan.ksplit > 1) {
