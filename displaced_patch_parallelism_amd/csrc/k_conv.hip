@@ -8,16 +8,32 @@
 //   y[b,y,x,o] = bias[o] + sum_{ky,kx,c} w[o,ky,kx,c] * src(b, r0+y+ky-1, x+kx-1, c)
 // src = fresh patch inside the band, stale map at other image rows, 0 outside.
 //
-// bf16 path: implicit GEMM on MFMA (v_mfma_f32_16x16x32_bf16).
-//   M = B*h*W output pixels, N = Cout, K = 9*Cin with k = tap*Cin + c, so a
-//   K tile of 64 channels lies inside one tap.  Weights [Cout][3][3][Cin] are
-//   the GEMM's B^T, row-contiguous in K.  The A loader resolves each pixel's
-//   source row once per tap (fresh band / stale map / zero) and streams its
-//   128-byte channel runs straight into LDS with direct-to-LDS loads.  Tile
-//   128 pixels x 160 channels, 4 waves of 64x80; a 2-stage LDS ring of 36 KB
-//   per stage lets two workgroups share a CU so one's waits overlap the
-//   other's MFMAs.  Small M is split along K; the fp32 partials are summed in
-//   split order by a second kernel (deterministic).
+// bf16 path: implicit GEMM on MFMA (v_mfma_f32_16x16x32_bf16), M = output
+// pixels, N = Cout, K = 9*Cin, over rectangular pixel tiles (TR rows x 32
+// columns of the band) so the three horizontal taps of a kernel row read the
+// same source pixels:
+//   * The K loop runs over stages (cc, ky): 32 input channels of kernel row
+//     ky.  A stage holds the tile's source pixels for that row -- TR rows x 34
+//     columns (one extra column each side), 64 bytes each, resolved per pixel
+//     to the fresh band, the stale map or zero padding -- and the three taps
+//     (ky, 0..2) of the tile's output channels, 64 bytes per (tap, channel).
+//     Each source pixel is fetched once per stage instead of once per tap.
+//   * Stages are streamed global -> LDS with direct-to-LDS loads
+//     (global_load_lds_dwordx4: lane l of a load fills the l-th 16-byte slot of
+//     a 1 KB run), double-buffered.  Slot layout: chunk c (8 channels) of pixel
+//     or tap row p sits at slot 4p + (c ^ ((p >> 1) & 3)), so the 16
+//     consecutive rows of an MFMA operand read hit distinct banks at any
+//     column offset.
+//   * Workgroups are dispatched round-robin over the 8 XCDs; tiles are renumbered
+//     so each XCD walks a contiguous run of pixel tiles, keeping the inputs those
+//     tiles share in one L2.
+//   Large maps: 128x160 tiles (4 rows x 32 columns), one LDS ring shared by
+//   4 waves (2x2 of 64 pixels x 80 channels), two workgroups per CU.  Small
+//   maps: 64x80 tiles (2 rows x 32 columns) whose 4 waves each take a quarter
+//   of K through a private ring and are summed through LDS in wave order; K is
+//   also split across workgroups until about 256 of them run, the fp32
+//   partials summed in split order by a second kernel.  Every sum has a fixed
+//   order, so results are deterministic.
 // f32 path: one thread per output element (correctness path for small maps).
 
 #include "dp_device.h"
@@ -27,12 +43,8 @@
 namespace dp {
 namespace {
 
-constexpr int BM = 128;
-constexpr int BN = 160;
-constexpr int BK = 64;
-constexpr int kStages = 2;   // LDS ring depth: 2 x 36 KB, so two workgroups share a CU
-constexpr int kWaveKB = 64;  // K tile of the wave-split kernel: 2 stages of 18 KB per wave
 constexpr int kThreads = 256;
+constexpr int kTileTC = 32;    // tile columns (both bf16 kernels)
 
 struct ConvArgs {
     const uint16_t* xp;
@@ -43,28 +55,15 @@ struct ConvArgs {
     float* part;
     int B, H, W, Cin, Cout, h, r0;
     int M;
-    int ktiles, ksplit;
-    int ntiles;
+    int ntx, nty;        // pixel tiles across the band's columns / rows (per batch)
+    int mtiles, ntiles;  // pixel tiles (B * nty * ntx), channel tiles
+    int kstages;         // K stages (cc, ky): 32 input channels of one kernel row; 3 * Cin / 32
+    int ksplit;          // K partitions across workgroups
 };
-
-// ---------------------------------------------------------------------------
-// bf16 implicit GEMM, pipelined through LDS with direct-to-LDS loads.
-//
-// Tile BM=128 pixels x BN output channels, 4 waves in a 2x2 grid, each wave
-// 64 pixels x BN/2 channels as 16x16 blocks of v_mfma_f32_16x16x32_bf16.
-// Every K tile (64 input channels of one tap) of A (128 rows) and B (BN rows)
-// is 128 bytes per row, fetched by global_load_lds_dwordx4 straight into an
-// LDS stage (lane l of a load writes the l-th 16-byte slot of a 1 KB chunk).
-// The 16-byte chunk c of row r sits at slot c ^ (r & 7) so the MFMA operand
-// reads (16 rows x one chunk) spread over the banks.  STAGES stages form a
-// ring: while stage k is multiplied, stages k+1.. are in flight.  A rows
-// whose source is outside the image (or past the last pixel) read a static
-// zero line instead.
-// ---------------------------------------------------------------------------
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __attribute__((aligned(64))) uint4 g_zero_line[8];   // never written: reads as zero
+__device__ __attribute__((aligned(64))) uint4 g_zero_line[4];   // never written: reads as zero
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -72,303 +71,183 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int BN, int STAGES>
-__global__ __launch_bounds__(256) void conv3x3_bf16_lds_dma_kernel(ConvArgs a) {
-    constexpr int BM2 = 128;
-    constexpr int A_CH = BM2 * 128 / 1024;      // 1 KB chunks per A stage (16)
-    constexpr int B_CH = BN * 128 / 1024;       // per B stage (BN/8)
-    static_assert(A_CH % 4 == 0 && B_CH % 4 == 0, "chunks split over 4 waves");
-    constexpr int A_PW = A_CH / 4;
-    constexpr int B_PW = B_CH / 4;
-    constexpr int LOADS = A_PW + B_PW;          // DMA loads per wave per stage
-    constexpr int STAGE = (A_CH + B_CH) * 1024;
-    constexpr int WN = BN / 2;                  // channels per wave
-    constexpr int NBK = WN / 16;                // 16-wide blocks per wave
-    constexpr int SMEM = STAGES * STAGE > BM2 * BN * 4 ? STAGES * STAGE : BM2 * BN * 4;
+__device__ __forceinline__ int slot_swz(int p) { return (p >> 1) & 3; }
+
+// Geometry of one stage for a TR x 32 pixel tile and BN output channels.
+template <int TR, int BN>
+struct Stage {
+    static constexpr int HWC = kTileTC + 2;                 // halo columns
+    static constexpr int A_SLOTS = TR * HWC * 4;            // 16-byte slots of source pixels
+    static constexpr int A_LOADS = (A_SLOTS + 63) / 64;     // 1 KB direct-to-LDS loads
+    static constexpr int A_TAIL = A_SLOTS - (A_LOADS - 1) * 64;   // active lanes of the last one
+    static constexpr int B_SLOTS = 3 * BN * 4;              // three taps x BN channel rows
+    static constexpr int B_LOADS = B_SLOTS / 64;
+    static constexpr int B_OFF = A_SLOTS * 16;
+    static constexpr int BYTES = (A_SLOTS + B_SLOTS) * 16;
+    static_assert(B_SLOTS % 64 == 0 && BN % 80 == 0, "channel tile");
+};
+
+// Workgroup b runs on XCD b % 8: give XCD x the contiguous run x*q + min(x, r) .. of the
+// logical tile order (q = total / 8, r = total % 8).  A bijection of [0, total).
+__device__ __forceinline__ int xcd_order(int b, int total) {
+    const int x = b & 7, i = b >> 3;
+    const int q = total >> 3, r = total & 7;
+    return x * q + (x < r ? x : r) + i;
+}
+
+// Source of A slot s of a stage of tile (bb, ty0, tx0), for kernel rows ky = 0, 1, 2:
+// pointer to channel chunk c of the pixel, or null where the pixel is zero padding.
+template <int TR>
+__device__ __forceinline__ void resolve_a_slot(const ConvArgs& a, int bb, int ty0, int tx0, int s,
+                                               const uint16_t*& p0, const uint16_t*& p1,
+                                               const uint16_t*& p2) {
+    constexpr int HWC = kTileTC + 2;
+    const int p = s >> 2;
+    const int t = p / HWC, u = p - t * HWC;
+    const int c = (s & 3) ^ slot_swz(p);
+    const int x = tx0 + u - 1;
+    const uint16_t* q[3];
+#pragma unroll
+    for (int ky = 0; ky < 3; ++ky) {
+        const int r = a.r0 + ty0 + t + ky - 1;    // image row feeding tile row t through kernel row ky
+        const bool ok = s < TR * HWC * 4 && x >= 0 && x < a.W && r >= 0 && r < a.H;
+        const bool fresh = r >= a.r0 && r < a.r0 + a.h;
+        const int64_t fo = (((int64_t)bb * a.h + (r - a.r0)) * a.W + x) * a.Cin;
+        const int64_t so = (((int64_t)bb * a.H + r) * a.W + x) * a.Cin;
+        q[ky] = ok ? (fresh ? a.xp + fo : a.xs + so) + c * 8 : nullptr;
+    }
+    p0 = q[0];
+    p1 = q[1];
+    p2 = q[2];
+}
+
+// Byte offset of B slot s (tap row kx*BN + n, chunk) from the weights of kernel row 0, channel 0.
+template <int BN>
+__device__ __forceinline__ uint32_t b_slot_offset(const ConvArgs& a, int n0, int s) {
+    const int nr = s >> 2;
+    const int kx = nr / BN, n = nr - kx * BN;
+    const int c = (s & 3) ^ slot_swz(nr);
+    int co = n0 + n;
+    if (co >= a.Cout) co = a.Cout - 1;      // clamped rows feed columns that are never stored
+    return (uint32_t)((((int64_t)co * 9 + kx) * a.Cin + c * 8) * 2);
+}
+
+// The 60 MFMAs of one stage for a wave's 64 pixels (tile rows tr0, tr0+1, 32 columns) x 80
+// channels.  aoff[r][kx]: byte offset of this lane's operand row for tile row tr0+r, columns
+// 0..15, tap kx; columns 16..31 are 1 KB further.  boff: this lane's operand row of tap 0,
+// channel block 0 of the wave; tap kx, block n are (kx*BN + 16n) * 64 bytes further.
+template <int BN>
+__device__ __forceinline__ void stage_mfma(const char* st, const int (&aoff)[2][3], int boff,
+                                           f32x4 (&acc)[4][5]) {
+#pragma unroll
+    for (int kx = 0; kx < 3; ++kx) {
+        bf16x8 af[4], bfr[5];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8*)(st + aoff[i >> 1][kx] + (i & 1) * 1024);
+#pragma unroll
+        for (int n = 0; n < 5; ++n) bfr[n] = *(const bf16x8*)(st + boff + (kx * BN + n * 16) * 64);
+#pragma unroll
+        for (int n = 0; n < 5; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[n], acc[i][n], 0, 0, 0);
+    }
+}
+
+// Operand read offsets of this lane for a wave whose pixels are tile rows tr0, tr0+1.
+template <int TR, int BN>
+__device__ __forceinline__ void operand_offsets(int lane, int tr0, int wn, int (&aoff)[2][3], int& boff) {
+    constexpr int HWC = kTileTC + 2;
+    const int row = lane & 15, ch = lane >> 4;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int kx = 0; kx < 3; ++kx) {
+            const int p = (tr0 + r) * HWC + kx + row;
+            aoff[r][kx] = (4 * p + (ch ^ slot_swz(p))) * 16;
+        }
+    boff = Stage<TR, BN>::B_OFF + (4 * (wn * 80 + row) + (ch ^ slot_swz(row))) * 16;
+}
+
+// Decode a tile index: batch, first band row, first column.
+template <int TR>
+__device__ __forceinline__ void tile_origin(const ConvArgs& a, int mt, int& bb, int& ty0, int& tx0) {
+    const int txt = mt % a.ntx;
+    const int rest = mt / a.ntx;
+    const int tyt = rest % a.nty;
+    bb = rest / a.nty;
+    ty0 = tyt * TR;
+    tx0 = txt * kTileTC;
+}
+
+// ---------------------------------------------------------------------------
+// Large maps: tile 4 rows x 32 columns x 160 channels, 4 waves (2 pixel-row pairs x 2 channel
+// halves), one 2-stage ring shared by the workgroup (2 x 38.5 KB, so two workgroups share a CU
+// and one's waits overlap the other's MFMAs).  The 39 loads of a stage are dealt round-robin
+// to the waves; a barrier per stage publishes it.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 2) void conv3x3_bf16_halo_tile_kernel(ConvArgs a) {
+    constexpr int TR = 4, BN = 160;
+    using S = Stage<TR, BN>;
+    constexpr int AQ = (S::A_LOADS + 3) / 4;     // A loads per wave (at most)
+    constexpr int BQ = (S::B_LOADS + 3) / 4;
+    constexpr int SMEM = 2 * S::BYTES > 128 * BN * 2 ? 2 * S::BYTES : 128 * BN * 2;
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave & 1, wn = wave >> 1;
-    const int mt = blockIdx.x / a.ntiles;
-    const int nt = blockIdx.x - mt * a.ntiles;
-    const int m0 = mt * BM2;
+    const int lt = xcd_order(blockIdx.x, gridDim.x);
+    const int mt = lt % a.mtiles;
+    const int nt = lt / a.mtiles;
+    int bb, ty0, tx0;
+    tile_origin<TR>(a, mt, bb, ty0, tx0);
     const int n0 = nt * BN;
-    const int split = blockIdx.y;
-    const int kt0 = (int)((int64_t)a.ktiles * split / a.ksplit);
-    const int kt1 = (int)((int64_t)a.ktiles * (split + 1) / a.ksplit);
-    const int nkt = kt1 - kt0;
-    const int cpt = a.Cin / 64;
-    const int64_t wrow = 9 * (int64_t)a.Cin;
     const uint16_t* zero = (const uint16_t*)g_zero_line;
 
-    // ---- loader state: this lane's A rows (pixels) and B rows (channels) ----
-    const int sub = lane >> 3;          // row within a 1 KB chunk (8 rows of 128 B)
-    const int slot = lane & 7;          // physical 16-byte slot in the row
-    int pb[A_PW], py[A_PW], px[A_PW], achunk[A_PW];
+    const uint16_t* ap0[AQ];
+    const uint16_t* ap1[AQ];
+    const uint16_t* ap2[AQ];
 #pragma unroll
-    for (int j = 0; j < A_PW; ++j) {
-        const int row = (wave * A_PW + j) * 8 + sub;
-        achunk[j] = slot ^ (row & 7);
-        const int m = m0 + row;
-        if (m < a.M) {
-            const int hw = a.h * a.W;
-            pb[j] = m / hw;
-            const int rem = m - pb[j] * hw;
-            py[j] = rem / a.W;
-            px[j] = rem - py[j] * a.W;
-        } else {
-            pb[j] = -1;
-            py[j] = px[j] = 0;
-        }
+    for (int q = 0; q < AQ; ++q) {
+        const int j = wave + 4 * q;
+        resolve_a_slot<TR>(a, bb, ty0, tx0, j * 64 + lane, ap0[q], ap1[q], ap2[q]);
     }
-    const uint16_t* bsrc[B_PW];
+    uint32_t bo[BQ];
 #pragma unroll
-    for (int j = 0; j < B_PW; ++j) {
-        const int row = (wave * B_PW + j) * 8 + sub;
-        const int co = n0 + row;
-        const int ch = slot ^ (row & 7);
-        bsrc[j] = co < a.Cout ? a.w + co * wrow + ch * 8 : nullptr;
-    }
-    const uint16_t* asrc[A_PW];
-    int cur_tap = -1;
+    for (int q = 0; q < BQ; ++q) bo[q] = b_slot_offset<BN>(a, n0, (wave + 4 * q) * 64 + lane);
 
-    f32x4 acc[4][NBK];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int n = 0; n < NBK; ++n) acc[i][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-#define DP_ISSUE_STAGE(KT, BUF)                                                                     \
+    // Issue the loads of stage (cc, KY) into ring buffer BUF; KY is a literal so each kernel row
+    // reads its own source array (a runtime select between them becomes a scratch-indexed load).
+#define DPH_ISSUE_KY(CC, KY, SRC, BUF)                                                              \
     do {                                                                                            \
-        const int kt_ = (KT);                                                                       \
-        const int tap_ = kt_ / cpt;                                                                 \
-        const int cc_ = kt_ - tap_ * cpt;                                                           \
-        const int coff_ = cc_ * 64;                                                                 \
-        const int64_t kofs_ = (int64_t)tap_ * a.Cin + coff_;                                        \
-        if (tap_ != cur_tap) {                                                                      \
-            cur_tap = tap_;                                                                         \
-            const int ky_ = tap_ / 3, kx_ = tap_ - 3 * (tap_ / 3);                                  \
-            _Pragma("unroll") for (int j = 0; j < A_PW; ++j) {                                      \
-                const int r_ = a.r0 + py[j] + ky_ - 1;                                              \
-                const int x_ = px[j] + kx_ - 1;                                                     \
-                const bool ok_ = pb[j] >= 0 && r_ >= 0 && r_ < a.H && x_ >= 0 && x_ < a.W;          \
-                const bool fr_ = r_ >= a.r0 && r_ < a.r0 + a.h;                                     \
-                const int64_t fo_ = (((int64_t)pb[j] * a.h + (r_ - a.r0)) * a.W + x_) * a.Cin;      \
-                const int64_t so_ = (((int64_t)pb[j] * a.H + r_) * a.W + x_) * a.Cin;               \
-                asrc[j] = ok_ ? (fr_ ? a.xp + fo_ : a.xs + so_) + achunk[j] * 8 : nullptr;          \
+        char* st_ = smem + (BUF) * S::BYTES;                                                        \
+        _Pragma("unroll") for (int q = 0; q < AQ; ++q) {                                            \
+            const int j_ = wave + 4 * q;                                                            \
+            if (j_ < S::A_LOADS) {                                                                  \
+                const uint16_t* g_ = SRC[q] ? SRC[q] + (CC) * 32 : zero;                            \
+                if (j_ < S::A_LOADS - 1 || lane < S::A_TAIL)                                        \
+                    __builtin_amdgcn_global_load_lds((const void*)g_, (lds_void*)(st_ + j_ * 1024), \
+                                                     16, 0, 0);                                    \
             }                                                                                       \
         }                                                                                           \
-        char* st_ = smem + (BUF) * STAGE;                                                           \
-        _Pragma("unroll") for (int j = 0; j < A_PW; ++j) {                                          \
-            const uint16_t* g_ = asrc[j] ? asrc[j] + coff_ : zero;                                  \
-            __builtin_amdgcn_global_load_lds((const void*)g_, (lds_void*)(st_ + (wave * A_PW + j) * 1024), \
-                                             16, 0, 0);                                            \
-        }                                                                                           \
-        _Pragma("unroll") for (int j = 0; j < B_PW; ++j) {                                          \
-            const uint16_t* g_ = bsrc[j] ? bsrc[j] + kofs_ : zero;                                  \
-            __builtin_amdgcn_global_load_lds((const void*)g_,                                      \
-                                             (lds_void*)(st_ + A_CH * 1024 + (wave * B_PW + j) * 1024), \
-                                             16, 0, 0);                                            \
+        const char* wk_ = (const char*)a.w + ((int64_t)3 * (KY) * a.Cin + (CC) * 32) * 2;          \
+        _Pragma("unroll") for (int q = 0; q < BQ; ++q) {                                            \
+            const int j_ = wave + 4 * q;                                                            \
+            if (j_ < S::B_LOADS)                                                                    \
+                __builtin_amdgcn_global_load_lds((const void*)(wk_ + bo[q]),                       \
+                                                 (lds_void*)(st_ + S::B_OFF + j_ * 1024), 16, 0, 0); \
         }                                                                                           \
     } while (0)
-
-    for (int s = 0; s < STAGES - 1; ++s)
-        if (s < nkt) DP_ISSUE_STAGE(kt0 + s, s);
-
-    // operand read offsets: row (l & 15) of a 16-row block, chunk (ks*4 + l/16) swizzled by (l & 7)
-    const int frow = lane & 15;
-    const int aoff = (wm * 64 + frow) * 128;
-    const int boff = A_CH * 1024 + (wn * WN + frow) * 128;
-    const int p0 = ((0 * 4 + (lane >> 4)) ^ (lane & 7)) * 16;
-    const int p1 = ((1 * 4 + (lane >> 4)) ^ (lane & 7)) * 16;
-
-    for (int it = 0; it < nkt; ++it) {
-        const int ahead = nkt - 1 - it;     // stages issued after this one, capped
-        if (ahead >= STAGES - 2)
-            wait_vmcnt<(STAGES - 2) * LOADS>();
-        else if (STAGES > 3 && ahead == 1)
-            wait_vmcnt<LOADS>();
-        else
-            wait_vmcnt<0>();
-        __syncthreads();
-        if (it + STAGES - 1 < nkt) DP_ISSUE_STAGE(kt0 + it + STAGES - 1, (it + STAGES - 1) % STAGES);
-        const char* st = smem + (it % STAGES) * STAGE;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int po = ks ? p1 : p0;
-            bf16x8 af[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8*)(st + aoff + i * 16 * 128 + po);
-#pragma unroll
-            for (int n = 0; n < NBK; ++n) {
-                const bf16x8 bfr = *(const bf16x8*)(st + boff + n * 16 * 128 + po);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr, acc[i][n], 0, 0, 0);
-            }
-        }
-    }
-#undef DP_ISSUE_STAGE
-    __syncthreads();   // all waves done with the ring; reuse it for the output tile
-
-    // ---- epilogue through LDS: lane holds pixel 4*(l/16)+r, channel l%16 of each block ----
-    const int ecol = lane & 15;
-    const int erow = 4 * (lane >> 4);
-    if (a.ksplit == 1) {
-        uint16_t* tile = (uint16_t*)smem;   // [BM2][BN] bf16
-#pragma unroll
-        for (int n = 0; n < NBK; ++n) {
-            const int ch = wn * WN + n * 16 + ecol;
-            const float bv = (a.bias && n0 + ch < a.Cout) ? a.bias[n0 + ch] : 0.f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    tile[(wm * 64 + i * 16 + erow + r) * BN + ch] = f32_to_bf16(acc[i][n][r] + bv);
-        }
-        __syncthreads();
-        constexpr int CPR = BN * 2 / 16;    // 16-byte chunks per output row
-        for (int q = tid; q < BM2 * CPR; q += 256) {
-            const int row = q / CPR, c16 = q - (q / CPR) * CPR;
-            const int m = m0 + row, co = n0 + c16 * 8;
-            if (m < a.M && co < a.Cout)
-                *(uint4*)(a.y + (int64_t)m * a.Cout + co) = *(const uint4*)(tile + row * BN + c16 * 8);
-        }
-    } else {
-        float* tile = (float*)smem;         // [BM2][BN] fp32
-#pragma unroll
-        for (int n = 0; n < NBK; ++n) {
-            const int ch = wn * WN + n * 16 + ecol;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) tile[(wm * 64 + i * 16 + erow + r) * BN + ch] = acc[i][n][r];
-        }
-        __syncthreads();
-        constexpr int CPR = BN * 4 / 16;
-        float* part = a.part + (int64_t)split * a.M * a.Cout;
-        for (int q = tid; q < BM2 * CPR; q += 256) {
-            const int row = q / CPR, c16 = q - (q / CPR) * CPR;
-            const int m = m0 + row, co = n0 + c16 * 4;
-            if (m < a.M && co < a.Cout)
-                *(float4*)(part + (int64_t)m * a.Cout + co) = *(const float4*)(tile + row * BN + c16 * 4);
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// bf16 implicit GEMM for small M: each wave owns a K range.
-//
-// A workgroup computes one 64-pixel x 80-channel tile; its 4 waves split the
-// workgroup's K range into 4 consecutive parts and each wave accumulates the
-// whole 64x80 tile (4x5 blocks of v_mfma_f32_16x16x32_bf16) over its part,
-// streaming its own A (64 rows) and B (80 rows) K tiles through a private
-// 2-stage LDS ring with direct-to-LDS loads -- no barrier in the main loop.
-// At the end the four accumulators are added through LDS in wave order
-// (deterministic) and the tile is written with coalesced 16-byte stores, as
-// bf16 output (+bias) or, when K is also split across workgroups, as fp32
-// partials for the ordered reduce kernel.
-// ---------------------------------------------------------------------------
-constexpr int KS_BM = 64;
-constexpr int KS_BN = 80;
-constexpr int KS_WAVE_LDS = 36 * 1024;                    // per wave; 4 waves = 144 KB
-
-// KB = K tile width (64: 2 stages of 18 KB; 32: 4 stages of 9 KB per wave).
-// Rows of a stage are KB*2 bytes; 16-byte chunk c of row r sits at slot
-// c ^ swz(r) (swz = r & 7 for 128-byte rows, (r >> 2) & 3 for 64-byte rows)
-// so the 16 rows x 16 bytes of an operand read spread over the LDS banks.
-template <int KB>
-__global__ __launch_bounds__(256) void conv3x3_bf16_wave_ksplit_kernel(ConvArgs a) {
-    constexpr int RB = KB * 2;                          // bytes per row
-    constexpr int SLOTS = RB / 16;                      // 16-byte chunks per row
-    constexpr int RPC = 1024 / RB;                      // rows per 1 KB DMA chunk
-    constexpr int A_CH = KS_BM * RB / 1024;             // DMA chunks per stage for A
-    constexpr int B_CH = KS_BN * RB / 1024;             // ... for B
-    constexpr int LOADS = A_CH + B_CH;
-    constexpr int STAGE = LOADS * 1024;
-    constexpr int STAGES = KS_WAVE_LDS / STAGE;         // 2 (KB=64) or 4 (KB=32)
-    constexpr int KSTEPS = KB / 32;
-    static_assert(STAGES >= 2, "ring depth");
-    __shared__ __attribute__((aligned(1024))) char smem[4 * KS_WAVE_LDS];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int mt = blockIdx.x / a.ntiles;
-    const int nt = blockIdx.x - mt * a.ntiles;
-    const int m0 = mt * KS_BM;
-    const int n0 = nt * KS_BN;
-    const int split = blockIdx.y;
-    const int kw0 = (int)((int64_t)a.ktiles * split / a.ksplit);
-    const int kw1 = (int)((int64_t)a.ktiles * (split + 1) / a.ksplit);
-    const int kt0 = kw0 + (kw1 - kw0) * wave / 4;
-    const int kt1 = kw0 + (kw1 - kw0) * (wave + 1) / 4;
-    const int nkt = kt1 - kt0;
-    const int cpt = a.Cin / KB;
-    const int wrow = 9 * a.Cin;
-    const uint16_t* zero = (const uint16_t*)g_zero_line;
-    char* ring = smem + wave * KS_WAVE_LDS;
-
-    auto swz = [](int row) { return SLOTS == 8 ? (row & 7) : ((row >> 2) & 3); };
-    const int sub = lane / SLOTS;
-    const int slot = lane % SLOTS;
-    int pb[A_CH], py[A_CH], px[A_CH], achunk[A_CH];
-#pragma unroll
-    for (int j = 0; j < A_CH; ++j) {
-        const int row = j * RPC + sub;
-        achunk[j] = (slot ^ swz(row)) * 8;
-        const int m = m0 + row;
-        if (m < a.M) {
-            const int hw = a.h * a.W;
-            pb[j] = m / hw;
-            const int rem = m - pb[j] * hw;
-            py[j] = rem / a.W;
-            px[j] = rem - py[j] * a.W;
-        } else {
-            pb[j] = -1;
-            py[j] = px[j] = 0;
-        }
-    }
-    uint32_t boff[B_CH];
-#pragma unroll
-    for (int j = 0; j < B_CH; ++j) {
-        const int row = j * RPC + sub;
-        int co = n0 + row;
-        if (co >= a.Cout) co = a.Cout - 1;       // clamped rows feed columns that are never stored
-        boff[j] = (uint32_t)(((co - n0) * wrow + (slot ^ swz(row)) * 8) * 2);
-    }
-    const char* wbase = (const char*)(a.w + (int64_t)n0 * wrow);
-    const uint16_t* asrc[A_CH];
-    int cur_tap = -1;
-
-#define DPK_ISSUE(KT, BUF)                                                                          \
+#define DPH_ISSUE(K, BUF)                                                                           \
     do {                                                                                            \
-        const int kt_ = (KT);                                                                       \
-        const int tap_ = kt_ / cpt;                                                                 \
-        const int coff_ = (kt_ - tap_ * cpt) * KB;                                                  \
-        if (tap_ != cur_tap) {                                                                      \
-            cur_tap = tap_;                                                                         \
-            const int ky_ = tap_ / 3, kx_ = tap_ - 3 * (tap_ / 3);                                  \
-            _Pragma("unroll") for (int j = 0; j < A_CH; ++j) {                                      \
-                const int r_ = a.r0 + py[j] + ky_ - 1;                                              \
-                const int x_ = px[j] + kx_ - 1;                                                     \
-                const bool ok_ = pb[j] >= 0 && r_ >= 0 && r_ < a.H && x_ >= 0 && x_ < a.W;          \
-                const bool fr_ = r_ >= a.r0 && r_ < a.r0 + a.h;                                     \
-                const int64_t fo_ = (((int64_t)pb[j] * a.h + (r_ - a.r0)) * a.W + x_) * a.Cin;      \
-                const int64_t so_ = (((int64_t)pb[j] * a.H + r_) * a.W + x_) * a.Cin;               \
-                asrc[j] = ok_ ? (fr_ ? a.xp + fo_ : a.xs + so_) + achunk[j] : nullptr;              \
-            }                                                                                       \
+        const int cc_ = (K) / 3;                                                                    \
+        switch ((K) - 3 * cc_) {                                                                    \
+            case 0: DPH_ISSUE_KY(cc_, 0, ap0, BUF); break;                                          \
+            case 1: DPH_ISSUE_KY(cc_, 1, ap1, BUF); break;                                          \
+            default: DPH_ISSUE_KY(cc_, 2, ap2, BUF); break;                                         \
         }                                                                                           \
-        char* st_ = ring + (BUF) * STAGE;                                                           \
-        _Pragma("unroll") for (int j = 0; j < A_CH; ++j) {                                          \
-            const uint16_t* g_ = asrc[j] ? asrc[j] + coff_ : zero;   /* padding rows: zero line */ \
-            __builtin_amdgcn_global_load_lds((const void*)g_, (lds_void*)(st_ + j * 1024), 16, 0, 0); \
-        }                                                                                           \
-        const char* wk_ = wbase + ((int64_t)tap_ * a.Cin + coff_) * 2;                              \
-        _Pragma("unroll") for (int j = 0; j < B_CH; ++j)                                            \
-            __builtin_amdgcn_global_load_lds((const void*)(wk_ + boff[j]),                         \
-                                             (lds_void*)(st_ + (A_CH + j) * 1024), 16, 0, 0);      \
     } while (0)
 
     f32x4 acc[4][5];
@@ -376,40 +255,130 @@ __global__ __launch_bounds__(256) void conv3x3_bf16_wave_ksplit_kernel(ConvArgs 
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int n = 0; n < 5; ++n) acc[i][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int aoff[2][3], boff;
+    operand_offsets<TR, BN>(lane, 2 * wm, wn, aoff, boff);
 
-    const int frow = lane & 15;
-    int po[KSTEPS];
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) po[ks] = ((ks * 4 + (lane >> 4)) ^ swz(frow)) * 16;
-    for (int s = 0; s < STAGES - 1; ++s)
-        if (s < nkt) DPK_ISSUE(kt0 + s, s);
-    for (int it = 0; it < nkt; ++it) {
-        // this wave's stage `it` has landed; later stages may still be in flight
-        const int ahead = nkt - 1 - it;
-        if (STAGES >= 4 && ahead >= 2) wait_vmcnt<(STAGES >= 4 ? 2 : 0) * LOADS>();
-        else if (STAGES >= 3 && ahead >= 1) wait_vmcnt<(STAGES >= 3 ? 1 : 0) * LOADS>();
-        else wait_vmcnt<0>();
-        if (it + STAGES - 1 < nkt) DPK_ISSUE(kt0 + it + STAGES - 1, (it + STAGES - 1) % STAGES);
-        const char* st = ring + (it % STAGES) * STAGE;
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            bf16x8 af[4], bfr[5];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8*)(st + (i * 16 + frow) * RB + po[ks]);
-#pragma unroll
-            for (int n = 0; n < 5; ++n) bfr[n] = *(const bf16x8*)(st + A_CH * 1024 + (n * 16 + frow) * RB + po[ks]);
-#pragma unroll
-            for (int n = 0; n < 5; ++n)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[n], acc[i][n], 0, 0, 0);
-        }
+    const int nk = a.kstages;
+    DPH_ISSUE(0, 0);
+    for (int it = 0; it < nk; ++it) {
+        wait_vmcnt<0>();     // this wave's loads of stage it have landed ...
+        __syncthreads();     // ... and everyone's; everyone is also done with stage it-1
+        if (it + 1 < nk) DPH_ISSUE(it + 1, (it + 1) & 1);
+        stage_mfma<BN>(smem + (it & 1) * S::BYTES, aoff, boff, acc);
     }
-#undef DPK_ISSUE
+#undef DPH_ISSUE
+#undef DPH_ISSUE_KY
+    __syncthreads();   // ring no longer read: reuse it for the output tile
+
+    // acc[i][n][r] = D[pixel 16i + 4(l>>4) + r of the wave][channel 16n + (l&15) of the wave]
+    uint16_t* tile = (uint16_t*)smem;    // [128 pixels][BN] bf16, pixel = tile row * 32 + column
+    const int ecol = lane & 15;
+    const int erow = 4 * (lane >> 4);
+#pragma unroll
+    for (int n = 0; n < 5; ++n) {
+        const int ch = wn * 80 + n * 16 + ecol;
+        const float bv = (a.bias && n0 + ch < a.Cout) ? a.bias[n0 + ch] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                tile[(wm * 64 + i * 16 + erow + r) * BN + ch] = f32_to_bf16(acc[i][n][r] + bv);
+    }
+    __syncthreads();
+    constexpr int CPR = BN * 2 / 16;    // 16-byte chunks per output pixel
+    for (int q = tid; q < 128 * CPR; q += kThreads) {
+        const int px = q / CPR, c16 = q - px * CPR;
+        const int y = ty0 + (px >> 5), x = tx0 + (px & 31), co = n0 + c16 * 8;
+        if (y < a.h && x < a.W && co < a.Cout)
+            *(uint4*)(a.y + (((int64_t)bb * a.h + y) * a.W + x) * a.Cout + co) =
+                *(const uint4*)(tile + px * BN + c16 * 8);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Small maps: tile 2 rows x 32 columns x 80 channels.  Each of the 4 waves takes a quarter of
+// the workgroup's stages and streams them through its own 2-stage ring (2 x 19.25 KB) -- no
+// barrier in the main loop; the four accumulators are then added through LDS in wave order
+// and written as bf16 (+bias) or, when K is also split across workgroups, as fp32 partials.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void conv3x3_bf16_halo_wave_kernel(ConvArgs a) {
+    constexpr int TR = 2, BN = 80;
+    using S = Stage<TR, BN>;
+    constexpr int WAVE_LDS = 2 * S::BYTES;
+    static_assert(4 * WAVE_LDS >= 4 * 64 * BN * 4 + 64 * BN * 2, "reduction area");
+    __shared__ __attribute__((aligned(1024))) char smem[4 * WAVE_LDS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    // logical order (channel tile, K split, pixel tile), pixel tile fastest
+    const int lt = xcd_order(blockIdx.x, gridDim.x);
+    const int mt = lt % a.mtiles;
+    const int rest = lt / a.mtiles;
+    const int split = rest % a.ksplit;
+    const int nt = rest / a.ksplit;
+    int bb, ty0, tx0;
+    tile_origin<TR>(a, mt, bb, ty0, tx0);
+    const int n0 = nt * BN;
+    const int k0 = (int)((int64_t)a.kstages * split / a.ksplit);
+    const int k1 = (int)((int64_t)a.kstages * (split + 1) / a.ksplit);
+    const int kb = k0 + (k1 - k0) * wave / 4;
+    const int nk = k0 + (k1 - k0) * (wave + 1) / 4 - kb;
+    const uint16_t* zero = (const uint16_t*)g_zero_line;
+    char* ring = smem + wave * WAVE_LDS;
+
+    const uint16_t* ap0[S::A_LOADS];
+    const uint16_t* ap1[S::A_LOADS];
+    const uint16_t* ap2[S::A_LOADS];
+#pragma unroll
+    for (int j = 0; j < S::A_LOADS; ++j) resolve_a_slot<TR>(a, bb, ty0, tx0, j * 64 + lane, ap0[j], ap1[j], ap2[j]);
+    uint32_t bo[S::B_LOADS];
+#pragma unroll
+    for (int j = 0; j < S::B_LOADS; ++j) bo[j] = b_slot_offset<BN>(a, n0, j * 64 + lane);
+
+#define DPW_ISSUE_KY(CC, KY, SRC, BUF)                                                              \
+    do {                                                                                            \
+        char* st_ = ring + (BUF) * S::BYTES;                                                        \
+        _Pragma("unroll") for (int j = 0; j < S::A_LOADS; ++j) {                                    \
+            const uint16_t* g_ = SRC[j] ? SRC[j] + (CC) * 32 : zero;                                \
+            if (j < S::A_LOADS - 1 || lane < S::A_TAIL)                                             \
+                __builtin_amdgcn_global_load_lds((const void*)g_, (lds_void*)(st_ + j * 1024), 16, 0, 0); \
+        }                                                                                           \
+        const char* wk_ = (const char*)a.w + ((int64_t)3 * (KY) * a.Cin + (CC) * 32) * 2;          \
+        _Pragma("unroll") for (int j = 0; j < S::B_LOADS; ++j)                                      \
+            __builtin_amdgcn_global_load_lds((const void*)(wk_ + bo[j]),                           \
+                                             (lds_void*)(st_ + S::B_OFF + j * 1024), 16, 0, 0);     \
+    } while (0)
+#define DPW_ISSUE(K, BUF)                                                                           \
+    do {                                                                                            \
+        const int cc_ = (K) / 3;                                                                    \
+        switch ((K) - 3 * cc_) {                                                                    \
+            case 0: DPW_ISSUE_KY(cc_, 0, ap0, BUF); break;                                          \
+            case 1: DPW_ISSUE_KY(cc_, 1, ap1, BUF); break;                                          \
+            default: DPW_ISSUE_KY(cc_, 2, ap2, BUF); break;                                         \
+        }                                                                                           \
+    } while (0)
+
+    f32x4 acc[4][5];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int n = 0; n < 5; ++n) acc[i][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    int aoff[2][3], boff;
+    operand_offsets<TR, BN>(lane, 0, 0, aoff, boff);
+
+    if (nk > 0) DPW_ISSUE(kb, 0);
+    for (int it = 0; it < nk; ++it) {
+        wait_vmcnt<0>();     // stage it has landed; stage it-1's reads finished before this point
+        if (it + 1 < nk) DPW_ISSUE(kb + it + 1, (it + 1) & 1);
+        stage_mfma<BN>(ring + (it & 1) * S::BYTES, aoff, boff, acc);
+    }
+#undef DPW_ISSUE
+#undef DPW_ISSUE_KY
     __syncthreads();   // every wave is done with its ring: reuse the LDS for the reduction
 
-    // acc[i][n][r] = C[pixel i*16 + 4*(l>>4) + r][channel n*16 + (l&15)]
-    float* red = (float*)smem;                   // [4 waves][64][80] fp32 (80 KB)
+    // acc[i][n][r] = D[pixel 16i + 4(l>>4) + r][channel 16n + (l&15)], pixel = tile row * 32 + column
+    float* red = (float*)smem;                   // [4 waves][64][80] fp32
     const int ecol = lane & 15;
     const int erow = 4 * (lane >> 4);
 #pragma unroll
@@ -418,17 +387,16 @@ __global__ __launch_bounds__(256) void conv3x3_bf16_wave_ksplit_kernel(ConvArgs 
         for (int n = 0; n < 5; ++n)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                red[(wave * KS_BM + i * 16 + erow + r) * KS_BN + n * 16 + ecol] = acc[i][n][r];
+                red[(wave * 64 + i * 16 + erow + r) * BN + n * 16 + ecol] = acc[i][n][r];
     __syncthreads();
-    // each thread: 4 consecutive channels of 5 (pixel, 4-channel) groups; sum waves in order
     if (a.ksplit == 1) {
-        uint16_t* tile = (uint16_t*)(smem + 4 * KS_BM * KS_BN * 4);   // [64][80] bf16 after the fp32 area
-        for (int q = tid; q < KS_BM * KS_BN / 4; q += 256) {
-            const int row = q / (KS_BN / 4), c4 = (q - row * (KS_BN / 4)) * 4;
-            float4 v = *(const float4*)(red + row * KS_BN + c4);
+        uint16_t* tile = (uint16_t*)(smem + 4 * 64 * BN * 4);   // [64][80] bf16 after the fp32 area
+        for (int q = tid; q < 64 * BN / 4; q += kThreads) {
+            const int px = q / (BN / 4), c4 = (q - px * (BN / 4)) * 4;
+            float4 v = *(const float4*)(red + px * BN + c4);
 #pragma unroll
             for (int w = 1; w < 4; ++w) {
-                const float4 u = *(const float4*)(red + (w * KS_BM + row) * KS_BN + c4);
+                const float4 u = *(const float4*)(red + (w * 64 + px) * BN + c4);
                 v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
             }
             const int co = n0 + c4;
@@ -438,28 +406,30 @@ __global__ __launch_bounds__(256) void conv3x3_bf16_wave_ksplit_kernel(ConvArgs 
             uint2 o;
             o.x = pack_bf16x2(v.x, v.y);
             o.y = pack_bf16x2(v.z, v.w);
-            *(uint2*)(tile + row * KS_BN + c4) = o;
+            *(uint2*)(tile + px * BN + c4) = o;
         }
         __syncthreads();
-        constexpr int CPR = KS_BN * 2 / 16;       // 10 chunks of 16 bytes per row
-        for (int q = tid; q < KS_BM * CPR; q += 256) {
-            const int row = q / CPR, c16 = q - (q / CPR) * CPR;
-            const int m = m0 + row, co = n0 + c16 * 8;
-            if (m < a.M && co < a.Cout)
-                *(uint4*)(a.y + (int64_t)m * a.Cout + co) = *(const uint4*)(tile + row * KS_BN + c16 * 8);
+        constexpr int CPR = BN * 2 / 16;       // 10 chunks of 16 bytes per pixel
+        for (int q = tid; q < 64 * CPR; q += kThreads) {
+            const int px = q / CPR, c16 = q - px * CPR;
+            const int y = ty0 + (px >> 5), x = tx0 + (px & 31), co = n0 + c16 * 8;
+            if (y < a.h && x < a.W && co < a.Cout)
+                *(uint4*)(a.y + (((int64_t)bb * a.h + y) * a.W + x) * a.Cout + co) =
+                    *(const uint4*)(tile + px * BN + c16 * 8);
         }
     } else {
         float* part = a.part + (int64_t)split * a.M * a.Cout;
-        for (int q = tid; q < KS_BM * KS_BN / 4; q += 256) {
-            const int row = q / (KS_BN / 4), c4 = (q - row * (KS_BN / 4)) * 4;
-            float4 v = *(const float4*)(red + row * KS_BN + c4);
+        for (int q = tid; q < 64 * BN / 4; q += kThreads) {
+            const int px = q / (BN / 4), c4 = (q - px * (BN / 4)) * 4;
+            float4 v = *(const float4*)(red + px * BN + c4);
 #pragma unroll
             for (int w = 1; w < 4; ++w) {
-                const float4 u = *(const float4*)(red + (w * KS_BM + row) * KS_BN + c4);
+                const float4 u = *(const float4*)(red + (w * 64 + px) * BN + c4);
                 v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
             }
-            const int m = m0 + row, co = n0 + c4;
-            if (m < a.M && co < a.Cout) *(float4*)(part + (int64_t)m * a.Cout + co) = v;
+            const int y = ty0 + (px >> 5), x = tx0 + (px & 31), co = n0 + c4;
+            if (y < a.h && x < a.W && co < a.Cout)
+                *(float4*)(part + (((int64_t)bb * a.h + y) * a.W + x) * a.Cout + co) = v;
         }
     }
 }
@@ -531,32 +501,25 @@ ConvPlan plan_conv(const Geom& g, int Cout, bool bf16) {
         p.kind = 0;
         return p;
     }
-    const int64_t M = (int64_t)g.B * g.h * g.W;
-    p.ktiles = 9 * g.C / BK;
-    const int64_t big_tiles = ((M + BM - 1) / BM) * ((Cout + BN - 1) / BN);
+    const int ntx = (g.W + kTileTC - 1) / kTileTC;
+    const int64_t big = (int64_t)g.B * ((g.h + 3) / 4) * ntx * ((Cout + 159) / 160);
+    p.ktiles = 3 * g.C / 32;          // K stages (cc, ky)
     int ks = 1;
-    if (big_tiles >= 128) {
-        // enough 128x160 tiles: waves share A and B through LDS; split K if < 256 tiles
+    if (big >= 384) {
+        // enough 128x160 tiles for two per CU: shared ring, no K split
         p.kind = 1;
-        p.bm = BM;
-        p.bn = BN;
-        p.mtiles = (int)((M + BM - 1) / BM);
-        p.ntiles = (Cout + BN - 1) / BN;
-        const int tiles = p.mtiles * p.ntiles;
-        if (tiles < 256) {
-            ks = (256 + tiles - 1) / tiles;
-            const int maxk = p.ktiles / 4 > 0 ? p.ktiles / 4 : 1;
-            if (ks > maxk) ks = maxk;
-        }
+        p.bm = 128;
+        p.bn = 160;
+        p.mtiles = (int)((int64_t)g.B * ((g.h + 3) / 4) * ntx);
+        p.ntiles = (Cout + 159) / 160;
     } else {
-        // small M: 64x80 tiles, K split over the 4 waves of a workgroup (and across
-        // workgroups until about 256 workgroups, keeping >= 2 K tiles per wave)
+        // 64x80 tiles, K split over the 4 waves of a workgroup and across workgroups until
+        // about 256 workgroups run, keeping >= 2 stages per wave
         p.kind = 2;
-        p.bm = KS_BM;
-        p.bn = KS_BN;
-        p.ktiles = 9 * g.C / kWaveKB;
-        p.mtiles = (int)((M + KS_BM - 1) / KS_BM);
-        p.ntiles = (Cout + KS_BN - 1) / KS_BN;
+        p.bm = 64;
+        p.bn = 80;
+        p.mtiles = (int)((int64_t)g.B * ((g.h + 1) / 2) * ntx);
+        p.ntiles = (Cout + 79) / 80;
         const int tiles = p.mtiles * p.ntiles;
         if (tiles < 256) {
             ks = (256 + tiles / 2) / tiles;
@@ -567,6 +530,7 @@ ConvPlan plan_conv(const Geom& g, int Cout, bool bf16) {
     }
     if (ks > 32) ks = 32;
     p.ksplit = ks;
+    const int64_t M = (int64_t)g.B * g.h * g.W;
     p.ws_bytes = ks > 1 ? (size_t)ks * M * Cout * sizeof(float) : 0;
     return p;
 }
@@ -597,15 +561,17 @@ hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout,
     a.h = g.h;
     a.r0 = g.r0;
     a.M = g.B * g.h * g.W;
-    a.ktiles = plan.ktiles;
-    a.ksplit = plan.ksplit;
+    a.ntx = (g.W + kTileTC - 1) / kTileTC;
+    a.nty = (g.h + (plan.kind == 1 ? 3 : 1)) / (plan.kind == 1 ? 4 : 2);
+    a.mtiles = plan.mtiles;
     a.ntiles = plan.ntiles;
-    dim3 grid((unsigned)(plan.mtiles * plan.ntiles), (unsigned)plan.ksplit);
-    if (plan.kind == 2) {
-        conv3x3_bf16_wave_ksplit_kernel<kWaveKB><<<grid, kThreads, 0, stream>>>(a);
-    }
+    a.kstages = plan.ktiles;
+    a.ksplit = plan.ksplit;
+    const unsigned grid = (unsigned)(plan.mtiles * plan.ntiles * plan.ksplit);
+    if (plan.kind == 1)
+        conv3x3_bf16_halo_tile_kernel<<<grid, kThreads, 0, stream>>>(a);
     else
-        conv3x3_bf16_lds_dma_kernel<BN, kStages><<<grid, kThreads, 0, stream>>>(a);
+        conv3x3_bf16_halo_wave_kernel<<<grid, kThreads, 0, stream>>>(a);
     if (plan.ksplit > 1) {
         const int64_t total4 = (int64_t)a.M * Cout / 4;
         conv_splitk_reduce_kernel<<<(unsigned)((total4 + 255) / 256), 256, 0, stream>>>(

@@ -49,6 +49,16 @@ def test_ragged_bf16(B, H, W, cin, cout, P):
         run_case(B, H, W, cin, cout, P, i, "bf16", seed=i)
 
 
+@pytest.mark.parametrize("B,H,W,cin,cout,P", [
+    (1, 124, 500, 64, 288, 2),  # large-map tiles: 62 = 15*4 + 2 rows, 500 = 15*32 + 20 columns, 288 = 160 + 128
+    (2, 96, 254, 64, 320, 2),   # large-map tiles over two batch images, ragged columns
+])
+def test_large_map_tiles_bf16(B, H, W, cin, cout, P):
+    for i in range(P):
+        announce("conv large-map tiles", B, H, W, cin, cout, P, i)
+        run_case(B, H, W, cin, cout, P, i, "bf16", seed=20 + i)
+
+
 @pytest.mark.parametrize("B,H,W,cin,cout,P", [(1, 6, 5, 3, 4, 3), (2, 8, 4, 8, 5, 2), (1, 16, 16, 32, 32, 2)])
 def test_f32(B, H, W, cin, cout, P):
     for i in range(P):
