@@ -34,7 +34,20 @@ PEAK_HBM_GBS = 8000.0
 # source file of each call's main kernel (for the counter file's staleness check)
 KERNEL_SOURCES = {"conv": "k_conv.hip", "attn": "k_attention.hip", "gn": "k_groupnorm.hip",
                   "gn_silu": "k_groupnorm.hip", "stale_update": "k_splice.hip"}
-KERNEL_NAMES = {"conv": "conv3x3_bf16_mfma_kernel", "attn": "attn_bf16_d64_kernel"}
+
+
+def kernel_name(op, cfg, cout=None):
+    """Main kernel of a call: the bf16 conv picks its tile kernel from the map size (the
+    library's plan: 128x160 tiles when at least 384 of them exist, else 64x80 tiles)."""
+    if op == "attn":
+        return "attn_bf16_d64_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel"
+    if op == "conv":
+        if cfg.dtype != "bf16":
+            return "conv3x3_f32_direct_kernel"
+        cout = cout or cfg.C
+        big = cfg.B * -(-cfg.h // 4) * -(-cfg.W // 32) * -(-cout // 160)
+        return "conv3x3_bf16_halo_tile_kernel" if big >= 384 else "conv3x3_bf16_halo_wave_kernel"
+    return op
 
 
 def log(*a):
@@ -171,7 +184,7 @@ def main():
     dom = max(compute, key=lambda k: per_call_us[k])
     dom_flops = cfg.conv_flops() if dom == "conv" else cfg.attn_flops()
     achieved = dom_flops / (per_call_us[dom] * 1e-6) / 1e12
-    roofline = {"bound": "mfma", "kernel": KERNEL_NAMES.get(dom, dom), "achieved": round(achieved, 2),
+    roofline = {"bound": "mfma", "kernel": kernel_name(dom, cfg), "achieved": round(achieved, 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": traffic_for(dom, cfg.name),
                 "algorithmic_flops_per_launch": dom_flops}
