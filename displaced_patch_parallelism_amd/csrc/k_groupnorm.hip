@@ -11,16 +11,20 @@
 //
 // Two launches, both streaming the band [B][h*W][C] with 16-byte vectors.
 // A block is vpt x R threads: thread (cv, r) owns channel vector cv (8 bf16
-// or 4 f32 channels) and walks token rows r, r+R, ... of the block's range
-// with four loads in flight, so per-channel state stays in registers.
+// or 4 f32 channels) and token rows r, r+R, ... of the block's range, so
+// per-channel state stays in registers.
 //   1. gn_stats: fp32 per-channel sums, reduced through LDS in a fixed order
-//      to per-group (sum, sum of squares) partials [block][B][G].
-//   2. gn_apply: every block first adds the partials of its batch in a fixed
-//      order, forms the fresh moments (block 0 stores them), combines them
-//      with the stale table into (mean, rstd) and per-channel (scale, shift),
-//      then writes y = x*scale + shift (+ SiLU) rounded to the storage type.
-// Both kernels use the same token split (about one block per CU).
-// No atomics: results are bitwise reproducible.
+//      to per-group (sum, sum of squares) partials [block][B][G]; at most 128
+//      blocks per batch, so the partials stay small.
+//   2. gn_apply: each block owns 4 token rows per thread.  It issues the loads
+//      of its tokens, gamma/beta and the stale moments first; then adds the
+//      statistics partials of its batch (every partial load in flight at
+//      once, each lane summing its share in a fixed order, lanes combined in
+//      order through LDS), forms the fresh moments (block 0 stores them),
+//      combines them with the stale table into (mean, rstd), and writes
+//      y = x*scale + shift (+ SiLU) rounded to the storage type.
+// The statistics split depends only on the geometry, so the fresh moments are
+// bitwise identical whichever entry path computes them.  No atomics.
 
 
 #include "dp_device.h"
@@ -115,13 +119,15 @@ __global__ void gn_stats_kernel(const void* __restrict__ x, int64_t tokens, int 
     }
 }
 
+constexpr int kApplyTokensPerThread = 4;
+
 struct GnApplyArgs {
     const void* x;
     void* y;                 // null: moments only
     const float2* partial;   // [nblk][B][G]
-    int nblk;
+    int nblk;                // statistics blocks per batch
     int64_t tokens;          // per batch
-    int B, C, G, P, i, mode, vpt, rows, tok_per_blk;
+    int B, C, G, P, i, mode, vpt, rows, tok_per_blk;   // tok_per_blk: tokens per apply block
     float inv_count, eps;
     const float* stale;      // [P][B][G][2]
     const float* gamma;
@@ -129,33 +135,72 @@ struct GnApplyArgs {
     float* fresh_out;        // [B][G][2] or null
 };
 
-// Every block: (1) adds the stats partials of its batch in a fixed order and
-// forms each group's fresh moments (block 0 of the batch stores them); (2)
-// combines them with the stale table per mode into (mean, rstd) and this
-// thread's per-channel (scale, shift); (3) normalises its token range.
 template <bool BF16, bool SILU>
 __global__ void gn_apply_kernel(GnApplyArgs a) {
     constexpr int VEC = BF16 ? 8 : 4;
+    constexpr int TPT = kApplyTokensPerThread;
     extern __shared__ float2 gsh[];          // [lanes_per_g][G] partial sums, then [G] (mean, rstd)
     const int tid = threadIdx.x;
     const int b = blockIdx.y;
     const int G = a.G;
-    const int lanes_per_g = blockDim.x / G;  // >= 1: the plan gives blocks of >= G threads
-    if (tid < lanes_per_g * G) {
+    const int cv = tid % a.vpt;
+    const int r = tid / a.vpt;
+    const bool data = a.y != nullptr && r < a.rows;
+
+    // (1) independent loads first: this thread's tokens, its channels' gamma/beta, and (one
+    // thread per group) the stale moments the mode combines with the fresh ones
+    const int64_t t0 = (int64_t)blockIdx.x * a.tok_per_blk + r;
+    const int64_t base = (int64_t)b * a.tokens * a.vpt + cv;
+    const uint4* xv = (const uint4*)a.x + base;
+    uint4 v[TPT];
+    float ga[VEC], be[VEC];
+    if (data) {
+#pragma unroll
+        for (int u = 0; u < TPT; ++u)
+            if (t0 + u * a.rows < a.tokens) v[u] = xv[(t0 + u * a.rows) * a.vpt];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const int c = cv * VEC + e;
+            ga[e] = a.gamma ? a.gamma[c] : 1.f;
+            be[e] = a.beta ? a.beta[c] : 0.f;
+        }
+    }
+    float st_e = 0.f, st_q = 0.f;            // sum of the other bands' stale moments (thread g)
+    if (tid < G && a.mode != 1) {
+        for (int j = 0; j < a.P; ++j) {
+            if (a.mode == 0 && j == a.i) continue;
+            st_e += a.stale[((int64_t)j * a.B + b) * G * 2 + tid * 2 + 0];
+            st_q += a.stale[((int64_t)j * a.B + b) * G * 2 + tid * 2 + 1];
+        }
+    }
+
+    // (2) fresh moments: lane j0 of group g sums partials j0, j0+L, ... in order (8 loads in
+    // flight), then the L lane sums are added in lane order
+    const int L = blockDim.x / G;            // >= 1: the plan gives blocks of >= G threads
+    if (tid < L * G) {
         const int g = tid % G, j0 = tid / G;
         float sa = 0.f, sq = 0.f;
-        for (int j = j0; j < a.nblk; j += lanes_per_g) {
-            const float2 v = a.partial[((int64_t)j * a.B + b) * G + g];
-            sa += v.x;
-            sq += v.y;
+        for (int jb = j0; jb < a.nblk; jb += 8 * L) {
+            float2 pv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int j = jb + u * L;
+                pv[u] = j < a.nblk ? a.partial[((int64_t)j * a.B + b) * G + g] : make_float2(0.f, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                sa += pv[u].x;
+                sq += pv[u].y;
+            }
         }
         gsh[j0 * G + g] = make_float2(sa, sq);
     }
     __syncthreads();
-    float2* mr = gsh + lanes_per_g * G;
-    for (int g = tid; g < G; g += blockDim.x) {
+    float2* mr = gsh + L * G;
+    if (tid < G) {
+        const int g = tid;
         float sa = 0.f, sq = 0.f;
-        for (int j = 0; j < lanes_per_g; ++j) {
+        for (int j = 0; j < L; ++j) {
             sa += gsh[j * G + g].x;
             sq += gsh[j * G + g].y;
         }
@@ -165,67 +210,46 @@ __global__ void gn_apply_kernel(GnApplyArgs a) {
             a.fresh_out[(b * G + g) * 2 + 1] = qm;
         }
         float E = m, Q = qm;
-        if (a.mode != 1) {  // corrected (0) or stale (2): the table in band order
-            float se = 0.f, sqq = 0.f;
-            for (int j = 0; j < a.P; ++j) {
-                if (a.mode == 0 && j == a.i) {
-                    se += m;
-                    sqq += qm;
-                } else {
-                    se += a.stale[((int64_t)j * a.B + b) * G * 2 + g * 2 + 0];
-                    sqq += a.stale[((int64_t)j * a.B + b) * G * 2 + g * 2 + 1];
-                }
-            }
-            E = se / (float)a.P;
-            Q = sqq / (float)a.P;
+        if (a.mode == 0) {            // corrected: own band fresh, the others stale
+            E = (m + st_e) / (float)a.P;
+            Q = (qm + st_q) / (float)a.P;
+        } else if (a.mode == 2) {     // stale: every band from the table
+            E = st_e / (float)a.P;
+            Q = st_q / (float)a.P;
         }
         const float var = fmaxf(Q - E * E, 0.f);
         mr[g] = make_float2(E, 1.0f / sqrtf(var + a.eps));
     }
     if (!a.y) return;
     __syncthreads();
-    const int cv = tid % a.vpt;
-    const int r = tid / a.vpt;
-    if (r >= a.rows) return;
+    if (!data) return;
+
+    // (3) normalise the tokens loaded in (1)
     const int cg = a.C / G;
     float sc[VEC], sf[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-        const int c = cv * VEC + e;
-        const float2 m = mr[c / cg];
-        const float ga = a.gamma ? a.gamma[c] : 1.f;
-        const float be = a.beta ? a.beta[c] : 0.f;
-        sc[e] = m.y * ga;
-        sf[e] = be - m.x * sc[e];
+        const float2 mv = mr[(cv * VEC + e) / cg];
+        sc[e] = mv.y * ga[e];
+        sf[e] = be[e] - mv.x * sc[e];
     }
-    const int64_t t0 = (int64_t)blockIdx.x * a.tok_per_blk;
-    int64_t t1 = t0 + a.tok_per_blk;
-    if (t1 > a.tokens) t1 = a.tokens;
-    const int64_t base = (int64_t)b * a.tokens * a.vpt + cv;
-    const uint4* xv = (const uint4*)a.x + base;
     uint4* yv = (uint4*)a.y + base;
-    int64_t t = t0 + r;
-    for (; t < t1; t += 4 * a.rows) {
-        uint4 v[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            if (t + u * a.rows < t1) v[u] = xv[(t + u * a.rows) * a.vpt];
+    for (int u = 0; u < TPT; ++u) {
+        const int64_t t = t0 + u * a.rows;
+        if (t >= a.tokens) continue;
+        float f[VEC];
+        to_f32<BF16>(v[u], f);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (t + u * a.rows >= t1) continue;
-            float f[VEC];
-            to_f32<BF16>(v[u], f);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                float z = fmaf(f[e], sc[e], sf[e]);
-                if (SILU) z = silu(z);
-                f[e] = z;
-            }
-            uint4 o;
-            if (BF16) o = pack8(f);
-            else o = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
-            yv[(t + u * a.rows) * a.vpt] = o;
+        for (int e = 0; e < VEC; ++e) {
+            float z = fmaf(f[e], sc[e], sf[e]);
+            if (SILU) z = silu(z);
+            f[e] = z;
         }
+        uint4 o;
+        if (BF16) o = pack8(f);
+        else o = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+        yv[t * a.vpt] = o;
     }
 }
 
@@ -238,13 +262,9 @@ hipError_t launch_gn_typed(const Geom& g, const GnPlan& plan, GnApplyArgs a, flo
         gn_stats_kernel<BF16><<<grid, plan.threads, shmem, stream>>>(a.x, a.tokens, g.C, a.G, plan.vpt, plan.rows,
                                                                     plan.tok_per_blk, partial);
     }
-    // apply: the same token split (<= 256 blocks); a moments-only call runs one block per batch
-    int64_t nb = 1;
-    a.tok_per_blk = (int)a.tokens;
-    if (a.y) {
-        nb = plan.nblk;
-        a.tok_per_blk = plan.tok_per_blk;
-    }
+    // apply: rows * 4 tokens per block; a moments-only call runs one block per batch
+    a.tok_per_blk = plan.rows * kApplyTokensPerThread;
+    const int64_t nb = a.y ? plan.nblk_apply : 1;
     const size_t shmem = ((size_t)(plan.threads / a.G) * a.G + a.G) * sizeof(float2);
     gn_apply_kernel<BF16, SILU><<<dim3((unsigned)nb, (unsigned)g.B), plan.threads, shmem, stream>>>(a);
     return hipGetLastError();
@@ -264,12 +284,15 @@ GnPlan plan_groupnorm(const Geom& g, int G, bool bf16) {
         p.threads = p.vpt * p.rows;
     }
     const int64_t tokens = g.band_tokens();
-    // Token split shared by both kernels (so the fresh moments never depend on the call's
-    // other arguments): about one block per CU over the whole batch, 256 blocks.
-    int64_t per_batch = 256 / g.B;
-    if (per_batch < 1) per_batch = 1;
-    p.tok_per_blk = (int)((tokens + per_batch - 1) / per_batch);
-    p.nblk = (int)((tokens + p.tok_per_blk - 1) / p.tok_per_blk);
+    // Statistics split (depends only on the geometry): at least one round of 4 token rows per
+    // thread, at most 128 blocks per batch.
+    int64_t tpb = (int64_t)p.rows * 4;
+    if ((tokens + tpb - 1) / tpb > 128) tpb = (tokens + 127) / 128;
+    p.tok_per_blk = (int)tpb;
+    p.nblk = (int)((tokens + tpb - 1) / tpb);
+    // Apply split: 4 token rows per thread.
+    const int64_t tpa = (int64_t)p.rows * 4;
+    p.nblk_apply = (int)((tokens + tpa - 1) / tpa);
     p.partial_floats = (size_t)p.nblk * g.B * G * 2;
     p.ws_bytes = p.partial_floats * sizeof(float);
     return p;
