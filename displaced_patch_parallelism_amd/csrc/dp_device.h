@@ -43,6 +43,11 @@ __device__ __forceinline__ uint4 pack8(const float* f) {
     return v;
 }
 
-__device__ __forceinline__ float silu(float y) { return y / (1.0f + __expf(-y)); }
+// SiLU y * sigmoid(y) as y * rcp(1 + 2^(-y log2 e)): v_exp_f32 and v_rcp_f32 (about 1 ulp
+// each) instead of an IEEE division.  Saturates correctly: exp overflows to inf for y << 0
+// (rcp gives 0, so the result is -0) and underflows to 0 for y >> 0 (result y).
+__device__ __forceinline__ float silu(float y) {
+    return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-y * 1.4426950408889634f));
+}
 
 }  // namespace dp

@@ -13,10 +13,10 @@
 // A block is vpt x R threads: thread (cv, r) owns channel vector cv (8 bf16
 // or 4 f32 channels) and token rows r, r+R, ... of the block's range, so
 // per-channel state stays in registers.
-//   1. gn_stats: fp32 per-channel sums, reduced through LDS in a fixed order
+//   1. gn_stats: 8 token loads in flight per thread; fp32 per-channel sums, reduced through LDS in a fixed order
 //      to per-group (sum, sum of squares) partials [block][B][G]; at most 128
 //      blocks per batch, so the partials stay small.
-//   2. gn_apply: each block owns 4 token rows per thread.  It issues the loads
+//   2. gn_apply: each block owns 4 token rows per thread (one round).  It issues the loads
 //      of its tokens, gamma/beta and the stale moments first; then adds the
 //      statistics partials of its batch (every partial load in flight at
 //      once, each lane summing its share in a fixed order, lanes combined in
@@ -65,12 +65,12 @@ __global__ void gn_stats_kernel(const void* __restrict__ x, int64_t tokens, int 
     for (int e = 0; e < VEC; ++e) s[e] = q[e] = 0.f;
     const uint4* xb = (const uint4*)x + (int64_t)b * tokens * vpt + cv;
     int64_t t = t0 + r;
-    for (; t + 3 * rows < t1; t += 4 * rows) {
-        uint4 v[4];
+    for (; t + 7 * rows < t1; t += 8 * rows) {
+        uint4 v[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = xb[(t + u * rows) * vpt];
+        for (int u = 0; u < 8; ++u) v[u] = xb[(t + u * rows) * vpt];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < 8; ++u) {
             float f[VEC];
             to_f32<BF16>(v[u], f);
 #pragma unroll
@@ -155,9 +155,11 @@ __global__ void gn_apply_kernel(GnApplyArgs a) {
     uint4 v[TPT];
     float ga[VEC], be[VEC];
     if (data) {
+        const int64_t t_end = (int64_t)(blockIdx.x + 1) * a.tok_per_blk < a.tokens
+                                  ? (int64_t)(blockIdx.x + 1) * a.tok_per_blk : a.tokens;
 #pragma unroll
         for (int u = 0; u < TPT; ++u)
-            if (t0 + u * a.rows < a.tokens) v[u] = xv[(t0 + u * a.rows) * a.vpt];
+            if (t0 + u * a.rows < t_end) v[u] = xv[(t0 + u * a.rows) * a.vpt];
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
             const int c = cv * VEC + e;
@@ -224,7 +226,7 @@ __global__ void gn_apply_kernel(GnApplyArgs a) {
     __syncthreads();
     if (!data) return;
 
-    // (3) normalise the tokens loaded in (1)
+    // (3) normalise: the tokens loaded in (1), then the block's further rounds of 4 rows
     const int cg = a.C / G;
     float sc[VEC], sf[VEC];
 #pragma unroll
@@ -234,22 +236,31 @@ __global__ void gn_apply_kernel(GnApplyArgs a) {
         sf[e] = be[e] - mv.x * sc[e];
     }
     uint4* yv = (uint4*)a.y + base;
+    const int64_t t_end = (int64_t)(blockIdx.x + 1) * a.tok_per_blk < a.tokens
+                              ? (int64_t)(blockIdx.x + 1) * a.tok_per_blk : a.tokens;
+    for (int64_t tr = t0;; tr += TPT * a.rows) {
 #pragma unroll
-    for (int u = 0; u < TPT; ++u) {
-        const int64_t t = t0 + u * a.rows;
-        if (t >= a.tokens) continue;
-        float f[VEC];
-        to_f32<BF16>(v[u], f);
+        for (int u = 0; u < TPT; ++u) {
+            const int64_t t = tr + u * a.rows;
+            if (t >= t_end) continue;
+            float f[VEC];
+            to_f32<BF16>(v[u], f);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            float z = fmaf(f[e], sc[e], sf[e]);
-            if (SILU) z = silu(z);
-            f[e] = z;
+            for (int e = 0; e < VEC; ++e) {
+                float z = fmaf(f[e], sc[e], sf[e]);
+                if (SILU) z = silu(z);
+                f[e] = z;
+            }
+            uint4 o;
+            if (BF16) o = pack8(f);
+            else o = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+            yv[t * a.vpt] = o;
         }
-        uint4 o;
-        if (BF16) o = pack8(f);
-        else o = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
-        yv[t * a.vpt] = o;
+        const int64_t tn = tr + TPT * a.rows;
+        if (tn >= t_end) break;
+#pragma unroll
+        for (int u = 0; u < TPT; ++u)
+            if (tn + u * a.rows < t_end) v[u] = xv[(tn + u * a.rows) * a.vpt];
     }
 }
 
@@ -262,8 +273,9 @@ hipError_t launch_gn_typed(const Geom& g, const GnPlan& plan, GnApplyArgs a, flo
         gn_stats_kernel<BF16><<<grid, plan.threads, shmem, stream>>>(a.x, a.tokens, g.C, a.G, plan.vpt, plan.rows,
                                                                     plan.tok_per_blk, partial);
     }
-    // apply: rows * 4 tokens per block; a moments-only call runs one block per batch
-    a.tok_per_blk = plan.rows * kApplyTokensPerThread;
+    // apply: the plan's rounds of rows * 4 tokens per block; a moments-only call runs one
+    // block per batch
+    a.tok_per_blk = plan.tok_per_blk_apply;
     const int64_t nb = a.y ? plan.nblk_apply : 1;
     const size_t shmem = ((size_t)(plan.threads / a.G) * a.G + a.G) * sizeof(float2);
     gn_apply_kernel<BF16, SILU><<<dim3((unsigned)nb, (unsigned)g.B), plan.threads, shmem, stream>>>(a);
@@ -284,15 +296,16 @@ GnPlan plan_groupnorm(const Geom& g, int G, bool bf16) {
         p.threads = p.vpt * p.rows;
     }
     const int64_t tokens = g.band_tokens();
-    // Statistics split (depends only on the geometry): at least one round of 4 token rows per
-    // thread, at most 128 blocks per batch.
-    int64_t tpb = (int64_t)p.rows * 4;
+    // Statistics split (depends only on the geometry): at least 8 token rows per thread (one
+    // round of loads), at most 128 blocks per batch.
+    int64_t tpb = (int64_t)p.rows * 8;
     if ((tokens + tpb - 1) / tpb > 128) tpb = (tokens + 127) / 128;
     p.tok_per_blk = (int)tpb;
     p.nblk = (int)((tokens + tpb - 1) / tpb);
-    // Apply split: 4 token rows per thread.
-    const int64_t tpa = (int64_t)p.rows * 4;
-    p.nblk_apply = (int)((tokens + tpa - 1) / tpa);
+    // Apply split: one round of 4 token rows per thread, so every block's loads are in flight
+    // together (a whole band is a few MB to a few tens of MB).
+    p.tok_per_blk_apply = p.rows * 4;
+    p.nblk_apply = (int)((tokens + p.tok_per_blk_apply - 1) / p.tok_per_blk_apply);
     p.partial_floats = (size_t)p.nblk * g.B * G * 2;
     p.ws_bytes = p.partial_floats * sizeof(float);
     return p;
