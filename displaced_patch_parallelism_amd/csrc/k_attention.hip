@@ -215,9 +215,14 @@ __global__ __launch_bounds__(64 * WAVES) void attn_bf16_d64_kernel(AttnArgs a) {
                 if (off + 32 >= kvalid) s1[i] = -INFINITY;
             }
         }
-        float mx = fmaxf(s0[0], s1[0]);
+        // two independent chains of 3-input maxima (v_max3_f32)
+        float mx0 = fmaxf(s0[0], s0[1]), mx1 = fmaxf(s1[0], s1[1]);
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+        for (int i = 2; i < 16; i += 2) {
+            mx0 = fmaxf(fmaxf(mx0, s0[i]), s0[i + 1]);
+            mx1 = fmaxf(fmaxf(mx1, s1[i]), s1[i + 1]);
+        }
+        float mx = fmaxf(mx0, mx1);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         // rescale the running sum and O only when some query's max grew
         const float m_new = fmaxf(m_run, mx * a.sc);
