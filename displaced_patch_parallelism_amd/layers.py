@@ -19,8 +19,8 @@ from typing import Dict, List, Optional, Sequence, Tuple
 
 import torch
 
-from . import (Patch, dp_attention_splice, dp_conv3x3_halo, dp_groupnorm_async, dp_stale_update,
-               dp_stats_update)
+from . import (Patch, _dtype_code, dp_attention_splice, dp_conv3x3_halo, dp_groupnorm_async,
+               dp_stale_update, dp_stats_update, workspace_bytes)
 
 
 def torch_dtype(name):
@@ -57,6 +57,18 @@ class DisplacedLayer:
         # patch-sized intermediates, reused by every step
         band = (c.B, c.h, c.W, c.C)
         self.bufs = [torch.empty(band, dtype=self.dt, device=self.device) for _ in c.graph]
+        # one workspace for every call of a step (calls are ordered on one stream); owned by the
+        # layer so a captured graph keeps pointing at live memory
+        code = _dtype_code(self.bufs[0])
+        need = 0
+        for w, _ in self.convs:
+            need = max(need, workspace_bytes("conv", self.patch(0), code, int(w.shape[0])))
+        for s in c.graph:
+            if s in ("gn", "gn_silu"):
+                need = max(need, workspace_bytes("groupnorm", self.patch(0), code, c.G))
+            elif s == "attn":
+                need = max(need, workspace_bytes("attention", self.patch(0), code, c.heads, c.C // c.heads))
+        self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
 
     def patch(self, i) -> Patch:
         c = self.cfg
@@ -70,6 +82,40 @@ class DisplacedLayer:
         return t.reshape(t.shape[0], -1, t.shape[-1])
 
     # ---- one patch, displaced ------------------------------------------------
+    def calls(self, x_patch, i, gn_mode="corrected", update_state=True):
+        """Patch i's displaced layer step as a list of (name, launch, output): each launch
+        enqueues one C-ABI call on the current stream.  Running them in order is one step
+        (without the splice of ``step`` when the state is not refreshed in place)."""
+        c = self.cfg
+        p = self.patch(i)
+        in_place = update_state and c.B == 1 and gn_mode == "corrected"
+        h = x_patch
+        out_list = []
+        conv_i = 0
+        for k, s in enumerate(c.graph):
+            nxt = k + 1
+            if in_place and nxt < len(c.graph) and nxt in self.maps:
+                out = self.maps[nxt][:, i * c.h:(i + 1) * c.h]      # contiguous for B == 1
+            else:
+                out = self.bufs[k]
+            if s in ("gn", "gn_silu"):
+                stats = self.table[i] if in_place else self.fresh_stats
+                act = "silu" if s == "gn_silu" else None
+                fn = (lambda h=h, out=out, stats=stats, act=act: dp_groupnorm_async(
+                    p, h, c.G, self.table, c.eps, gn_mode, act, fresh_stats_out=stats, y_patch=out, ws=self.ws))
+            elif s == "conv":
+                w, b = self.convs[conv_i]
+                conv_i += 1
+                fn = (lambda h=h, out=out, k=k, w=w, b=b: dp_conv3x3_halo(
+                    p, h, self.maps[k], w, b, y_patch=out, ws=self.ws))
+            else:
+                tok, st, o = self._tok(h), self._tok(self.maps[k]), self._tok(out)
+                fn = (lambda tok=tok, st=st, o=o: dp_attention_splice(
+                    p, c.heads, tok, tok, tok, st, st, o_patch=o, ws=self.ws))
+            out_list.append((s, fn, out))
+            h = out
+        return out_list
+
     def step(self, x_patch, i, gn_mode="corrected", update_state=True, events=None) -> List[torch.Tensor]:
         """Patch i's displaced layer step; returns every graph step's patch output.
 
@@ -87,36 +133,32 @@ class DisplacedLayer:
         launches on), appended to events[name] as (start, end).
         """
         c = self.cfg
-        p = self.patch(i)
         in_place = update_state and c.B == 1 and gn_mode == "corrected"
-        h = x_patch
         outs = []
-        conv_i = 0
-        for k, s in enumerate(c.graph):
-            nxt = k + 1
-            if in_place and nxt < len(c.graph) and nxt in self.maps:
-                out = self.maps[nxt][:, i * c.h:(i + 1) * c.h]      # contiguous for B == 1
-            else:
-                out = self.bufs[k]
+        for s, fn, out in self.calls(x_patch, i, gn_mode, update_state):
             ev = _mark(events, s)
-            if s in ("gn", "gn_silu"):
-                stats = self.table[i] if in_place else self.fresh_stats
-                dp_groupnorm_async(p, h, c.G, self.table, c.eps, gn_mode, "silu" if s == "gn_silu" else None,
-                                   fresh_stats_out=stats, y_patch=out)
-            elif s == "conv":
-                w, b = self.convs[conv_i]
-                conv_i += 1
-                dp_conv3x3_halo(p, h, self.maps[k], w, b, y_patch=out)
-            elif s == "attn":
-                tok = self._tok(h)
-                st = self._tok(self.maps[k])
-                dp_attention_splice(p, c.heads, tok, tok, tok, st, st, o_patch=self._tok(out))
+            fn()
             _done(ev)
             outs.append(out)
-            h = out
         if update_state and not in_place:
             self.splice_state(i, x_patch, outs, events)
         return outs
+
+    def capture(self, x_patch, i, gn_mode="corrected", update_state=True, steps=1):
+        """``steps`` consecutive steps captured as one HIP graph (torch.cuda.CUDAGraph);
+        replaying it repeats them on the same buffers with no host launch cost (a graph
+        launch has a fixed cost of its own, which several steps per graph amortise)."""
+        side = torch.cuda.Stream(self.device)
+        side.wait_stream(torch.cuda.current_stream(self.device))
+        with torch.cuda.stream(side):
+            for _ in range(2):
+                self.step(x_patch, i, gn_mode, update_state)
+        torch.cuda.current_stream(self.device).wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(steps):
+                self.step(x_patch, i, gn_mode, update_state)
+        return graph
 
     def splice_state(self, i, x_patch, outs, events=None):
         """Write patch i's fresh statistics and consumer-input bands into the state."""
