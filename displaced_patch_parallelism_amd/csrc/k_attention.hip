@@ -9,8 +9,8 @@
 //   K[n] = k_patch[n - r0*W] for n in the band, k_stale[n] elsewhere (same for V).
 //
 // bf16 path (d = 64): flash-style single pass with an online softmax in the
-// base-2 domain (log2(e) folded into the scale).  A workgroup holds 128
-// queries (4 waves x 32); K/V tiles of 64 tokens are staged in LDS, K
+// base-2 domain (log2(e) folded into the scale).  A workgroup holds 256
+// queries (8 waves x 32); K/V tiles of 64 tokens are staged in LDS, K
 // row-major and V transposed.  Each wave computes S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16 so that lane l owns query l%32: the running max
 // and sum stay in the lane (one cross-half exchange per tile for the max).
@@ -46,6 +46,7 @@ struct AttnArgs {
     float2* part_ml;   // [split][B*heads][Nq] (max, sum)
     int B, heads, C, Nq, N, band0;
     int kv_tiles, kvsplit;
+    int qtiles;        // query tiles per (batch, head)
     float sc;          // scale * log2(e)
 };
 
@@ -106,11 +107,19 @@ __global__ __launch_bounds__(64 * WAVES) void attn_bf16_d64_kernel(AttnArgs a) {
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int hsel = lane >> 5;
-    const int bh = blockIdx.y;
+    // Workgroups are dispatched round-robin over the 8 XCDs (workgroup w on XCD w % 8).  Give
+    // XCD x a contiguous run of the order (head, key split, query tile), query tile fastest:
+    // the workgroups resident on an XCD then stream the same keys and values through its L2.
+    const int total = gridDim.x;
+    const int xcd = blockIdx.x & 7, within = blockIdx.x >> 3;
+    const int lt = xcd * (total >> 3) + (xcd < (total & 7) ? xcd : (total & 7)) + within;
+    const int qt = lt % a.qtiles;
+    const int rest = lt / a.qtiles;
+    const int split = rest % a.kvsplit;
+    const int bh = rest / a.kvsplit;
     const int b = bh / a.heads;
     const int e = bh - b * a.heads;
-    const int split = blockIdx.z;
-    const int myq = blockIdx.x * QTW + wave * 32 + (lane & 31);
+    const int myq = qt * QTW + wave * 32 + (lane & 31);
     const bool qvalid = myq < a.Nq;
     const int col0 = e * D;
 
@@ -304,7 +313,10 @@ __global__ __launch_bounds__(64 * WAVES) void attn_bf16_d64_kernel(AttnArgs a) {
     }
 }
 
-// Merge of key-split partials, in split order.  One thread per (b*heads, query, 4 dims).
+// Merge of key-split partials, in split order.  One thread per (b*heads, query, 4 dims); all
+// of a thread's partial loads are issued before any is used (kvsplit <= kMaxSplit).
+constexpr int kMaxSplit = 16;
+
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ part_o,
                                                          const float2* __restrict__ part_ml,
                                                          uint16_t* __restrict__ o, int B, int heads, int C,
@@ -316,19 +328,31 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
     const int64_t row = idx / (D / 4);  // (bh, q)
     const int q = (int)(row % Nq);
     const int bh = (int)(row / Nq);
+    float2 ml[kMaxSplit];
+    float4 v[kMaxSplit];
+#pragma unroll
+    for (int s = 0; s < kMaxSplit; ++s) {
+        if (s < kvsplit) {
+            ml[s] = part_ml[(int64_t)s * rows + row];
+            v[s] = *(const float4*)(part_o + ((int64_t)s * rows + row) * D + d4 * 4);
+        }
+    }
     float M = kNegBig;
-    for (int s = 0; s < kvsplit; ++s) M = fmaxf(M, part_ml[(int64_t)s * rows + row].x);
+#pragma unroll
+    for (int s = 0; s < kMaxSplit; ++s)
+        if (s < kvsplit) M = fmaxf(M, ml[s].x);
     float L = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < kvsplit; ++s) {
-        const float2 ml = part_ml[(int64_t)s * rows + row];
-        const float w = __builtin_amdgcn_exp2f(ml.x - M);
-        L = fmaf(ml.y, w, L);
-        const float4 v = *(const float4*)(part_o + ((int64_t)s * rows + row) * D + d4 * 4);
-        acc.x = fmaf(v.x, w, acc.x);
-        acc.y = fmaf(v.y, w, acc.y);
-        acc.z = fmaf(v.z, w, acc.z);
-        acc.w = fmaf(v.w, w, acc.w);
+#pragma unroll
+    for (int s = 0; s < kMaxSplit; ++s) {
+        if (s < kvsplit) {
+            const float w = __builtin_amdgcn_exp2f(ml[s].x - M);
+            L = fmaf(ml[s].y, w, L);
+            acc.x = fmaf(v[s].x, w, acc.x);
+            acc.y = fmaf(v[s].y, w, acc.y);
+            acc.z = fmaf(v[s].z, w, acc.z);
+            acc.w = fmaf(v[s].w, w, acc.w);
+        }
     }
     const float inv = 1.0f / L;
     const int b = bh / heads, e = bh - (bh / heads) * heads;
@@ -396,18 +420,21 @@ AttnPlan plan_attention(const Geom& g, int heads, int head_dim, bool bf16) {
     }
     p.kind = 1;
     const int64_t Nq = g.band_tokens();
-    // 8 waves (256 queries) share each K/V tile when the band is large; 4 waves otherwise
-    p.qtile = Nq >= 2048 ? 256 : 128;
+    // 8 waves (256 queries) share each K/V tile.  A wave's tile loop is a serial chain (S
+    // MFMAs, max, exponentials, P.V MFMAs), so throughput needs several waves per SIMD; the
+    // 64 KB ring allows two workgroups per CU, i.e. four waves per SIMD.  Measured on
+    // the small bands too (1024 and 128 queries), 8-wave tiles beat 4-wave ones.
+    p.qtile = 256;
     p.qtiles = (int)((Nq + p.qtile - 1) / p.qtile);
     const int kv_tiles = (int)((g.map_tokens() + KT - 1) / KT);
     const int64_t units = (int64_t)p.qtiles * g.B * heads;
-    // Resident workgroups (register-limited): 2 of 4 waves or 1 of 8 waves per CU, 256 CUs.
-    // Pick the key split that fills whole rounds of workgroups best (>= 2 key tiles per
-    // split), preferring fewer splits.
-    const int64_t slots = p.qtile == 256 ? 256 : 512;
+    // Pick the key split that fills whole rounds of 256 workgroups best (>= 2 key tiles per
+    // split), preferring fewer splits: fewer, longer workgroups pay the pipeline fill, the
+    // partial write and the merge less often.
+    const int64_t slots = 256;
     int ks = 1;
     double best = 0.0;
-    for (int k = 1; k <= 16; ++k) {
+    for (int k = 1; k <= kMaxSplit; ++k) {
         if (k > 1 && kv_tiles / k < 2) break;
         const int64_t wgs = units * k;
         const int64_t rounds = (wgs + slots - 1) / slots;
@@ -468,11 +495,9 @@ hipError_t launch_attention(const Geom& g, const AttnPlan& plan, bool bf16, int 
     a.kv_tiles = (N + KT - 1) / KT;
     a.kvsplit = plan.kvsplit;
     a.sc = scale * kLog2e;
-    dim3 grid((unsigned)plan.qtiles, (unsigned)(g.B * heads), (unsigned)plan.kvsplit);
-    if (plan.qtile == 256)
-        attn_bf16_d64_kernel<kStages, 8><<<grid, 512, 0, stream>>>(a);
-    else
-        attn_bf16_d64_kernel<kStages, 4><<<grid, 256, 0, stream>>>(a);
+    a.qtiles = plan.qtiles;
+    const unsigned grid = (unsigned)((int64_t)plan.qtiles * g.B * heads * plan.kvsplit);
+    attn_bf16_d64_kernel<kStages, 8><<<grid, 512, 0, stream>>>(a);
     if (plan.kvsplit > 1) {
         const int64_t threads = (int64_t)g.B * heads * Nq * (D / 4);
         attn_merge_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(
