@@ -160,6 +160,35 @@ class DisplacedLayer:
                 self.step(x_patch, i, gn_mode, update_state)
         return graph
 
+    def step_all(self, x_full, gn_mode="corrected") -> List[torch.Tensor]:
+        """Every patch's displaced step of one denoising step; returns each graph step's
+        full-map output.
+
+        Every patch reads the state the previous step left (the stale context is the
+        previous step's for all patches alike); the fresh bands and moments are gathered
+        into a second set of buffers and become the state only after the last patch --
+        on one GPU this stands for the exchange that refreshes every device's context.
+        ``gn_mode`` "corrected", "local" or "stale" selects the GroupNorm statistics.
+        """
+        c = self.cfg
+        full = (c.B, c.H, c.W, c.C)
+        outs_full = [torch.empty(full, dtype=self.dt, device=self.device) for _ in c.graph]
+        has_gn = any(s in ("gn", "gn_silu") for s in c.graph)
+        next_table = torch.empty_like(self.table)
+        for i in range(c.P):
+            p = self.patch(i)
+            outs = self.step(self.band(x_full, i), i, gn_mode, update_state=False)
+            for k, o in enumerate(outs):
+                dp_stale_update(p, o, outs_full[k])
+            if has_gn:
+                dp_stats_update(c.P, i, self.fresh_stats, next_table)
+        if has_gn:
+            self.table.copy_(next_table)
+        inputs = [x_full] + outs_full[:-1]
+        for k, m in self.maps.items():
+            m.copy_(inputs[k])
+        return outs_full
+
     def splice_state(self, i, x_patch, outs, events=None):
         """Write patch i's fresh statistics and consumer-input bands into the state."""
         c = self.cfg

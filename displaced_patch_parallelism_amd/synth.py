@@ -82,6 +82,30 @@ def layer_inputs(cfg, seed: int, perturb: float = PERTURB) -> LayerInputs:
 
 
 @dataclass
+class Trajectory:
+    """Inputs of one layer over several denoising steps (see ``trajectory``)."""
+    xs: List[np.ndarray]     # steps + 1 maps [B][H][W][C]: xs[0] feeds the warm-up step
+    convs: List[Tuple[np.ndarray, np.ndarray]]
+
+
+def trajectory(cfg, seed: int, steps: int, perturb: float = PERTURB) -> Trajectory:
+    """A slowly drifting layer input: x_0 ~ N(0,1), x_t = x_{t-1} + 0.05*N(0,1).
+
+    Draw order: x_0, then each step's perturbation, then each conv's w and b.
+    Accumulated in float32 and rounded to the storage type per step.
+    """
+    rng = np.random.default_rng(seed)
+    shape = (cfg.B, cfg.H, cfg.W, cfg.C)
+    x = rng.standard_normal(shape, dtype=np.float32)
+    xs = [to_storage(x, cfg.dtype)]
+    for _ in range(steps):
+        x = x + np.float32(perturb) * rng.standard_normal(shape, dtype=np.float32)
+        xs.append(to_storage(x, cfg.dtype))
+    convs = [conv_params(rng, cfg.C, cfg.C, cfg.dtype) for s in cfg.graph if s == "conv"]
+    return Trajectory(xs, convs)
+
+
+@dataclass
 class ConvCase:
     fresh: np.ndarray      # [B][H][W][Cin] current map (its band i is the patch)
     stale: np.ndarray      # [B][H][W][Cin] previous step's map

@@ -264,3 +264,33 @@ def displaced_layer(graph, params, x_patch, state, P, i, gn_mode=GN_CORRECTED):
             raise ValueError(f"unknown step {step!r}")
         outputs.append(h)
     return outputs, {"stats": new_stats, "maps": new_maps}
+
+
+def displaced_step_all(graph, params, x_full, state, P, gn_mode=GN_CORRECTED):
+    """One denoising step of a layer with every patch displaced.
+
+    study.space page, Method: each device computes only its own patch, using
+    the previous step's activations as the context of the other patches;
+    DistriFusion summary (atlas.scime.ai), Approach: the fresh activations are
+    gathered to every device and become the next step's context.  So every
+    patch i runs ``displaced_layer`` against the same previous-step ``state``,
+    and the next state holds every patch's fresh band of each conv/attention
+    input map and every patch's fresh GroupNorm moments.
+
+    Returns (outputs, next_state): outputs is every graph step's full-map
+    output [B][H][W][C] (float64, patches side by side).
+    """
+    x = np.asarray(x_full, dtype=F64)
+    B, H, W, C = x.shape
+    h = H // P
+    outputs = [np.empty((B, H, W, C), dtype=F64) for _ in graph]
+    next_stats = None if state["stats"] is None else np.array(state["stats"], dtype=F64, copy=True)
+    for i in range(P):
+        outs, new_state = displaced_layer(graph, params, x[:, i * h:(i + 1) * h], state, P, i, gn_mode)
+        for k, o in enumerate(outs):
+            outputs[k][:, i * h:(i + 1) * h] = o
+        if next_stats is not None:
+            next_stats[i] = new_state["stats"][i]
+    inputs = [x] + outputs[:-1]
+    next_maps = {k: np.array(inputs[k], copy=True) for k in state["maps"]}
+    return outputs, {"stats": next_stats, "maps": next_maps}

@@ -1,0 +1,55 @@
+"""All-patch displaced steps over a short trajectory, on the GPU against the oracle.
+
+Both sides start from the synchronous warm-up on x_0 and then run every patch's
+displaced step on x_1, x_2 against the state of the previous step (the oracle's
+``displaced_step_all``, the layer's ``step_all`` with its ping-pong state), in
+each GroupNorm mode.  Only the generator's raw inputs cross between them.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from displaced_patch_parallelism_amd import synth, trajectory
+from displaced_patch_parallelism_amd.configs import CONFIGS, LayerConfig
+from displaced_patch_parallelism_amd.layers import DisplacedLayer
+from tests.gpu_util import announce, assert_parity, gpu, host
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "c0": CONFIGS["c0"],
+    "c1-like": LayerConfig("c1s", "bf16", B=1, H=32, W=24, C=128, G=32, P=4, graph=("gn_silu", "conv")),
+    "c2-like": LayerConfig("c2s", "bf16", B=1, H=16, W=16, C=128, G=32, P=4, graph=("gn", "attn", "conv"),
+                           heads=2, head_dim=64),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("mode", ["corrected", "local", "stale"])
+def test_step_all_matches_oracle(name, mode):
+    c = CASES[name]
+    tr = synth.trajectory(c, seed=4, steps=2)
+    params = {"G": c.G, "eps": c.eps, "heads": c.heads, "convs": tr.convs}
+    layer = DisplacedLayer(c, tr.convs)
+    layer.warmup(gpu(tr.xs[0], c.dtype))
+    _, state = oracle.sync_layer(c.graph, params, tr.xs[0], c.P)
+    gn_mode = {"corrected": oracle.GN_CORRECTED, "local": oracle.GN_LOCAL, "stale": oracle.GN_STALE}[mode]
+    for t in (1, 2):
+        announce("all-patch step", name, mode, "t", t)
+        outs = layer.step_all(gpu(tr.xs[t], c.dtype), gn_mode=mode)
+        ref, state = oracle.displaced_step_all(c.graph, params, tr.xs[t], state, c.P, gn_mode)
+        for k, (g, r) in enumerate(zip(outs, ref)):
+            assert_parity(host(g), r, c.dtype, f"{name} {mode} t{t} step {k} ({c.graph[k]})")
+        assert_parity(host(layer.table), state["stats"], "f32", f"{name} {mode} t{t} statistics table")
+
+
+def test_corrected_groupnorm_drifts_least():
+    """Of the three statistics choices, the corrected one stays closest to the synchronous
+    layer (the ordering of the ablation table on the DistriFusion summary)."""
+    c = CASES["c1-like"]
+    rows = list(trajectory.run(c, steps=3, seed=1))
+    for row in rows:
+        announce("drift", row)
+        assert row["corrected"] < row["local"] and row["corrected"] < row["stale"], row

@@ -141,3 +141,47 @@ def test_all_patches_displaced_converge_to_sync():
                            for i in range(2)], axis=1)
     err = np.linalg.norm(full - sync_outs[-1]) / np.linalg.norm(sync_outs[-1])
     assert err < 0.1
+
+
+@pytest.mark.parametrize("gname", list(GRAPHS))
+def test_step_all_with_current_state_is_sync(gname):
+    """All patches displaced against the current step's own (synchronous) state give the
+    synchronous layer, and the next state they leave is that state again."""
+    cfg = small_cfg(GRAPHS[gname])
+    inp = synth.layer_inputs(cfg, seed=11)
+    params = params_of(cfg, inp)
+    sync_outs, state = oracle.sync_layer(cfg.graph, params, inp.x, cfg.P)
+    outs, nxt = oracle.displaced_step_all(cfg.graph, params, inp.x, state, cfg.P)
+    for k, (o, r) in enumerate(zip(outs, sync_outs)):
+        np.testing.assert_allclose(o, r, rtol=1e-11, atol=1e-11, err_msg=f"step {k}")
+    np.testing.assert_allclose(nxt["stats"], state["stats"], rtol=1e-12, atol=1e-12)
+    for k in state["maps"]:
+        np.testing.assert_allclose(nxt["maps"][k], state["maps"][k], rtol=1e-11, atol=1e-11)
+
+
+@pytest.mark.parametrize("gname", list(GRAPHS))
+def test_step_all_one_patch_is_plain_layer(gname):
+    """P = 1: nothing stale is ever read, whatever the state holds."""
+    cfg = small_cfg(GRAPHS[gname], P=1)
+    inp = synth.layer_inputs(cfg, seed=12)
+    params = params_of(cfg, inp)
+    _, prev = oracle.sync_layer(cfg.graph, params, inp.x_prev, cfg.P)
+    outs, _ = oracle.displaced_step_all(cfg.graph, params, inp.x, prev, cfg.P)
+    ref = torch_sync(cfg.graph, params, inp.x)
+    for k, (o, r) in enumerate(zip(outs, ref)):
+        np.testing.assert_allclose(o, r, rtol=1e-10, atol=1e-10, err_msg=f"step {k}")
+
+
+def test_step_all_next_state_is_gathered_fresh_inputs():
+    """The next state holds every band's fresh moments of the GroupNorm input and every
+    conv/attention step's full (gathered) input."""
+    cfg = small_cfg(GRAPHS["gn_silu-conv-attn"])
+    inp = synth.layer_inputs(cfg, seed=13)
+    params = params_of(cfg, inp)
+    _, prev = oracle.sync_layer(cfg.graph, params, inp.x_prev, cfg.P)
+    outs, nxt = oracle.displaced_step_all(cfg.graph, params, inp.x, prev, cfg.P)
+    np.testing.assert_allclose(nxt["stats"], oracle.band_moments(inp.x, cfg.G, cfg.P), rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(nxt["maps"][1], outs[0])
+    np.testing.assert_array_equal(nxt["maps"][2], outs[1])
+    # and it differs from the previous state (the step did advance it)
+    assert np.abs(nxt["maps"][1] - prev["maps"][1]).max() > 1e-3

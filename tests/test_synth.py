@@ -36,3 +36,19 @@ def test_distributions():
     assert w.shape == (320, 3, 3, 320) and b.dtype == np.float32
     assert abs(w.std() * np.sqrt(9 * 320) - 1) < 0.02
     assert synth.bf16_round(w).tobytes() == w.tobytes()
+
+
+def test_trajectory_is_a_small_random_walk():
+    from displaced_patch_parallelism_amd.configs import LayerConfig
+    cfg = LayerConfig("t", "f32", B=1, H=16, W=16, C=32, G=8, P=2, graph=("gn_silu", "conv"))
+    tr = synth.trajectory(cfg, seed=3, steps=4)
+    assert len(tr.xs) == 5 and len(tr.convs) == 1
+    rng = np.random.default_rng(3)
+    x0 = rng.standard_normal((1, 16, 16, 32), dtype=np.float32)
+    np.testing.assert_array_equal(tr.xs[0], x0)
+    for a, b in zip(tr.xs[:-1], tr.xs[1:]):
+        d = (b - a).ravel()
+        assert abs(d.std() - 0.05) < 0.005 and abs(d.mean()) < 0.005
+    again = synth.trajectory(cfg, seed=3, steps=4)
+    for a, b in zip(tr.xs, again.xs):
+        np.testing.assert_array_equal(a, b)
