@@ -52,7 +52,11 @@ class LayerConfig:
 
     @property
     def has_attn(self) -> bool:
-        return "attn" in self.graph
+        return "attn" in self.graph or "attn_proj" in self.graph
+
+    @property
+    def has_proj(self) -> bool:
+        return "attn_proj" in self.graph
 
     @property
     def has_conv(self) -> bool:
@@ -69,6 +73,12 @@ class LayerConfig:
         if not self.has_attn:
             return 0.0
         return 4.0 * self.B * self.heads * self.Nq * self.N * self.head_dim
+
+    def proj_flops(self) -> float:
+        """The four C x C projections (Q, K, V, O) of the patch's tokens."""
+        if not self.has_proj:
+            return 0.0
+        return 4 * 2.0 * self.B * self.Nq * self.C * self.C
 
     def band_bytes(self) -> int:
         """Bytes of one activation band [B][h][W][C]."""
@@ -100,4 +110,14 @@ CONFIGS = {
         "c4b", "bf16", B=1, H=240, W=240, C=640, G=32, P=8,
         graph=("gn", "attn"), heads=10, head_dim=64,
         note="3840px attention layer: GN, 10x64 attention, 7200 queries over 57600 keys"),
+    # The two attention layers again with learned Q/K/V/O projections: the stale context is
+    # the previous step's projected K and V maps.
+    "c2p": LayerConfig(
+        "c2p", "bf16", B=1, H=64, W=64, C=640, G=32, P=4,
+        graph=("gn", "attn_proj", "conv"), heads=10, head_dim=64,
+        note="c2 with Q/K/V/O projections 640->640 and a projected K/V cache"),
+    "c4bp": LayerConfig(
+        "c4bp", "bf16", B=1, H=240, W=240, C=640, G=32, P=8,
+        graph=("gn", "attn_proj"), heads=10, head_dim=64,
+        note="c4b with Q/K/V/O projections 640->640 and a projected K/V cache"),
 }

@@ -11,7 +11,8 @@ Conventions
 -----------
 * Generator: ``numpy.random.default_rng(seed)`` (PCG64), drawing in float32.
 * Draw order for a layer: fresh map ``x``, perturbation ``eps``, then for each
-  conv of the graph its weights and its bias.
+  conv of the graph its weights and its bias, then for each projected
+  attention step its Q, K, V and O weights and biases (N(0, 1/C)).
 * Weights ``[Cout][3][3][Cin]`` and bias ``[Cout]`` are N(0, 1/fan_in) with
   fan_in = 9*Cin.  The bias stays float32; weights are rounded to the
   activation storage type.
@@ -61,12 +62,24 @@ def map_pair(rng: np.random.Generator, shape, dtype: str) -> Tuple[np.ndarray, n
     return to_storage(fresh, dtype), to_storage(stale, dtype)
 
 
+def proj_params(rng: np.random.Generator, C: int, dtype: str) -> Tuple[np.ndarray, ...]:
+    """(wq, bq, wk, bk, wv, bv, wo, bo): weights [C][C] and biases [C], N(0, 1/C)."""
+    std = np.float32(1.0 / np.sqrt(C))
+    out = []
+    for _ in range(4):
+        w = rng.standard_normal((C, C), dtype=np.float32) * std
+        b = rng.standard_normal((C,), dtype=np.float32) * std
+        out += [to_storage(w, dtype), b.astype(np.float32)]
+    return tuple(out)
+
+
 @dataclass
 class LayerInputs:
     """Raw inputs of one layer: current-step input, previous-step input, weights."""
     x: np.ndarray            # [B][H][W][C] fresh (current step) layer input
     x_prev: np.ndarray       # [B][H][W][C] previous step's layer input
     convs: List[Tuple[np.ndarray, np.ndarray]]
+    projs: List[Tuple[np.ndarray, ...]] = None   # per attn_proj step: (wq, bq, wk, bk, wv, bv, wo, bo)
 
 
 def layer_inputs(cfg, seed: int, perturb: float = PERTURB) -> LayerInputs:
@@ -78,7 +91,8 @@ def layer_inputs(cfg, seed: int, perturb: float = PERTURB) -> LayerInputs:
     x_prev = x + np.float32(perturb) * eps
     convs = [conv_params(rng, cfg.C, cfg.C, cfg.dtype)
              for s in cfg.graph if s == "conv"]
-    return LayerInputs(to_storage(x, cfg.dtype), to_storage(x_prev, cfg.dtype), convs)
+    projs = [proj_params(rng, cfg.C, cfg.dtype) for s in cfg.graph if s == "attn_proj"]
+    return LayerInputs(to_storage(x, cfg.dtype), to_storage(x_prev, cfg.dtype), convs, projs)
 
 
 @dataclass
@@ -86,6 +100,7 @@ class Trajectory:
     """Inputs of one layer over several denoising steps (see ``trajectory``)."""
     xs: List[np.ndarray]     # steps + 1 maps [B][H][W][C]: xs[0] feeds the warm-up step
     convs: List[Tuple[np.ndarray, np.ndarray]]
+    projs: List[Tuple[np.ndarray, ...]] = None
 
 
 def trajectory(cfg, seed: int, steps: int, perturb: float = PERTURB) -> Trajectory:
@@ -102,7 +117,8 @@ def trajectory(cfg, seed: int, steps: int, perturb: float = PERTURB) -> Trajecto
         x = x + np.float32(perturb) * rng.standard_normal(shape, dtype=np.float32)
         xs.append(to_storage(x, cfg.dtype))
     convs = [conv_params(rng, cfg.C, cfg.C, cfg.dtype) for s in cfg.graph if s == "conv"]
-    return Trajectory(xs, convs)
+    projs = [proj_params(rng, cfg.C, cfg.dtype) for s in cfg.graph if s == "attn_proj"]
+    return Trajectory(xs, convs, projs)
 
 
 @dataclass

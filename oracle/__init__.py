@@ -18,13 +18,14 @@ float64), brute-force loops on tiny maps, and the invariants the method fixes
 (stale == fresh gives the synchronous layer, one patch gives the plain layer).
 """
 
-from .displaced import (GN_CORRECTED, GN_LOCAL, GN_STALE, attention_splice, band,
+from .displaced import (GN_CORRECTED, GN_LOCAL, GN_STALE, attention_proj_splice, attention_splice, band,
                         conv3x3_halo, displaced_layer, displaced_step_all, gn_async, gn_band_stats,
-                        gn_moments, silu, splice, splice_tokens, stale_update)
-from .sync import band_moments, conv3x3, group_norm, self_attention, sync_layer
+                        gn_moments, linear, silu, splice, splice_tokens, stale_update)
+from .sync import attention, band_moments, conv3x3, group_norm, project, self_attention, sync_layer
 
 __all__ = [
-    "GN_CORRECTED", "GN_LOCAL", "GN_STALE", "attention_splice", "band", "conv3x3_halo",
+    "GN_CORRECTED", "GN_LOCAL", "GN_STALE", "attention_proj_splice", "attention_splice", "linear",
+    "attention", "project", "band", "conv3x3_halo",
     "displaced_layer", "displaced_step_all", "gn_async", "gn_band_stats", "gn_moments", "silu", "splice",
     "splice_tokens", "stale_update", "band_moments", "conv3x3", "group_norm",
     "self_attention", "sync_layer",

@@ -205,6 +205,37 @@ def attention_splice(q_patch, k_patch, v_patch, k_stale, v_stale, H, W, P, i,
 
 
 # --------------------------------------------------------------------------
+# Learned projections of an attention layer
+# --------------------------------------------------------------------------
+
+def linear(x, w, bias=None):
+    """y = x W^T + bias over the last axis: x [..][K], w [N][K], bias [N] (or None)."""
+    y = np.asarray(x, dtype=F64) @ np.asarray(w, dtype=F64).T
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=F64)
+    return y
+
+
+def attention_proj_splice(h_tokens, proj, k_stale, v_stale, H, W, P, i, heads, scale=None):
+    """Attention layer with learned projections for patch i.
+
+    The fresh patch's queries, keys and values are its projections
+    (Q, K, V = h W_q^T + b_q, ...); every device keeps the full K and V maps of
+    the layer from the previous step (PipeFusion explainer on gist.science,
+    Problem Statement and Memory Efficiency), so the stale context of the other
+    bands is those cached projections, and the fresh K and V replace band i.
+    The output is the attention projected by W_o.  Returns (O, K, V) with O
+    [B][Nq][C] and the fresh K, V [B][Nq][C] that refresh the cache.
+    """
+    wq, bq, wk, bk, wv, bv, wo, bo = proj
+    q = linear(h_tokens, wq, bq)
+    k = linear(h_tokens, wk, bk)
+    v = linear(h_tokens, wv, bv)
+    a = attention_splice(q, k, v, k_stale, v_stale, H, W, P, i, heads, scale)
+    return linear(a, wo, bo), k, v
+
+
+# --------------------------------------------------------------------------
 # Splice of the fresh band into the resident stale buffer
 # --------------------------------------------------------------------------
 
@@ -225,12 +256,14 @@ def stale_update(stale, x_patch, P, i):
 def displaced_layer(graph, params, x_patch, state, P, i, gn_mode=GN_CORRECTED):
     """Run patch i of a layer graph against the previous step's state.
 
-    graph: sequence of "gn", "gn_silu", "conv", "attn".
+    graph: sequence of "gn", "gn_silu", "conv", "attn", "attn_proj".
     params: dict with G, eps, heads, scale (optional), gamma/beta (optional),
-            convs: list of (w, bias) in graph order.
+            convs: list of (w, bias) in graph order, projs: list of
+            (wq, bq, wk, bk, wv, bv, wo, bo) for the attn_proj steps in order.
     state: dict with "stats" [P][B][G][2] (GroupNorm moments per band of the
            previous step) and "maps": {step index: [B][H][W][C] stale input map
-           of that conv or attention step}.
+           of that conv or attention step; (step index, "k") / (step index, "v"):
+           the previous step's projected K / V maps of an attn_proj step}.
     Returns (outputs, new_state): outputs is the list of every step's patch
     output (float64); new_state is the state with patch i's band and
     statistics spliced in.
@@ -242,12 +275,22 @@ def displaced_layer(graph, params, x_patch, state, P, i, gn_mode=GN_CORRECTED):
     new_stats = np.array(state["stats"], dtype=F64, copy=True)
     new_maps = {k: np.array(v, dtype=F64, copy=True) for k, v in state["maps"].items()}
     conv_iter = iter(params.get("convs", []))
+    proj_iter = iter(params.get("projs", []))
     for k, step in enumerate(graph):
         if step in ("gn", "gn_silu"):
             h, fresh = gn_async(h, state["stats"], P, i, params["G"], params.get("eps", 1e-5),
                                 gn_mode, params.get("gamma"), params.get("beta"),
                                 "silu" if step == "gn_silu" else None)
             new_stats[i] = fresh
+        elif step == "attn_proj":
+            tok = h.reshape(B, hb * W, C)
+            ks_ = np.asarray(state["maps"][(k, "k")], dtype=F64).reshape(B, H * W, C)
+            vs_ = np.asarray(state["maps"][(k, "v")], dtype=F64).reshape(B, H * W, C)
+            out, kf, vf = attention_proj_splice(tok, next(proj_iter), ks_, vs_, H, W, P, i,
+                                                params["heads"], params.get("scale"))
+            new_maps[(k, "k")] = stale_update(new_maps[(k, "k")], kf.reshape(B, hb, W, C), P, i)
+            new_maps[(k, "v")] = stale_update(new_maps[(k, "v")], vf.reshape(B, hb, W, C), P, i)
+            h = out.reshape(B, hb, W, C)
         elif step == "conv":
             w, bias = next(conv_iter)
             out = conv3x3_halo(h, state["maps"][k], w, bias, P, i)
@@ -292,5 +335,13 @@ def displaced_step_all(graph, params, x_full, state, P, gn_mode=GN_CORRECTED):
         if next_stats is not None:
             next_stats[i] = new_state["stats"][i]
     inputs = [x] + outputs[:-1]
-    next_maps = {k: np.array(inputs[k], copy=True) for k in state["maps"]}
+    next_maps = {}
+    proj_iter = iter(params.get("projs", []))
+    for k, step in enumerate(graph):
+        if step in ("conv", "attn"):
+            next_maps[k] = np.array(inputs[k], copy=True)
+        elif step == "attn_proj":
+            wq, bq, wk, bk, wv, bv, wo, bo = next(proj_iter)
+            next_maps[(k, "k")] = linear(inputs[k], wk, bk)
+            next_maps[(k, "v")] = linear(inputs[k], wv, bv)
     return outputs, {"stats": next_stats, "maps": next_maps}

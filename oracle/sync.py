@@ -85,18 +85,54 @@ def self_attention(x, heads, scale=None, chunk=512):
     return out.reshape(B, H, W, C)
 
 
+def attention(q, k, v, heads, scale=None, chunk=512):
+    """softmax(scale * Q K^T) V per head over full maps [B][H][W][C] (no splice)."""
+    q, k, v = (np.asarray(a, dtype=F64) for a in (q, k, v))
+    B, H, W, C = q.shape
+    tq, tk, tv = (a.reshape(B, H * W, C) for a in (q, k, v))
+    d = C // heads
+    if scale is None or scale <= 0:
+        scale = d ** -0.5
+    out = np.empty_like(tq)
+    for b in range(B):
+        for e in range(heads):
+            sl = slice(e * d, (e + 1) * d)
+            for s in range(0, H * W, chunk):
+                S = scale * (tq[b, s:s + chunk, sl] @ tk[b, :, sl].T)
+                S = S - S.max(axis=1, keepdims=True)
+                E = np.exp(S)
+                out[b, s:s + chunk, sl] = (E / E.sum(axis=1, keepdims=True)) @ tv[b, :, sl]
+    return out.reshape(B, H, W, C)
+
+
+def project(x, w, bias):
+    """x W^T + bias over the channel axis of a map."""
+    y = np.asarray(x, dtype=F64) @ np.asarray(w, dtype=F64).T
+    return y + np.asarray(bias, dtype=F64) if bias is not None else y
+
+
 def sync_layer(graph, params, x, P):
     """Run the layer on the full map; returns (outputs, state) for the next step.
 
     outputs: every step's full-map output.  state: "stats" = per-band moments
     of the GroupNorm input, "maps" = {step index: full input map of that conv
-    or attention step}.
+    or attention step; (step index, "k"/"v"): the projected K / V maps of an
+    attn_proj step}.
     """
     h = np.asarray(x, dtype=F64)
     outputs = []
     state = {"stats": None, "maps": {}}
     conv_iter = iter(params.get("convs", []))
+    proj_iter = iter(params.get("projs", []))
     for k, step in enumerate(graph):
+        if step == "attn_proj":
+            wq, bq, wk, bk, wv, bv, wo, bo = next(proj_iter)
+            q, kk, vv = project(h, wq, bq), project(h, wk, bk), project(h, wv, bv)
+            state["maps"][(k, "k")] = kk
+            state["maps"][(k, "v")] = vv
+            h = project(attention(q, kk, vv, params["heads"], params.get("scale")), wo, bo)
+            outputs.append(h)
+            continue
         if step in ("gn", "gn_silu"):
             state["stats"] = band_moments(h, params["G"], P)
             h = group_norm(h, params["G"], params.get("eps", 1e-5), params.get("gamma"),

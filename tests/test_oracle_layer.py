@@ -24,6 +24,8 @@ GRAPHS = {
     "gn-attn-conv": ("gn", "attn", "conv"),
     "gn_silu-conv": ("gn_silu", "conv"),
     "gn-attn": ("gn", "attn"),
+    "gn-attn_proj-conv": ("gn", "attn_proj", "conv"),
+    "gn-attn_proj": ("gn", "attn_proj"),
 }
 
 
@@ -33,15 +35,23 @@ def small_cfg(graph, H=8, W=6, C=8, G=4, P=4, heads=2):
 
 
 def params_of(cfg, inp):
-    return {"G": cfg.G, "eps": cfg.eps, "heads": cfg.heads, "convs": inp.convs}
+    return {"G": cfg.G, "eps": cfg.eps, "heads": cfg.heads, "convs": inp.convs, "projs": inp.projs}
 
 
 def torch_sync(graph, params, x):
     h = t64(x)
     outs = []
     convs = iter(params["convs"])
+    projs = iter(params.get("projs") or [])
     for step in graph:
-        if step.startswith("gn"):
+        if step == "attn_proj":
+            wq, bq, wk, bk, wv, bv, wo, bo = (t64(a) for a in next(projs))
+            B, H, W, C = h.shape
+            tok = h.reshape(B, H * W, C)
+            lin = torch.nn.functional.linear
+            a = sdpa_tokens(lin(tok, wq, bq), lin(tok, wk, bk), lin(tok, wv, bv), params["heads"])
+            h = lin(a, wo, bo).reshape(B, H, W, C)
+        elif step.startswith("gn"):
             h = group_norm_nhwc(h, params["G"], params["eps"])
             if step == "gn_silu":
                 h = torch.nn.functional.silu(h)
@@ -79,7 +89,9 @@ def test_sync_layer_matches_torch(gname):
         np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
     # the state holds every band's moments and each consumer's full input map
     assert state["stats"].shape == (cfg.P, 1, cfg.G, 2)
-    assert set(state["maps"]) == {k for k, s in enumerate(cfg.graph) if s in ("conv", "attn")}
+    expected = {k for k, s in enumerate(cfg.graph) if s in ("conv", "attn")}
+    expected |= {(k, kv) for k, s in enumerate(cfg.graph) if s == "attn_proj" for kv in ("k", "v")}
+    assert set(state["maps"]) == expected
 
 
 @pytest.mark.parametrize("gname", list(GRAPHS))
@@ -185,3 +197,43 @@ def test_step_all_next_state_is_gathered_fresh_inputs():
     np.testing.assert_array_equal(nxt["maps"][2], outs[1])
     # and it differs from the previous state (the step did advance it)
     assert np.abs(nxt["maps"][1] - prev["maps"][1]).max() > 1e-3
+
+
+
+def test_linear_brute_force():
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((2, 3, 5))
+    w = rng.standard_normal((4, 5))
+    b = rng.standard_normal(4)
+    y = oracle.linear(x, w, b)
+    for i in range(2):
+        for j in range(3):
+            for n in range(4):
+                ref = b[n]
+                for k in range(5):
+                    ref += x[i, j, k] * w[n, k]
+                assert abs(y[i, j, n] - ref) < 1e-12
+    np.testing.assert_array_equal(oracle.linear(x, w), oracle.linear(x, w, np.zeros(4)))
+
+
+@pytest.mark.parametrize("P,i", [(4, 1), (2, 0)])
+def test_identity_projections_reduce_to_plain_attention(P, i):
+    """W = I, b = 0 for Q, K, V and O: the projected step is the unprojected one, and the
+    K and V it caches are the input map itself."""
+    cfg = small_cfg(("gn", "attn"), P=P)
+    inp = synth.layer_inputs(cfg, seed=22)
+    eye, zero = np.eye(cfg.C), np.zeros(cfg.C)
+    params = params_of(cfg, inp)
+    pparams = dict(params, projs=[(eye, zero) * 4])
+    pgraph = ("gn", "attn_proj")
+    _, prev = oracle.sync_layer(cfg.graph, params, inp.x_prev, P)
+    _, pprev = oracle.sync_layer(pgraph, pparams, inp.x_prev, P)
+    np.testing.assert_allclose(pprev["maps"][(1, "k")], prev["maps"][1], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(pprev["maps"][(1, "v")], prev["maps"][1], rtol=0, atol=1e-15)
+    h = cfg.h
+    xb = inp.x[:, i * h:(i + 1) * h]
+    outs, st = oracle.displaced_layer(cfg.graph, params, xb, prev, P, i)
+    pouts, pst = oracle.displaced_layer(pgraph, pparams, xb, pprev, P, i)
+    for a, b in zip(pouts, outs):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(pst["maps"][(1, "k")], st["maps"][1], rtol=0, atol=1e-12)
