@@ -73,6 +73,7 @@ def lib():
             "dp_attention_splice_ws": [pp, i32, i32, i32, psz],
             "dp_attention_splice": [pp, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "dp_stale_update": [pp, i32, vp, vp, vp],
+            "dp_linear": [i32, i32, i32, i32, vp, ctypes.c_int64, vp, vp, vp, ctypes.c_int64, vp],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -252,6 +253,44 @@ def dp_attention_splice(patch: Patch, heads, q_patch, k_patch, v_patch, k_stale,
                                      k_patch.data_ptr(), v_patch.data_ptr(), k_stale.data_ptr(),
                                      v_stale.data_ptr(), o_patch.data_ptr(), wptr, wbytes, _stream(dev)))
     return o_patch
+
+
+def dp_linear(x, w, bias=None, y=None):
+    """y = x W^T + bias over the last axis.  x: [..., K] whose rows may be strided (the last axis
+    contiguous, the leading axes collapsible to one row stride), w: [N][K] contiguous, bias: [N]
+    float32 or None; y: [..., N] with the same row structure, allocated if None."""
+    torch = _torch()
+    dt = _dtype_code(x)
+    dev = x.device
+    N, K = int(w.shape[0]), int(w.shape[1])
+    if x.shape[-1] != K:
+        raise ValueError(f"x has {x.shape[-1]} columns, w expects {K}")
+    _ptr(w, "w", (N, K), x.dtype, dev)
+    _ptr(bias, "bias", (N,), torch.float32, dev)
+    if y is None:
+        y = torch.empty(tuple(x.shape[:-1]) + (N,), dtype=x.dtype, device=dev)
+
+    def rows(t, name, width):
+        if t.dim() < 1 or t.shape[-1] != width or (t.numel() and t.stride(-1) != 1):
+            raise ValueError(f"{name} must end in a contiguous axis of {width}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        m = 1
+        for d in t.shape[:-1]:
+            m *= int(d)
+        flat = t.reshape(m, width) if m else t
+        if m and flat.data_ptr() != t.data_ptr():
+            raise ValueError(f"{name} rows are not one strided sequence")
+        ld = flat.stride(0) if m > 1 else width
+        return m, ld
+
+    M, ldx = rows(x, "x", K)
+    My, ldy = rows(y, "y", N)
+    if My != M:
+        raise ValueError(f"y has {My} rows, x has {M}")
+    _check(lib().dp_linear(dt, M, N, K, x.data_ptr(), ldx, w.data_ptr(),
+                           None if bias is None else bias.data_ptr(), y.data_ptr(), ldy, _stream(dev)))
+    return y
 
 
 def version():

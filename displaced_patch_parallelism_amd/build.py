@@ -28,7 +28,7 @@ COMMON = [
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
-SOURCES = ["dp_api.cpp", "k_splice.hip", "k_groupnorm.hip", "k_conv.hip", "k_attention.hip"]
+SOURCES = ["dp_api.cpp", "k_splice.hip", "k_groupnorm.hip", "k_conv.hip", "k_attention.hip", "k_linear.hip"]
 
 
 def hipcc():

@@ -284,4 +284,30 @@ dp_status dp_attention_splice(const dp_patch* p, dp_dtype dtype, int32_t heads, 
                       "dp_attention_splice launch");
 }
 
+dp_status dp_linear(dp_dtype dtype, int32_t M, int32_t N, int32_t K, const void* x, int64_t ldx, const void* w,
+                    const float* bias, void* y, int64_t ldy, hipStream_t stream) {
+    if (dtype != DP_F32 && dtype != DP_BF16) return fail(DP_ERR_ARG, "unknown dtype %d", (int)dtype);
+    if (M < 0 || N < 1 || K < 1) return fail(DP_ERR_ARG, "need M >= 0, N >= 1, K >= 1 (got %d, %d, %d)", M, N, K);
+    if (ldx < K || ldy < N) return fail(DP_ERR_ARG, "row strides must cover a row (ldx=%lld K=%d ldy=%lld N=%d)",
+                                        (long long)ldx, K, (long long)ldy, N);
+    if ((int64_t)M * ldx > ((int64_t)1 << 40) || (int64_t)M * ldy > ((int64_t)1 << 40))
+        return fail(DP_ERR_ARG, "matrix too large");
+    if (dtype == DP_BF16 && (K % 64 != 0 || N % 8 != 0 || ldx % 8 != 0 || ldy % 8 != 0))
+        return fail(DP_ERR_UNSUPPORTED, "bf16 linear needs K %% 64 == 0 and N, ldx, ldy multiples of 8 "
+                    "(K=%d N=%d ldx=%lld ldy=%lld)", K, N, (long long)ldx, (long long)ldy);
+    if (M == 0) return ok();   // nothing to compute; x and y may be NULL
+    DP_NEED(x, "x");
+    DP_NEED(w, "w");
+    DP_OPT(bias, "bias");
+    DP_NEED(y, "y");
+    const size_t es = elem_size(dtype);
+    const size_t xb = M ? ((size_t)(M - 1) * ldx + K) * es : 0;
+    const size_t yb = M ? ((size_t)(M - 1) * ldy + N) * es : 0;
+    const size_t wb = (size_t)N * K * es;
+    if (overlaps(y, yb, x, xb) || overlaps(y, yb, w, wb) || overlaps(y, yb, bias, bias ? (size_t)N * 4 : 0))
+        return fail(DP_ERR_ARG, "y overlaps an input");
+    return hip_status(dp::launch_linear(dtype == DP_BF16, M, N, K, x, ldx, w, bias, y, ldy, stream),
+                      "dp_linear launch");
+}
+
 }  // extern "C"

@@ -69,4 +69,8 @@ hipError_t launch_attention(const Geom& g, const AttnPlan& plan, bool bf16, int 
                             const void* k_stale, const void* v_stale, void* o, void* ws,
                             hipStream_t stream);
 
+// ---- learned projections: y = x W^T + bias ----------------------------------
+hipError_t launch_linear(bool bf16, int M, int N, int K, const void* x, int64_t ldx, const void* w,
+                         const float* bias, void* y, int64_t ldy, hipStream_t stream);
+
 }  // namespace dp

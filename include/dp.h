@@ -17,6 +17,8 @@
  *                        values from the full stale map with the patch
  *                        spliced in
  *   dp_stale_update      writes the fresh patch into the resident stale map
+ *   dp_linear            y = x W^T + b, the Q/K/V/O projections of an attention
+ *                        layer whose K/V cache holds projected keys and values
  *
  * Geometry.  Maps are NHWC, batch-major: element (b, r, c, ch) of a [B][H][W][C]
  * map sits at ((b*H + r)*W + c)*C + ch.  The P patches are equal row bands:
@@ -199,6 +201,28 @@ dp_status dp_attention_splice(const dp_patch* p, dp_dtype dtype, int32_t heads, 
  * ---------------------------------------------------------------------- */
 dp_status dp_stale_update(const dp_patch* p, dp_dtype dtype, const void* x_patch, void* stale,
                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * dp_linear -- y = x W^T + bias: the learned projections of an attention layer.
+ *
+ * Source: PipeFusion explainer (gist.science), Problem Statement and Memory
+ * Efficiency: every device keeps the full spatial K and V of every layer; with
+ * learned projections those are the projected keys and values, so a patch
+ * projects its own tokens (Q, K, V = h W^T + b) and writes its fresh K and V
+ * into band i of the cached maps, then projects the attention output by W_o.
+ *
+ *   x     [M][K] dtype, row r at x + r*ldx (elements)
+ *   w     [N][K] dtype, contiguous
+ *   bias  [N] float or NULL (0)
+ *   y     [M][N] dtype, row r at y + r*ldy; must not overlap x, w or bias
+ *         (a band of a token-major map [B][H*W][C] with B == 1 is M = h*W rows
+ *         with ldy = C, so K and V can be written straight into the cache)
+ * M may be 0 (nothing is enqueued; x and y may then be NULL).  bf16: K % 64 == 0, N, ldx, ldy multiples
+ * of 8; fp32 accumulate, outputs rounded to nearest even.  f32: any K, N.
+ * No workspace.
+ * ---------------------------------------------------------------------- */
+dp_status dp_linear(dp_dtype dtype, int32_t M, int32_t N, int32_t K, const void* x, int64_t ldx, const void* w,
+                    const float* bias, void* y, int64_t ldy, hipStream_t stream);
 
 /* Description of the last error on the calling thread (empty if none). The
  * string stays valid until the thread's next dp_* call. */

@@ -148,3 +148,22 @@ def test_python_binding_refuses_cpu_tensors():
     s = torch.zeros(1, 8, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         dp.dp_stale_update(dp.Patch(1, 8, 8, 64, 4, 1), x, s)
+
+
+def call_linear(dtype=dp.DP_BF16, M=16, N=64, K=64, x=FAKE, ldx=64, w=FAKE2, bias=None, y=0x30000000, ldy=64):
+    return dp.lib().dp_linear(dtype, M, N, K, x, ldx, w, bias, y, ldy, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(K=48, ldx=48), dp.DP_ERR_UNSUPPORTED, "K % 64"),
+    (dict(N=60, ldy=60), dp.DP_ERR_UNSUPPORTED, "multiples of 8"),
+    (dict(ldx=32), dp.DP_ERR_ARG, "row strides"),
+    (dict(N=0), dp.DP_ERR_ARG, "N >= 1"),
+    (dict(x=0), dp.DP_ERR_ARG, "NULL"),
+    (dict(y=FAKE + 8), dp.DP_ERR_ARG, "aligned"),
+    (dict(y=FAKE + 512), dp.DP_ERR_ARG, "overlaps"),
+    (dict(dtype=7), dp.DP_ERR_ARG, "dtype"),
+])
+def test_linear_rejects(kw, code, msg):
+    assert call_linear(**kw) == code
+    assert msg in dp.lib().dp_last_error().decode()
