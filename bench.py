@@ -11,7 +11,8 @@ fresh GroupNorm moments), so no separate splice is needed.  The default workload
 synthetic tensors already resident in HBM; the stale state comes from a
 synchronous warm-up step run by the same library.
 
-Prints one JSON line: whole-step TFLOP/s (algorithmic conv + attention flops
+Prints one JSON line: whole-step TFLOP/s (algorithmic conv + attention (+ learned
+projection) flops
 over the wall time of K steps run as replays of a HIP graph that holds
 several consecutive steps, between two device synchronisations; the eager, host-launched step time is
 reported beside it), per-call times (a graph of back-to-back launches of each
@@ -36,7 +37,24 @@ PEAK_HBM_GBS = 8000.0
 
 # source file of each call's main kernel (for the counter file's staleness check)
 KERNEL_SOURCES = {"conv": "k_conv.hip", "attn": "k_attention.hip", "gn": "k_groupnorm.hip",
-                  "gn_silu": "k_groupnorm.hip", "stale_update": "k_splice.hip"}
+                  "gn_silu": "k_groupnorm.hip", "stale_update": "k_splice.hip", "proj_q": "k_linear.hip",
+                  "proj_k": "k_linear.hip", "proj_v": "k_linear.hip", "proj_o": "k_linear.hip"}
+PROJ_CALLS = ("proj_q", "proj_k", "proj_v", "proj_o")
+
+
+def step_flops(cfg):
+    """Algorithmic flops of one patch step: conv + attention + learned projections."""
+    return cfg.conv_flops() + cfg.attn_flops() + cfg.proj_flops()
+
+
+def call_flops(cfg, name):
+    if name == "conv":
+        return cfg.conv_flops()
+    if name == "attn":
+        return cfg.attn_flops()
+    if name in PROJ_CALLS:
+        return cfg.proj_flops() / 4
+    return 0
 
 
 def kernel_name(op, cfg, cout=None):
@@ -44,6 +62,8 @@ def kernel_name(op, cfg, cout=None):
     library's plan: 128x160 tiles when at least 384 of them exist, else 64x80 tiles)."""
     if op == "attn":
         return "attn_bf16_d64_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel"
+    if op in PROJ_CALLS:
+        return "linear_bf16_kernel" if cfg.dtype == "bf16" else "linear_f32_kernel"
     if op == "conv":
         if cfg.dtype != "bf16":
             return "conv3x3_f32_direct_kernel"
@@ -85,7 +105,7 @@ def cpu_baseline(cfg, inp, i, seconds):
         cores = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = 1
-    params = {"G": cfg.G, "eps": cfg.eps, "heads": cfg.heads, "convs": inp.convs}
+    params = {"G": cfg.G, "eps": cfg.eps, "heads": cfg.heads, "convs": inp.convs, "projs": inp.projs}
     _, state = oracle.sync_layer(cfg.graph, params, inp.x_prev, cfg.P)
     xb = inp.x[:, i * cfg.h:(i + 1) * cfg.h]
     reps = 0
@@ -96,7 +116,7 @@ def cpu_baseline(cfg, inp, i, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    flops = (cfg.conv_flops() + cfg.attn_flops()) * reps
+    flops = step_flops(cfg) * reps
     return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{reps} x oracle displaced step of {cfg.name} patch {i} "
                       f"({'+'.join(cfg.graph)}, float64 numpy) in {el:.1f} s",
@@ -108,7 +128,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c1", help="layer shape: c1 (default), c2, c3, c4a, c4b, c0")
+    ap.add_argument("--config", default="c1",
+                    help="layer shape: c1 (default), c2, c3, c4a, c4b, c2p, c4bp, c0")
     ap.add_argument("--patch", type=int, default=None, help="patch index (default: the config's)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle sample length; 0 skips it")
     ap.add_argument("--seed", type=int, default=0)
@@ -138,7 +159,7 @@ def main():
         f"config {cfg.name}: {cfg.note}; patch {i}")
 
     inp = synth.layer_inputs(cfg, args.seed)
-    layer = DisplacedLayer(cfg, inp.convs, dev)
+    layer = DisplacedLayer(cfg, inp.convs, dev, projs=inp.projs)
     to = lambda a: torch.from_numpy(a).to(dev, layer.dt).contiguous()  # noqa: E731
     layer.warmup(to(inp.x_prev))                 # previous step: synchronous, builds the stale state
     x_patch = to(inp.x[:, i * cfg.h:(i + 1) * cfg.h])
@@ -188,7 +209,7 @@ def main():
         del g
 
     ms_per_step = 1e3 * wall / args.steps
-    flops = cfg.conv_flops() + cfg.attn_flops()
+    flops = step_flops(cfg)
     value = flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[cfg.dtype]
 
@@ -196,11 +217,8 @@ def main():
     kernels = {}
     for k, us in per_call_us.items():
         ent = {"us": round(us, 3)}
-        if k == "conv":
-            ent["tflops"] = round(cfg.conv_flops() / (us * 1e-6) / 1e12, 2)
-            ent["frac_mfma_peak"] = round(ent["tflops"] / peak, 4)
-        elif k == "attn":
-            ent["tflops"] = round(cfg.attn_flops() / (us * 1e-6) / 1e12, 2)
+        if call_flops(cfg, k):
+            ent["tflops"] = round(call_flops(cfg, k) / (us * 1e-6) / 1e12, 2)
             ent["frac_mfma_peak"] = round(ent["tflops"] / peak, 4)
         elif k in ("gn", "gn_silu", "stale_update"):
             gbs = 2 * band / (us * 1e-6) / 1e9       # one read + one write of the band
@@ -208,9 +226,9 @@ def main():
             ent["frac_hbm_peak"] = round(gbs / PEAK_HBM_GBS, 4)
         kernels[k] = ent
 
-    compute = [k for k in ("conv", "attn") if k in per_call_us]
+    compute = [k for k in per_call_us if call_flops(cfg, k)]
     dom = max(compute, key=lambda k: per_call_us[k])
-    dom_flops = cfg.conv_flops() if dom == "conv" else cfg.attn_flops()
+    dom_flops = call_flops(cfg, dom)
     achieved = dom_flops / (per_call_us[dom] * 1e-6) / 1e12
     roofline = {"bound": "mfma", "kernel": kernel_name(dom, cfg), "achieved": round(achieved, 2),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),

@@ -1,10 +1,12 @@
 """One layer's GPU state and its steps, composed from the four C-ABI calls.
 
 A layer (``configs.LayerConfig``) owns, on the GPU:
-  * the GroupNorm statistics table [P][B][G][2] of the previous step, and
+  * the GroupNorm statistics table [P][B][G][2] of the previous step,
   * for every conv or attention step of its graph, the previous step's full
     input map [B][H][W][C] (the stale context; for attention it is the K/V
-    map, since Q = K = V = the step's input).
+    map, since Q = K = V = the step's input), and
+  * for every attention step with learned projections ("attn_proj"), the
+    previous step's projected K and V maps (the K/V cache).
 
 ``warmup(x)`` runs a synchronous step on the full map, patch by patch, and
 leaves the state equal to that step's statistics and maps (warm-up steps are
@@ -19,7 +21,7 @@ from typing import Dict, List, Optional, Sequence, Tuple
 
 import torch
 
-from . import (Patch, _dtype_code, dp_attention_splice, dp_conv3x3_halo, dp_groupnorm_async,
+from . import (Patch, _dtype_code, dp_attention_splice, dp_conv3x3_halo, dp_groupnorm_async, dp_linear,
                dp_stale_update, dp_stats_update, workspace_bytes)
 
 
@@ -42,21 +44,33 @@ def _done(end):
 
 
 class DisplacedLayer:
-    def __init__(self, cfg, convs: Sequence[Tuple["np.ndarray", "np.ndarray"]], device="cuda"):  # noqa: F821
+    def __init__(self, cfg, convs: Sequence[Tuple["np.ndarray", "np.ndarray"]], device="cuda",  # noqa: F821
+                 projs=None):
         self.cfg = cfg
         self.device = torch.device(device)
         self.dt = torch_dtype(cfg.dtype)
         self.convs = [(torch.as_tensor(w).to(self.device, self.dt).contiguous(),
                        torch.as_tensor(b).to(self.device, torch.float32).contiguous()) for w, b in convs]
+        # per attn_proj step: (wq, bq, wk, bk, wv, bv, wo, bo), weights in the storage type
+        self.projs = [tuple(torch.as_tensor(a).to(self.device, self.dt if j % 2 == 0 else torch.float32).contiguous()
+                            for j, a in enumerate(pr)) for pr in (projs or [])]
         c = cfg
         self.table = torch.zeros((c.P, c.B, c.G, 2), dtype=torch.float32, device=self.device)
-        self.maps: Dict[int, torch.Tensor] = {
-            k: torch.zeros((c.B, c.H, c.W, c.C), dtype=self.dt, device=self.device)
-            for k, s in enumerate(c.graph) if s in ("conv", "attn")}
+        full = (c.B, c.H, c.W, c.C)
+        self.maps: Dict = {k: torch.zeros(full, dtype=self.dt, device=self.device)
+                           for k, s in enumerate(c.graph) if s in ("conv", "attn")}
+        for k, s in enumerate(c.graph):
+            if s == "attn_proj":
+                self.maps[(k, "k")] = torch.zeros(full, dtype=self.dt, device=self.device)
+                self.maps[(k, "v")] = torch.zeros(full, dtype=self.dt, device=self.device)
         self.fresh_stats = torch.empty((c.B, c.G, 2), dtype=torch.float32, device=self.device)
         # patch-sized intermediates, reused by every step
         band = (c.B, c.h, c.W, c.C)
         self.bufs = [torch.empty(band, dtype=self.dt, device=self.device) for _ in c.graph]
+        # attn_proj scratch bands: projected queries, attention output, fresh K and V (when
+        # they are not written straight into the cache)
+        self.pbufs = {k: {n: torch.empty(band, dtype=self.dt, device=self.device) for n in "qakv"}
+                      for k, s in enumerate(c.graph) if s == "attn_proj"}
         # one workspace for every call of a step (calls are ordered on one stream); owned by the
         # layer so a captured graph keeps pointing at live memory
         code = _dtype_code(self.bufs[0])
@@ -66,7 +80,7 @@ class DisplacedLayer:
         for s in c.graph:
             if s in ("gn", "gn_silu"):
                 need = max(need, workspace_bytes("groupnorm", self.patch(0), code, c.G))
-            elif s == "attn":
+            elif s in ("attn", "attn_proj"):
                 need = max(need, workspace_bytes("attention", self.patch(0), code, c.heads, c.C // c.heads))
         self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
 
@@ -84,14 +98,16 @@ class DisplacedLayer:
     # ---- one patch, displaced ------------------------------------------------
     def calls(self, x_patch, i, gn_mode="corrected", update_state=True):
         """Patch i's displaced layer step as a list of (name, launch, output): each launch
-        enqueues one C-ABI call on the current stream.  Running them in order is one step
-        (without the splice of ``step`` when the state is not refreshed in place)."""
+        enqueues one C-ABI call on the current stream; ``output`` is the graph step's patch
+        output on the last call of that step and None on the others.  Running them in order
+        is one step (without the splice of ``step`` when the state is not refreshed in place)."""
         c = self.cfg
         p = self.patch(i)
         in_place = update_state and c.B == 1 and gn_mode == "corrected"
         h = x_patch
         out_list = []
         conv_i = 0
+        proj_i = 0
         for k, s in enumerate(c.graph):
             nxt = k + 1
             if in_place and nxt < len(c.graph) and nxt in self.maps:
@@ -108,10 +124,28 @@ class DisplacedLayer:
                 conv_i += 1
                 fn = (lambda h=h, out=out, k=k, w=w, b=b: dp_conv3x3_halo(
                     p, h, self.maps[k], w, b, y_patch=out, ws=self.ws))
-            else:
+            elif s == "attn":
                 tok, st, o = self._tok(h), self._tok(self.maps[k]), self._tok(out)
                 fn = (lambda tok=tok, st=st, o=o: dp_attention_splice(
                     p, c.heads, tok, tok, tok, st, st, o_patch=o, ws=self.ws))
+            else:   # attn_proj
+                wq, bq, wk, bk, wv, bv, wo, bo = self.projs[proj_i]
+                proj_i += 1
+                pb = self.pbufs[k]
+                kcache, vcache = self.maps[(k, "k")], self.maps[(k, "v")]
+                if in_place:       # fresh K and V straight into band i of the cache
+                    kb = self._tok(kcache[:, i * c.h:(i + 1) * c.h])
+                    vb = self._tok(vcache[:, i * c.h:(i + 1) * c.h])
+                else:
+                    kb, vb = self._tok(pb["k"]), self._tok(pb["v"])
+                tok, q, a = self._tok(h), self._tok(pb["q"]), self._tok(pb["a"])
+                out_list.append(("proj_q", lambda tok=tok, q=q, w=wq, b=bq: dp_linear(tok, w, b, y=q), None))
+                out_list.append(("proj_k", lambda tok=tok, y=kb, w=wk, b=bk: dp_linear(tok, w, b, y=y), None))
+                out_list.append(("proj_v", lambda tok=tok, y=vb, w=wv, b=bv: dp_linear(tok, w, b, y=y), None))
+                out_list.append(("attn", lambda q=q, kb=kb, vb=vb, a=a, ks=self._tok(kcache), vs=self._tok(vcache):
+                                 dp_attention_splice(p, c.heads, q, kb, vb, ks, vs, o_patch=a, ws=self.ws), None))
+                fn = (lambda a=a, o=self._tok(out), w=wo, b=bo: dp_linear(a, w, b, y=o))
+                s = "proj_o"
             out_list.append((s, fn, out))
             h = out
         return out_list
@@ -139,7 +173,8 @@ class DisplacedLayer:
             ev = _mark(events, s)
             fn()
             _done(ev)
-            outs.append(out)
+            if out is not None:
+                outs.append(out)
         if update_state and not in_place:
             self.splice_state(i, x_patch, outs, events)
         return outs
@@ -175,18 +210,22 @@ class DisplacedLayer:
         outs_full = [torch.empty(full, dtype=self.dt, device=self.device) for _ in c.graph]
         has_gn = any(s in ("gn", "gn_silu") for s in c.graph)
         next_table = torch.empty_like(self.table)
+        next_kv = {key: torch.empty(full, dtype=self.dt, device=self.device)
+                   for key in self.maps if isinstance(key, tuple)}
         for i in range(c.P):
             p = self.patch(i)
             outs = self.step(self.band(x_full, i), i, gn_mode, update_state=False)
             for k, o in enumerate(outs):
                 dp_stale_update(p, o, outs_full[k])
+            for (k, kv), m in next_kv.items():
+                dp_stale_update(p, self.pbufs[k][kv], m)
             if has_gn:
                 dp_stats_update(c.P, i, self.fresh_stats, next_table)
         if has_gn:
             self.table.copy_(next_table)
         inputs = [x_full] + outs_full[:-1]
-        for k, m in self.maps.items():
-            m.copy_(inputs[k])
+        for key, m in self.maps.items():
+            m.copy_(next_kv[key] if isinstance(key, tuple) else inputs[key])
         return outs_full
 
     def splice_state(self, i, x_patch, outs, events=None):
@@ -198,6 +237,10 @@ class DisplacedLayer:
             if s in ("gn", "gn_silu"):
                 ev = _mark(events, "stats_update")
                 dp_stats_update(c.P, i, self.fresh_stats, self.table)
+            elif s == "attn_proj":
+                ev = _mark(events, "stale_update")
+                dp_stale_update(p, self.pbufs[k]["k"], self.maps[(k, "k")])
+                dp_stale_update(p, self.pbufs[k]["v"], self.maps[(k, "v")])
             elif k in self.maps:
                 ev = _mark(events, "stale_update")
                 dp_stale_update(p, inputs[k], self.maps[k])
@@ -212,6 +255,7 @@ class DisplacedLayer:
         h_full = x_full
         outs = []
         conv_i = 0
+        proj_i = 0
         for k, s in enumerate(c.graph):
             out_full = torch.empty((c.B, c.H, c.W, c.C), dtype=self.dt, device=self.device)
             if s in ("gn", "gn_silu"):
@@ -224,6 +268,21 @@ class DisplacedLayer:
                                               "corrected", "silu" if s == "gn_silu" else None,
                                               fresh_stats_out=self.fresh_stats)
                     dp_stale_update(self.patch(j), y, out_full)
+            elif s == "attn_proj":
+                wq, bq, wk, bk, wv, bv, wo, bo = self.projs[proj_i]
+                proj_i += 1
+                tok = self._tok(h_full)
+                kc, vc = self.maps[(k, "k")], self.maps[(k, "v")]
+                dp_linear(tok, wk, bk, y=self._tok(kc))
+                dp_linear(tok, wv, bv, y=self._tok(vc))
+                q_full = dp_linear(tok, wq, bq).reshape(h_full.shape)
+                a_full = torch.empty_like(h_full)
+                for j in range(c.P):
+                    pj = self.patch(j)
+                    qj, kj, vj = (self._tok(self.band(m, j)) for m in (q_full, kc, vc))
+                    a = dp_attention_splice(pj, c.heads, qj, kj, vj, self._tok(kc), self._tok(vc))
+                    dp_stale_update(pj, a.reshape(qj.shape[0], c.h, c.W, c.C), a_full)
+                dp_linear(self._tok(a_full), wo, bo, y=self._tok(out_full))
             else:
                 for j in range(c.P):
                     dp_stale_update(self.patch(j), self.band(h_full, j), self.maps[k])

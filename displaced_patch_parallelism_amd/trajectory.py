@@ -41,8 +41,8 @@ def run(cfg, steps, seed=0, modes=MODES, device="cuda:0", log=None):
     """Yields, per step t = 1..steps, {mode: relative L2 drift of the final output}."""
     dev = torch.device(device)
     tr = synth.trajectory(cfg, seed, steps)
-    sync = DisplacedLayer(cfg, tr.convs, dev)
-    layers = {m: DisplacedLayer(cfg, tr.convs, dev) for m in modes}
+    sync = DisplacedLayer(cfg, tr.convs, dev, projs=tr.projs)
+    layers = {m: DisplacedLayer(cfg, tr.convs, dev, projs=tr.projs) for m in modes}
     to = lambda a: torch.from_numpy(a).to(dev, sync.dt).contiguous()  # noqa: E731
     x0 = to(tr.xs[0])
     for layer in layers.values():

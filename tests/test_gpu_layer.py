@@ -26,13 +26,22 @@ SMALL = {
                             heads=3, head_dim=64),
     "batched": LayerConfig("b2", "bf16", B=2, H=8, W=16, C=64, G=8, P=2, graph=("gn_silu", "conv", "attn"),
                            heads=1, head_dim=64),
+    # learned Q/K/V/O projections: the K/V cache is the previous step's projected maps
+    "c2p-like": LayerConfig("c2ps", "bf16", B=1, H=16, W=16, C=128, G=32, P=4,
+                            graph=("gn", "attn_proj", "conv"), heads=2, head_dim=64),
+    "c4bp-like": LayerConfig("c4bps", "bf16", B=1, H=24, W=20, C=192, G=32, P=8, graph=("gn", "attn_proj"),
+                             heads=3, head_dim=64),
+    "batched-proj": LayerConfig("b2p", "bf16", B=2, H=8, W=16, C=64, G=8, P=2,
+                                graph=("gn_silu", "attn_proj", "conv"), heads=1, head_dim=64),
+    "f32-proj": LayerConfig("f32p", "f32", B=1, H=8, W=12, C=64, G=8, P=2, graph=("gn", "attn_proj"),
+                            heads=2, head_dim=32),
 }
 
 
 def two_step(c, seed=0, patches=None):
     inp = synth.layer_inputs(c, seed)
-    params = {"G": c.G, "eps": c.eps, "heads": c.heads, "convs": inp.convs}
-    layer = DisplacedLayer(c, inp.convs)
+    params = {"G": c.G, "eps": c.eps, "heads": c.heads, "convs": inp.convs, "projs": inp.projs}
+    layer = DisplacedLayer(c, inp.convs, projs=inp.projs)
     announce("layer warm-up", c.name)
     warm = layer.warmup(gpu(inp.x_prev, c.dtype))
     sync_outs, state = oracle.sync_layer(c.graph, params, inp.x_prev, c.P)
@@ -59,16 +68,19 @@ def test_small_graphs(name):
     two_step(SMALL[name], seed=1)
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c2p"])
 def test_config_layers_measured_patch(name):
     c = CONFIGS[name]
     two_step(c, seed=0, patches=[c.patch])
 
 
-def test_state_splice_matches_oracle():
-    c = SMALL["c2-like"]
+@pytest.mark.parametrize("name", ["c2-like", "c2p-like", "batched-proj"])
+def test_state_splice_matches_oracle(name):
+    """After patch i's step the state holds its fresh band / moments (in place for B == 1,
+    by a splice after the step otherwise); the next patch's step then reads it."""
+    c = SMALL[name]
     layer, inp, params, state = two_step(c, seed=2, patches=[])
-    i, h = 2, c.h
+    i, h = 1, c.h
     xb = inp.x[:, i * h:(i + 1) * h]
     layer.step(gpu(xb, c.dtype), i, update_state=True)
     _, new_state = oracle.displaced_layer(c.graph, params, xb, state, c.P, i)
@@ -76,13 +88,20 @@ def test_state_splice_matches_oracle():
     np.testing.assert_allclose(host(layer.table), new_state["stats"], rtol=1e-4, atol=1e-4)
     for k, m in layer.maps.items():
         assert_parity(host(m), new_state["maps"][k], c.dtype, f"state map {k}")
+    j = 0
+    xj = inp.x[:, j * h:(j + 1) * h]
+    outs = layer.step(gpu(xj, c.dtype), j, update_state=False)
+    ref, _ = oracle.displaced_layer(c.graph, params, xj, new_state, c.P, j)
+    for k, (g, r) in enumerate(zip(outs, ref)):
+        assert_parity(host(g), r, c.dtype, f"{c.name} patch {j} after the splice, step {k}")
 
 
-def test_stale_equal_fresh_gives_warmup_output():
+@pytest.mark.parametrize("name", ["c2-like", "c2p-like"])
+def test_stale_equal_fresh_gives_warmup_output(name):
     """Warm-up on x itself, then a displaced step on x: equals the warm-up's band (sync)."""
-    c = SMALL["c2-like"]
+    c = SMALL[name]
     inp = synth.layer_inputs(c, 3)
-    layer = DisplacedLayer(c, inp.convs)
+    layer = DisplacedLayer(c, inp.convs, projs=inp.projs)
     announce("layer stale==fresh")
     warm = layer.warmup(gpu(inp.x, c.dtype))
     for i in range(c.P):

@@ -23,6 +23,8 @@ CASES = {
     "c1-like": LayerConfig("c1s", "bf16", B=1, H=32, W=24, C=128, G=32, P=4, graph=("gn_silu", "conv")),
     "c2-like": LayerConfig("c2s", "bf16", B=1, H=16, W=16, C=128, G=32, P=4, graph=("gn", "attn", "conv"),
                            heads=2, head_dim=64),
+    "c2p-like": LayerConfig("c2ps", "bf16", B=1, H=16, W=16, C=128, G=32, P=4,
+                            graph=("gn", "attn_proj", "conv"), heads=2, head_dim=64),
 }
 
 
@@ -31,8 +33,8 @@ CASES = {
 def test_step_all_matches_oracle(name, mode):
     c = CASES[name]
     tr = synth.trajectory(c, seed=4, steps=2)
-    params = {"G": c.G, "eps": c.eps, "heads": c.heads, "convs": tr.convs}
-    layer = DisplacedLayer(c, tr.convs)
+    params = {"G": c.G, "eps": c.eps, "heads": c.heads, "convs": tr.convs, "projs": tr.projs}
+    layer = DisplacedLayer(c, tr.convs, projs=tr.projs)
     layer.warmup(gpu(tr.xs[0], c.dtype))
     _, state = oracle.sync_layer(c.graph, params, tr.xs[0], c.P)
     gn_mode = {"corrected": oracle.GN_CORRECTED, "local": oracle.GN_LOCAL, "stale": oracle.GN_STALE}[mode]
@@ -43,6 +45,8 @@ def test_step_all_matches_oracle(name, mode):
         for k, (g, r) in enumerate(zip(outs, ref)):
             assert_parity(host(g), r, c.dtype, f"{name} {mode} t{t} step {k} ({c.graph[k]})")
         assert_parity(host(layer.table), state["stats"], "f32", f"{name} {mode} t{t} statistics table")
+        for key, m in layer.maps.items():
+            assert_parity(host(m), state["maps"][key], c.dtype, f"{name} {mode} t{t} state map {key}")
 
 
 def test_corrected_groupnorm_drifts_least():
