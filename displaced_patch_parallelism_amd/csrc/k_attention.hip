@@ -12,8 +12,11 @@
 // base-2 domain (log2(e) folded into the scale).  A workgroup holds 256
 // queries (8 waves x 32); K/V tiles of 64 tokens are staged in LDS, K
 // row-major and V transposed.  Each wave computes S^T = K Q^T with
-// v_mfma_f32_32x32x16_bf16 so that lane l owns query l%32: the running max
-// and sum stay in the lane (one cross-half exchange per tile for the max).
+// v_mfma_f32_32x32x16_bf16 so that lane l owns query l%32: the running
+// offset and sum stay in the lane.  Q is pre-scaled and the S MFMAs start
+// from C = -offset, so S - offset comes out of the MFMA; the offset follows
+// the running maximum lazily (the cross-half exchange happens only when it
+// moves).
 // P^T (bf16) feeds O^T = V^T P^T directly from registers; within each 16-key
 // MFMA step the key order is permuted identically on both operands so the
 // S^T accumulator layout needs no shuffle.  The token loader picks the fresh
@@ -34,6 +37,7 @@ constexpr int kStages = 4;      // LDS ring depth (16 KB per stage)
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;
+constexpr float kLazy = 8.0f;     // offset moves when a score exceeds it by more than this (log2)
 
 struct AttnArgs {
     const uint16_t* q;
@@ -97,7 +101,7 @@ __device__ __forceinline__ s16x4 tr_read(const char* p) {
 // stays row-major in LDS.
 // ---------------------------------------------------------------------------
 template <int STAGES, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void attn_bf16_d64_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4))) void attn_bf16_d64_kernel(AttnArgs a) {
     constexpr int STAGE = 16 * 1024;          // K tile 8 KB + V tile 8 KB
     constexpr int LOADS = 16 / WAVES;         // DMA loads (1 KB chunks) per wave per stage
     constexpr int QTW = 32 * WAVES;           // queries per workgroup
@@ -123,42 +127,75 @@ __global__ __launch_bounds__(64 * WAVES) void attn_bf16_d64_kernel(AttnArgs a) {
     const bool qvalid = myq < a.Nq;
     const int col0 = e * D;
 
+    // Q scaled by scale * log2(e) once (rounded to bf16), so S = K Q^T is already in the
+    // base-2 exponent domain
     bf16x8 q0, q1, q2, q3;
     {
-        uint4 r0 = make_uint4(0, 0, 0, 0), r1 = r0, r2 = r0, r3 = r0;
+        uint4 r[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
+                      make_uint4(0, 0, 0, 0)};
         if (qvalid) {
             const uint16_t* qp = a.q + ((int64_t)b * a.Nq + myq) * a.C + col0 + hsel * 8;
-            r0 = *(const uint4*)(qp + 0);
-            r1 = *(const uint4*)(qp + 16);
-            r2 = *(const uint4*)(qp + 32);
-            r3 = *(const uint4*)(qp + 48);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) r[j] = *(const uint4*)(qp + 16 * j);
         }
-        q0 = __builtin_bit_cast(bf16x8, r0);
-        q1 = __builtin_bit_cast(bf16x8, r1);
-        q2 = __builtin_bit_cast(bf16x8, r2);
-        q3 = __builtin_bit_cast(bf16x8, r3);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float f[8];
+            unpack8(r[j], f);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) f[u] *= a.sc;
+            r[j] = pack8(f);
+        }
+        q0 = __builtin_bit_cast(bf16x8, r[0]);
+        q1 = __builtin_bit_cast(bf16x8, r[1]);
+        q2 = __builtin_bit_cast(bf16x8, r[2]);
+        q3 = __builtin_bit_cast(bf16x8, r[3]);
     }
 
     const int t0 = (int)((int64_t)a.kv_tiles * split / a.kvsplit);
     const int t1 = (int)((int64_t)a.kv_tiles * (split + 1) / a.kvsplit);
     const int nt = t1 - t0;
 
-    // DMA lanes: wave w issues chunks w*LOADS+j (0..7 K rows, 8..15 V rows), 8 rows of 128 B per chunk
+    // DMA lanes: wave w issues chunks w*LOADS+j (0..7 K rows, 8..15 V rows), 8 rows of 128 B per chunk.
+    // A tile wholly inside the fresh band or wholly in the stale map (all but at most two tiles
+    // per split) takes one wave-uniform base pointer plus a fixed per-lane offset; a tile that
+    // straddles a band edge or runs past the last key picks the buffer per row.
     const int sub = lane >> 3;
     const int slot = lane & 7;
     const uint16_t* zero = (const uint16_t*)g_attn_zero;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    int loff[LOADS];
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+        const int row = ((wave_u * LOADS + j) & 7) * 8 + sub;
+        loff[j] = row * a.C + col0 + (slot ^ (row & 7)) * 8;
+    }
+    const int64_t fresh_base = (int64_t)b * a.Nq - a.band0;   // token n of the band at fresh_base + n
+    const int64_t stale_base = (int64_t)b * a.N;
 #define DPA_ISSUE(T, BUF)                                                                           \
     do {                                                                                            \
         char* st_ = smem + (BUF) * STAGE;                                                           \
-        _Pragma("unroll") for (int j = 0; j < LOADS; ++j) {                                         \
-            const int q_ = wave * LOADS + j;                                                        \
-            const int row_ = (q_ & 7) * 8 + sub;                                                    \
-            const int n_ = (T) * KT + row_;                                                         \
-            const int ch_ = (slot ^ (row_ & 7)) * 8;                                                \
-            const uint16_t* fr_ = q_ < 8 ? a.k : a.v;                                               \
-            const uint16_t* sl_ = q_ < 8 ? a.ks : a.vs;                                             \
-            const uint16_t* g_ = n_ < a.N ? kv_row(fr_, sl_, b, n_, a, col0 + ch_) : zero;          \
-            __builtin_amdgcn_global_load_lds((const void*)g_, (lds_void*)(st_ + q_ * 1024), 16, 0, 0); \
+        const int n0_ = (T) * KT;                                                                   \
+        const bool in_band_ = n0_ >= a.band0 && n0_ + KT <= a.band0 + a.Nq;                         \
+        const bool in_stale_ = (n0_ + KT <= a.band0 || n0_ >= a.band0 + a.Nq) && n0_ + KT <= a.N;  \
+        if (in_band_ || in_stale_) {                                                                \
+            _Pragma("unroll") for (int j = 0; j < LOADS; ++j) {                                     \
+                const int q_ = wave_u * LOADS + j;                                                  \
+                const uint16_t* buf_ = in_band_ ? (q_ < 8 ? a.k : a.v) : (q_ < 8 ? a.ks : a.vs);    \
+                const uint16_t* g_ = buf_ + ((in_band_ ? fresh_base : stale_base) + n0_) * a.C + loff[j]; \
+                __builtin_amdgcn_global_load_lds((const void*)g_, (lds_void*)(st_ + q_ * 1024), 16, 0, 0); \
+            }                                                                                       \
+        } else {                                                                                    \
+            _Pragma("unroll") for (int j = 0; j < LOADS; ++j) {                                     \
+                const int q_ = wave_u * LOADS + j;                                                  \
+                const int row_ = (q_ & 7) * 8 + sub;                                                \
+                const int n_ = n0_ + row_;                                                          \
+                const int ch_ = (slot ^ (row_ & 7)) * 8;                                            \
+                const uint16_t* fr_ = q_ < 8 ? a.k : a.v;                                           \
+                const uint16_t* sl_ = q_ < 8 ? a.ks : a.vs;                                         \
+                const uint16_t* g_ = n_ < a.N ? kv_row(fr_, sl_, b, n_, a, col0 + ch_) : zero;      \
+                __builtin_amdgcn_global_load_lds((const void*)g_, (lds_void*)(st_ + q_ * 1024), 16, 0, 0); \
+            }                                                                                       \
         }                                                                                           \
     } while (0)
 
@@ -180,11 +217,17 @@ __global__ __launch_bounds__(64 * WAVES) void attn_bf16_d64_kernel(AttnArgs a) {
             voff[h][db] = 8192 + row * 128 + (((d >> 3) ^ (row & 7)) * 16) + (d & 7) * 2;
         }
 
-    f32x16 o0, o1;
+    // Online softmax with a lazily moved offset: the QK MFMAs start from C = -m_run, so they
+    // produce S - m_run directly and the exponent needs no subtraction.  m_run is set to the
+    // first tile's maximum and moved up to the running maximum only when some score exceeds
+    // it by more than kLazy (p <= 2^kLazy, harmless in fp32 sums and bf16 P); since m_run is
+    // always a score that occurred, the largest p of a row is >= 1.
+    f32x16 o0, o1, negm;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o0[i] = o1[i] = 0.f;
-    float m_run = kNegBig;
+    for (int i = 0; i < 16; ++i) o0[i] = o1[i] = negm[i] = 0.f;
+    float m_run = 0.f;
     float l_run = 0.f;
+    bool first = true;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
     if (nt > 0) {
@@ -203,10 +246,8 @@ __global__ __launch_bounds__(64 * WAVES) void attn_bf16_d64_kernel(AttnArgs a) {
 
         // S^T[key][query], keys kb*32 + 8q + 4*hsel + r in s_kb[4q + r]
         f32x16 s0, s1;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s0[i] = s1[i] = 0.f;
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + koff[0]), q0, s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + 4096 + koff[0]), q0, s1, 0, 0, 0);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + koff[0]), q0, negm, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + 4096 + koff[0]), q0, negm, 0, 0, 0);
         s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + koff[1]), q1, s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + 4096 + koff[1]), q1, s1, 0, 0, 0);
         s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + koff[2]), q2, s0, 0, 0, 0);
@@ -224,7 +265,16 @@ __global__ __launch_bounds__(64 * WAVES) void attn_bf16_d64_kernel(AttnArgs a) {
                 if (off + 32 >= kvalid) s1[i] = -INFINITY;
             }
         }
-        // two independent chains of 3-input maxima (v_max3_f32)
+        // Exponentials against the current offset; the tile maximum (two independent chains of
+        // 3-input maxima, v_max3_f32, over this lane's half of the keys) only decides whether
+        // the offset must move, which is rare after the first tile: then the exponentials are
+        // taken from the kept scores against the moved offset instead.
+        f32x16 p0f, p1f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            p0f[i] = __builtin_amdgcn_exp2f(s0[i]);
+            p1f[i] = __builtin_amdgcn_exp2f(s1[i]);
+        }
         float mx0 = fmaxf(s0[0], s0[1]), mx1 = fmaxf(s1[0], s1[1]);
 #pragma unroll
         for (int i = 2; i < 16; i += 2) {
@@ -232,21 +282,24 @@ __global__ __launch_bounds__(64 * WAVES) void attn_bf16_d64_kernel(AttnArgs a) {
             mx1 = fmaxf(fmaxf(mx1, s1[i]), s1[i + 1]);
         }
         float mx = fmaxf(mx0, mx1);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // rescale the running sum and O only when some query's max grew
-        const float m_new = fmaxf(m_run, mx * a.sc);
-        if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        if (__builtin_amdgcn_ballot_w64(first || mx > kLazy)) {
+            mx = fmaxf(mx, __shfl_xor(mx, 32));     // max of S - m_run over the tile's keys
+            const float delta = first ? mx : fmaxf(mx, 0.f);
+            const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(-delta);
             l_run *= alpha;
             o0 *= alpha;
             o1 *= alpha;
-            m_run = m_new;
-        }
+            m_run += delta;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], a.sc, -m_run));
-            s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], a.sc, -m_run));
+            for (int i = 0; i < 16; ++i) {
+                p0f[i] = __builtin_amdgcn_exp2f(s0[i] - delta);
+                p1f[i] = __builtin_amdgcn_exp2f(s1[i] - delta);
+                negm[i] = -m_run;
+            }
+            first = false;
         }
+        s0 = p0f;
+        s1 = p1f;
         // P^T operands (keys 16u + 4*hsel + {0..3, 8..11}); the row sum adds the same bf16 values
         const bf16x8 p0 = pack_probs<0>(s0);
         const bf16x8 p1 = pack_probs<2>(s0);
