@@ -43,7 +43,8 @@ hipError_t launch_groupnorm(const Geom& g, const GnPlan& plan, bool bf16, int G,
 
 // ---- conv3x3 with stale halo -------------------------------------------
 struct ConvPlan {
-    int kind;       // 0 = f32 direct, 1 = bf16 shared-ring 128x160 tiles, 2 = bf16 wave-split 64x80 tiles
+    int kind;       // 0 = f32 direct, 1 = bf16 shared-ring 128x160 tiles, 2 = bf16 wave-split 64x80
+                    // tiles, 3 = bf16 shared-ring 256x160 tiles
     int bm, bn;     // output tile (pixels x output channels)
     int mtiles, ntiles;
     int ktiles;     // K stages: 32 input channels of one kernel row each (3 * Cin / 32)

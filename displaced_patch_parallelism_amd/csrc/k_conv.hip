@@ -28,7 +28,9 @@
 //     so each XCD walks a contiguous run of pixel tiles, keeping the inputs those
 //     tiles share in one L2.
 //   Large maps: 128x160 tiles (4 rows x 32 columns), one LDS ring shared by
-//   4 waves (2x2 of 64 pixels x 80 channels), two workgroups per CU.  Small
+//   4 waves (2x2 of 64 pixels x 80 channels), two workgroups per CU; or, when
+//   they fill the GPU in no more rounds, 256x160 tiles (8 rows) with 8 waves,
+//   one workgroup per CU and a 3-stage ring.  Small
 //   maps: 64x80 tiles (2 rows x 32 columns) whose 4 waves each take a quarter
 //   of K through a private ring and are summed through LDS in wave order; K is
 //   also split across workgroups until about 256 of them run, the fp32
@@ -181,23 +183,27 @@ __device__ __forceinline__ void tile_origin(const ConvArgs& a, int mt, int& bb, 
 }
 
 // ---------------------------------------------------------------------------
-// Large maps: tile 4 rows x 32 columns x 160 channels, 4 waves (2 pixel-row pairs x 2 channel
-// halves), one 2-stage ring shared by the workgroup (2 x 38.5 KB, so two workgroups share a CU
-// and one's waits overlap the other's MFMAs).  The 39 loads of a stage are dealt round-robin
-// to the waves; a barrier per stage publishes it.
+// Large maps: tile TR rows x 32 columns x 160 channels; NW = TR waves (TR/2 pixel-row pairs x 2
+// channel halves of 64 pixels x 80 channels each) share one STAGES-deep ring; a barrier per
+// stage publishes it.  The stage's loads are dealt round-robin to the waves.
+//   TR = 4: 4 waves, 2 x 38.5 KB, two workgroups per CU (one's waits overlap the other's MFMAs).
+//   TR = 8: 8 waves, 3 x 47 KB, one workgroup per CU: the 160 channels' weights of a stage serve
+//           256 pixels instead of 128 (fewer bytes per MFMA from L2), and two stages load while
+//           one is multiplied.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 2) void conv3x3_bf16_halo_tile_kernel(ConvArgs a) {
-    constexpr int TR = 4, BN = 160;
+template <int TR, int STAGES>
+__device__ __forceinline__ void conv_tile_body(const ConvArgs& a, char* smem) {
+    constexpr int BN = 160;
+    constexpr int NW = TR;                        // waves: TR / 2 row pairs x 2 channel halves
     using S = Stage<TR, BN>;
-    constexpr int AQ = (S::A_LOADS + 3) / 4;     // A loads per wave (at most)
-    constexpr int BQ = (S::B_LOADS + 3) / 4;
-    constexpr int SMEM = 2 * S::BYTES > 128 * BN * 2 ? 2 * S::BYTES : 128 * BN * 2;
-    __shared__ __attribute__((aligned(1024))) char smem[SMEM];
+    constexpr int AQ = (S::A_LOADS + NW - 1) / NW;   // A loads per wave (at most)
+    constexpr int BQ = (S::B_LOADS + NW - 1) / NW;
+    constexpr int PX = TR * kTileTC;              // output pixels per tile
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % (TR / 2), wn = wave / (TR / 2);
     const int lt = xcd_order(blockIdx.x, gridDim.x);
     const int mt = lt % a.mtiles;
     const int nt = lt / a.mtiles;
@@ -211,12 +217,14 @@ __global__ __launch_bounds__(256, 2) void conv3x3_bf16_halo_tile_kernel(ConvArgs
     const uint16_t* ap2[AQ];
 #pragma unroll
     for (int q = 0; q < AQ; ++q) {
-        const int j = wave + 4 * q;
+        const int j = wave + NW * q;
         resolve_a_slot<TR>(a, bb, ty0, tx0, j * 64 + lane, ap0[q], ap1[q], ap2[q]);
     }
     uint32_t bo[BQ];
 #pragma unroll
-    for (int q = 0; q < BQ; ++q) bo[q] = b_slot_offset<BN>(a, n0, (wave + 4 * q) * 64 + lane);
+    for (int q = 0; q < BQ; ++q) bo[q] = b_slot_offset<BN>(a, n0, (wave + NW * q) * 64 + lane);
+    // this wave's loads per stage (the deal is uneven when NW does not divide the load counts)
+    const int nloads = (S::A_LOADS - wave + NW - 1) / NW + (S::B_LOADS - wave + NW - 1) / NW;
 
     // Issue the loads of stage (cc, KY) into ring buffer BUF; KY is a literal so each kernel row
     // reads its own source array (a runtime select between them becomes a scratch-indexed load).
@@ -224,7 +232,7 @@ __global__ __launch_bounds__(256, 2) void conv3x3_bf16_halo_tile_kernel(ConvArgs
     do {                                                                                            \
         char* st_ = smem + (BUF) * S::BYTES;                                                        \
         _Pragma("unroll") for (int q = 0; q < AQ; ++q) {                                            \
-            const int j_ = wave + 4 * q;                                                            \
+            const int j_ = wave + NW * q;                                                           \
             if (j_ < S::A_LOADS) {                                                                  \
                 const uint16_t* g_ = SRC[q] ? SRC[q] + (CC) * 32 : zero;                            \
                 if (j_ < S::A_LOADS - 1 || lane < S::A_TAIL)                                        \
@@ -234,7 +242,7 @@ __global__ __launch_bounds__(256, 2) void conv3x3_bf16_halo_tile_kernel(ConvArgs
         }                                                                                           \
         const char* wk_ = (const char*)a.w + ((int64_t)3 * (KY) * a.Cin + (CC) * 32) * 2;          \
         _Pragma("unroll") for (int q = 0; q < BQ; ++q) {                                            \
-            const int j_ = wave + 4 * q;                                                            \
+            const int j_ = wave + NW * q;                                                           \
             if (j_ < S::B_LOADS)                                                                    \
                 __builtin_amdgcn_global_load_lds((const void*)(wk_ + bo[q]),                       \
                                                  (lds_void*)(st_ + S::B_OFF + j_ * 1024), 16, 0, 0); \
@@ -259,19 +267,32 @@ __global__ __launch_bounds__(256, 2) void conv3x3_bf16_halo_tile_kernel(ConvArgs
     operand_offsets<TR, BN>(lane, 2 * wm, wn, aoff, boff);
 
     const int nk = a.kstages;
-    DPH_ISSUE(0, 0);
+#pragma unroll
+    for (int k = 0; k < STAGES - 1; ++k)
+        if (k < nk) DPH_ISSUE(k, k);
     for (int it = 0; it < nk; ++it) {
-        wait_vmcnt<0>();     // this wave's loads of stage it have landed ...
+        // this wave's loads of stage it have landed (those of the stages after it, issued later,
+        // may still be in flight; loads complete in order) ...
+        if (STAGES == 2 || it + 1 >= nk) {
+            wait_vmcnt<0>();
+        } else {
+            static_assert(STAGES == 2 || STAGES == 3, "ring depth");
+            // one later stage in flight: allow this wave's per-stage load count
+            if (nloads >= 7) wait_vmcnt<7>();
+            else if (nloads == 6) wait_vmcnt<6>();
+            else if (nloads == 5) wait_vmcnt<5>();
+            else wait_vmcnt<0>();
+        }
         __syncthreads();     // ... and everyone's; everyone is also done with stage it-1
-        if (it + 1 < nk) DPH_ISSUE(it + 1, (it + 1) & 1);
-        stage_mfma<BN>(smem + (it & 1) * S::BYTES, aoff, boff, acc);
+        if (it + STAGES - 1 < nk) DPH_ISSUE(it + STAGES - 1, (it + STAGES - 1) % STAGES);
+        stage_mfma<BN>(smem + (it % STAGES) * S::BYTES, aoff, boff, acc);
     }
 #undef DPH_ISSUE
 #undef DPH_ISSUE_KY
     __syncthreads();   // ring no longer read: reuse it for the output tile
 
     // acc[i][n][r] = D[pixel 16i + 4(l>>4) + r of the wave][channel 16n + (l&15) of the wave]
-    uint16_t* tile = (uint16_t*)smem;    // [128 pixels][BN] bf16, pixel = tile row * 32 + column
+    uint16_t* tile = (uint16_t*)smem;    // [PX pixels][BN] bf16, pixel = tile row * 32 + column
     const int ecol = lane & 15;
     const int erow = 4 * (lane >> 4);
 #pragma unroll
@@ -286,13 +307,29 @@ __global__ __launch_bounds__(256, 2) void conv3x3_bf16_halo_tile_kernel(ConvArgs
     }
     __syncthreads();
     constexpr int CPR = BN * 2 / 16;    // 16-byte chunks per output pixel
-    for (int q = tid; q < 128 * CPR; q += kThreads) {
+    for (int q = tid; q < PX * CPR; q += 64 * NW) {
         const int px = q / CPR, c16 = q - px * CPR;
         const int y = ty0 + (px >> 5), x = tx0 + (px & 31), co = n0 + c16 * 8;
         if (y < a.h && x < a.W && co < a.Cout)
             *(uint4*)(a.y + (((int64_t)bb * a.h + y) * a.W + x) * a.Cout + co) =
                 *(const uint4*)(tile + px * BN + c16 * 8);
     }
+}
+
+template <int TR, int STAGES>
+constexpr int tile_smem() {
+    using S = Stage<TR, 160>;
+    return STAGES * S::BYTES > TR * kTileTC * 160 * 2 ? STAGES * S::BYTES : TR * kTileTC * 160 * 2;
+}
+
+__global__ __launch_bounds__(256, 2) void conv3x3_bf16_halo_tile_kernel(ConvArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[tile_smem<4, 2>()];
+    conv_tile_body<4, 2>(a, smem);
+}
+
+__global__ __launch_bounds__(512, 1) void conv3x3_bf16_halo_tile8_kernel(ConvArgs a) {
+    __shared__ __attribute__((aligned(1024))) char smem[tile_smem<8, 3>()];
+    conv_tile_body<8, 3>(a, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -505,7 +542,16 @@ ConvPlan plan_conv(const Geom& g, int Cout, bool bf16) {
     const int64_t big = (int64_t)g.B * ((g.h + 3) / 4) * ntx * ((Cout + 159) / 160);
     p.ktiles = 3 * g.C / 32;          // K stages (cc, ky)
     int ks = 1;
-    if (big >= 384) {
+    const int64_t big8 = (int64_t)g.B * ((g.h + 7) / 8) * ntx * ((Cout + 159) / 160);
+    if (big >= 384 && (big8 + 255) / 256 <= (big + 511) / 512) {
+        // 256x160 tiles, one per CU, in no more rounds than the 128x160 tiles need at two per
+        // CU (a round of either moves the same output; the larger tile reads fewer bytes)
+        p.kind = 3;
+        p.bm = 256;
+        p.bn = 160;
+        p.mtiles = (int)((int64_t)g.B * ((g.h + 7) / 8) * ntx);
+        p.ntiles = (Cout + 159) / 160;
+    } else if (big >= 384) {
         // enough 128x160 tiles for two per CU: shared ring, no K split
         p.kind = 1;
         p.bm = 128;
@@ -562,13 +608,16 @@ hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout,
     a.r0 = g.r0;
     a.M = g.B * g.h * g.W;
     a.ntx = (g.W + kTileTC - 1) / kTileTC;
-    a.nty = (g.h + (plan.kind == 1 ? 3 : 1)) / (plan.kind == 1 ? 4 : 2);
+    const int tr = plan.kind == 3 ? 8 : plan.kind == 1 ? 4 : 2;     // tile rows
+    a.nty = (g.h + tr - 1) / tr;
     a.mtiles = plan.mtiles;
     a.ntiles = plan.ntiles;
     a.kstages = plan.ktiles;
     a.ksplit = plan.ksplit;
     const unsigned grid = (unsigned)(plan.mtiles * plan.ntiles * plan.ksplit);
-    if (plan.kind == 1)
+    if (plan.kind == 3)
+        conv3x3_bf16_halo_tile8_kernel<<<grid, 512, 0, stream>>>(a);
+    else if (plan.kind == 1)
         conv3x3_bf16_halo_tile_kernel<<<grid, kThreads, 0, stream>>>(a);
     else
         conv3x3_bf16_halo_wave_kernel<<<grid, kThreads, 0, stream>>>(a);

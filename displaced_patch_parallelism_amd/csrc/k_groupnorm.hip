@@ -13,7 +13,7 @@
 // A block is vpt x R threads: thread (cv, r) owns channel vector cv (8 bf16
 // or 4 f32 channels) and token rows r, r+R, ... of the block's range, so
 // per-channel state stays in registers.
-//   1. gn_stats: 8 token loads in flight per thread; fp32 per-channel sums, reduced through LDS in a fixed order
+//   1. gn_stats: rounds of 8 token loads in flight per thread; fp32 per-channel sums, reduced through LDS in a fixed order
 //      to per-group (sum, sum of squares) partials [block][B][G]; at most 128
 //      blocks per batch, so the partials stay small.
 //   2. gn_apply: each block owns 4 token rows per thread (one round).  It issues the loads
@@ -64,11 +64,13 @@ __global__ void gn_stats_kernel(const void* __restrict__ x, int64_t tokens, int 
 #pragma unroll
     for (int e = 0; e < VEC; ++e) s[e] = q[e] = 0.f;
     const uint4* xb = (const uint4*)x + (int64_t)b * tokens * vpt + cv;
-    int64_t t = t0 + r;
-    for (; t + 7 * rows < t1; t += 8 * rows) {
+    // rounds of 8 token rows per thread, all 8 loads in flight (rows past the end read as
+    // zeros, which add nothing to either sum)
+    for (int64_t t = t0 + r; t < t1; t += 8 * rows) {
         uint4 v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = xb[(t + u * rows) * vpt];
+        for (int u = 0; u < 8; ++u)
+            v[u] = t + u * rows < t1 ? xb[(t + u * rows) * vpt] : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             float f[VEC];
@@ -78,15 +80,6 @@ __global__ void gn_stats_kernel(const void* __restrict__ x, int64_t tokens, int 
                 s[e] += f[e];
                 q[e] = fmaf(f[e], f[e], q[e]);
             }
-        }
-    }
-    for (; t < t1; t += rows) {
-        float f[VEC];
-        to_f32<BF16>(xb[t * vpt], f);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            s[e] += f[e];
-            q[e] = fmaf(f[e], f[e], q[e]);
         }
     }
     float* sh_s = sh;
@@ -296,10 +289,11 @@ GnPlan plan_groupnorm(const Geom& g, int G, bool bf16) {
         p.threads = p.vpt * p.rows;
     }
     const int64_t tokens = g.band_tokens();
-    // Statistics split (depends only on the geometry): at least 8 token rows per thread (one
-    // round of loads), at most 128 blocks per batch.
-    int64_t tpb = (int64_t)p.rows * 8;
-    if ((tokens + tpb - 1) / tpb > 128) tpb = (tokens + 127) / 128;
+    // Statistics split (depends only on the geometry): whole rounds of 8 token rows per thread,
+    // at most 128 blocks per batch.
+    const int64_t round = (int64_t)p.rows * 8;
+    int64_t tpb = round;
+    if ((tokens + tpb - 1) / tpb > 128) tpb = ((tokens + 127) / 128 + round - 1) / round * round;
     p.tok_per_blk = (int)tpb;
     p.nblk = (int)((tokens + tpb - 1) / tpb);
     // Apply split: one round of 4 token rows per thread, so every block's loads are in flight

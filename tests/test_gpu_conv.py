@@ -50,8 +50,11 @@ def test_ragged_bf16(B, H, W, cin, cout, P):
 
 
 @pytest.mark.parametrize("B,H,W,cin,cout,P", [
-    (1, 124, 500, 64, 288, 2),  # large-map tiles: 62 = 15*4 + 2 rows, 500 = 15*32 + 20 columns, 288 = 160 + 128
-    (2, 96, 254, 64, 320, 2),   # large-map tiles over two batch images, ragged columns
+    # 256x160 tiles (8 rows): 62 = 7*8 + 6 rows, 500 = 15*32 + 20 columns, 288 = 160 + 128
+    (1, 124, 500, 64, 288, 2),
+    (2, 96, 254, 64, 320, 2),   # 256x160 tiles over two batch images, ragged columns
+    # 128x160 tiles (4 rows): 12-row bands need a second round of 8-row tiles
+    (2, 24, 1152, 64, 320, 2),
 ])
 def test_large_map_tiles_bf16(B, H, W, cin, cout, P):
     for i in range(P):
