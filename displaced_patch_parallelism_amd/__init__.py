@@ -70,6 +70,8 @@ def lib():
             "dp_groupnorm_async": [pp, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "dp_conv3x3_halo_ws": [pp, i32, i32, psz],
             "dp_conv3x3_halo": [pp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp],
+            "dp_conv3x3_pack_weights": [i32, i32, i32, vp, vp, vp],
+            "dp_conv3x3_halo_packed": [pp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp],
             "dp_attention_splice_ws": [pp, i32, i32, i32, psz],
             "dp_attention_splice": [pp, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "dp_stale_update": [pp, i32, vp, vp, vp],
@@ -79,6 +81,8 @@ def lib():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = ctypes.c_int
+        L.dp_conv3x3_packed_weights_bytes.argtypes = [i32, i32]
+        L.dp_conv3x3_packed_weights_bytes.restype = sz
         L.dp_last_error.restype = ctypes.c_char_p
         L.dp_last_error.argtypes = []
         L.dp_version.restype = ctypes.c_char_p
@@ -228,6 +232,45 @@ def dp_conv3x3_halo(patch: Patch, x_patch, x_stale, w, bias=None, y_patch=None, 
     _check(lib().dp_conv3x3_halo(_cpatch(p), dt, cout, x_patch.data_ptr(), x_stale.data_ptr(), w.data_ptr(),
                                  None if bias is None else bias.data_ptr(), y_patch.data_ptr(), wptr, wbytes,
                                  _stream(dev)))
+    return y_patch
+
+
+def dp_conv3x3_pack_weights(w, w_packed=None):
+    """bf16 conv weights [Cout][3][3][Cin] -> the packed layout [3][Cin/32][3][Cout][32] that
+    dp_conv3x3_halo_packed reads as whole cache lines (pack once; weights are constant)."""
+    torch = _torch()
+    cout, cin = int(w.shape[0]), int(w.shape[3])
+    _ptr(w, "w", (cout, 3, 3, cin))
+    if cin % 32:
+        raise DpError(DP_ERR_UNSUPPORTED, f"packed weights need Cin % 64 == 0 (Cin={cin})")
+    shape = (3, cin // 32, 3, cout, 32)
+    if w_packed is None:
+        w_packed = torch.empty(shape, dtype=w.dtype, device=w.device)
+    _ptr(w_packed, "w_packed", shape, w.dtype, w.device)
+    _check(lib().dp_conv3x3_pack_weights(_dtype_code(w), cin, cout, w.data_ptr(), w_packed.data_ptr(),
+                                         _stream(w.device)))
+    return w_packed
+
+
+def dp_conv3x3_halo_packed(patch: Patch, x_patch, x_stale, w_packed, bias=None, y_patch=None, ws=None):
+    """dp_conv3x3_halo on packed weights (from dp_conv3x3_pack_weights); bitwise the same result."""
+    torch = _torch()
+    p = Patch(*patch)
+    dt = _dtype_code(x_patch)
+    dev = x_patch.device
+    cout = int(w_packed.shape[3])
+    _ptr(x_patch, "x_patch", (p.B, p.h, p.W, p.C))
+    _ptr(x_stale, "x_stale", (p.B, p.H, p.W, p.C), x_patch.dtype, dev)
+    _ptr(w_packed, "w_packed", (3, p.C // 32, 3, cout, 32), x_patch.dtype, dev)
+    _ptr(bias, "bias", (cout,), torch.float32, dev)
+    if y_patch is None:
+        y_patch = torch.empty((p.B, p.h, p.W, cout), dtype=x_patch.dtype, device=dev)
+    _ptr(y_patch, "y_patch", (p.B, p.h, p.W, cout), x_patch.dtype, dev)
+    need = workspace_bytes("conv", p, dt, cout)
+    wptr, wbytes = _workspace(need, dev, ws)
+    _check(lib().dp_conv3x3_halo_packed(_cpatch(p), dt, cout, x_patch.data_ptr(), x_stale.data_ptr(),
+                                        w_packed.data_ptr(), None if bias is None else bias.data_ptr(),
+                                        y_patch.data_ptr(), wptr, wbytes, _stream(dev)))
     return y_patch
 
 

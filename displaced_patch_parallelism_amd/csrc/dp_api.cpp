@@ -210,14 +210,19 @@ dp_status dp_conv3x3_halo_ws(const dp_patch* p, dp_dtype dtype, int32_t Cout, si
     return ok();
 }
 
-dp_status dp_conv3x3_halo(const dp_patch* p, dp_dtype dtype, int32_t Cout, const void* x_patch,
-                          const void* x_stale, const void* w, const float* bias, void* y_patch,
-                          void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+dp_status conv_call(const dp_patch* p, dp_dtype dtype, int32_t Cout, const void* x_patch, const void* x_stale,
+                    const void* w, bool w_packed, const float* bias, void* y_patch, void* ws, size_t ws_bytes,
+                    hipStream_t stream, const char* name) {
     dp::Geom g;
     DP_TRY(check_conv(p, dtype, Cout, &g));
+    if (w_packed && dtype != DP_BF16) return fail(DP_ERR_UNSUPPORTED, "%s: packed weights are bf16 only", name);
     DP_NEED(x_patch, "x_patch");
     DP_NEED(x_stale, "x_stale");
-    DP_NEED(w, "w");
+    DP_NEED(w, w_packed ? "w_packed" : "w");
     DP_OPT(bias, "bias");
     DP_NEED(y_patch, "y_patch");
     const dp::ConvPlan plan = dp::plan_conv(g, Cout, dtype == DP_BF16);
@@ -236,9 +241,46 @@ dp_status dp_conv3x3_halo(const dp_patch* p, dp_dtype dtype, int32_t Cout, const
     if (plan.ws_bytes && (overlaps(ws, plan.ws_bytes, x_patch, in_band) || overlaps(ws, plan.ws_bytes, x_stale, in_map) ||
                           overlaps(ws, plan.ws_bytes, w, w_bytes)))
         return fail(DP_ERR_ARG, "workspace overlaps an input");
-    return hip_status(dp::launch_conv(g, plan, dtype == DP_BF16, Cout, x_patch, x_stale, w, bias, y_patch, ws,
-                                      stream),
-                      "dp_conv3x3_halo launch");
+    return hip_status(dp::launch_conv(g, plan, dtype == DP_BF16, Cout, x_patch, x_stale, w, w_packed, bias,
+                                      y_patch, ws, stream),
+                      name);
+}
+
+}  // namespace
+
+extern "C" {
+
+dp_status dp_conv3x3_halo(const dp_patch* p, dp_dtype dtype, int32_t Cout, const void* x_patch,
+                          const void* x_stale, const void* w, const float* bias, void* y_patch,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+    return conv_call(p, dtype, Cout, x_patch, x_stale, w, false, bias, y_patch, ws, ws_bytes, stream,
+                     "dp_conv3x3_halo launch");
+}
+
+size_t dp_conv3x3_packed_weights_bytes(int32_t Cin, int32_t Cout) {
+    if (Cin < 1 || Cout < 1) return 0;
+    return (size_t)Cout * 9 * Cin * 2;
+}
+
+dp_status dp_conv3x3_pack_weights(dp_dtype dtype, int32_t Cin, int32_t Cout, const void* w, void* w_packed,
+                                  hipStream_t stream) {
+    if (dtype != DP_BF16) return fail(DP_ERR_UNSUPPORTED, "dp_conv3x3_pack_weights: bf16 only");
+    if (Cin < 1 || Cout < 1) return fail(DP_ERR_ARG, "Cin=%d Cout=%d must be >= 1", Cin, Cout);
+    if (Cin % 64 != 0 || Cout % 32 != 0)
+        return fail(DP_ERR_UNSUPPORTED, "packed weights need Cin %% 64 == 0 and Cout %% 32 == 0 (Cin=%d Cout=%d)",
+                    Cin, Cout);
+    DP_NEED(w, "w");
+    DP_NEED(w_packed, "w_packed");
+    const size_t bytes = dp_conv3x3_packed_weights_bytes(Cin, Cout);
+    if (overlaps(w, bytes, w_packed, bytes)) return fail(DP_ERR_ARG, "w_packed overlaps w");
+    return hip_status(dp::launch_conv_pack(Cin, Cout, w, w_packed, stream), "dp_conv3x3_pack_weights launch");
+}
+
+dp_status dp_conv3x3_halo_packed(const dp_patch* p, dp_dtype dtype, int32_t Cout, const void* x_patch,
+                                 const void* x_stale, const void* w_packed, const float* bias, void* y_patch,
+                                 void* ws, size_t ws_bytes, hipStream_t stream) {
+    return conv_call(p, dtype, Cout, x_patch, x_stale, w_packed, true, bias, y_patch, ws, ws_bytes, stream,
+                     "dp_conv3x3_halo_packed launch");
 }
 
 dp_status dp_attention_splice_ws(const dp_patch* p, dp_dtype dtype, int32_t heads, int32_t head_dim,

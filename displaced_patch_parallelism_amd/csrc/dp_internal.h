@@ -53,8 +53,10 @@ struct ConvPlan {
 };
 ConvPlan plan_conv(const Geom& g, int Cout, bool bf16);
 hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout, const void* x_patch,
-                       const void* x_stale, const void* w, const float* bias, void* y, void* ws,
+                       const void* x_stale, const void* w, bool w_packed, const float* bias, void* y, void* ws,
                        hipStream_t stream);
+// bf16 weights [Cout][3][3][Cin] -> packed [3][Cin/32][3][Cout][32] (Cin % 32 == 0)
+hipError_t launch_conv_pack(int Cin, int Cout, const void* w, void* w_packed, hipStream_t stream);
 
 // ---- attention over spliced K/V ------------------------------------------
 struct AttnPlan {

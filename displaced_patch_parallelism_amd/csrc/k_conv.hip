@@ -61,6 +61,7 @@ struct ConvArgs {
     int mtiles, ntiles;  // pixel tiles (B * nty * ntx), channel tiles
     int kstages;         // K stages (cc, ky): 32 input channels of one kernel row; 3 * Cin / 32
     int ksplit;          // K partitions across workgroups
+    int wpacked;         // weights in the packed layout [ky][Cin/32][kx][Cout][32] (else [Cout][3][3][Cin])
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -131,7 +132,16 @@ __device__ __forceinline__ uint32_t b_slot_offset(const ConvArgs& a, int n0, int
     const int c = (s & 3) ^ slot_swz(nr);
     int co = n0 + n;
     if (co >= a.Cout) co = a.Cout - 1;      // clamped rows feed columns that are never stored
+    if (a.wpacked) return (uint32_t)((((int64_t)kx * a.Cout + co) * 32 + c * 8) * 2);
     return (uint32_t)((((int64_t)co * 9 + kx) * a.Cin + c * 8) * 2);
+}
+
+// First byte of stage (cc, ky)'s weights; b_slot_offset is relative to it.  In the packed
+// layout a stage is one contiguous block of 3 x Cout rows of 64 bytes, so the 16 tap rows one
+// direct-to-LDS load fills are 1 KB of consecutive memory (whole cache lines).
+__device__ __forceinline__ const char* stage_weights(const ConvArgs& a, int cc, int ky) {
+    if (a.wpacked) return (const char*)a.w + ((int64_t)ky * (a.Cin / 32) + cc) * 3 * a.Cout * 64;
+    return (const char*)a.w + ((int64_t)3 * ky * a.Cin + cc * 32) * 2;
 }
 
 // The 60 MFMAs of one stage for a wave's 64 pixels (tile rows tr0, tr0+1, 32 columns) x 80
@@ -240,7 +250,7 @@ __device__ __forceinline__ void conv_tile_body(const ConvArgs& a, char* smem) {
                                                      16, 0, 0);                                    \
             }                                                                                       \
         }                                                                                           \
-        const char* wk_ = (const char*)a.w + ((int64_t)3 * (KY) * a.Cin + (CC) * 32) * 2;          \
+        const char* wk_ = stage_weights(a, (CC), (KY));                                           \
         _Pragma("unroll") for (int q = 0; q < BQ; ++q) {                                            \
             const int j_ = wave + NW * q;                                                           \
             if (j_ < S::B_LOADS)                                                                    \
@@ -381,7 +391,7 @@ __global__ __launch_bounds__(256) void conv3x3_bf16_halo_wave_kernel(ConvArgs a)
             if (j < S::A_LOADS - 1 || lane < S::A_TAIL)                                             \
                 __builtin_amdgcn_global_load_lds((const void*)g_, (lds_void*)(st_ + j * 1024), 16, 0, 0); \
         }                                                                                           \
-        const char* wk_ = (const char*)a.w + ((int64_t)3 * (KY) * a.Cin + (CC) * 32) * 2;          \
+        const char* wk_ = stage_weights(a, (CC), (KY));                                           \
         _Pragma("unroll") for (int j = 0; j < S::B_LOADS; ++j)                                      \
             __builtin_amdgcn_global_load_lds((const void*)(wk_ + bo[j]),                           \
                                              (lds_void*)(st_ + S::B_OFF + j * 1024), 16, 0, 0);     \
@@ -532,6 +542,23 @@ __global__ __launch_bounds__(256) void conv3x3_f32_direct_kernel(const float* __
 
 }  // namespace
 
+// Packed weights: chunk (co, ky, kx, c8) of 8 channels of w[Cout][3][3][Cin] goes to
+// wp[ky][c8 / 4][kx][co][(c8 % 4) * 8 ..].  One thread per 16-byte chunk.
+__global__ __launch_bounds__(256) void conv_pack_weights_kernel(const uint4* __restrict__ w, uint4* __restrict__ wp,
+                                                                int Cin, int Cout) {
+    const int64_t total = (int64_t)Cout * 9 * (Cin / 8);
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const int c8n = Cin / 8;
+    const int c8 = (int)(i % c8n);
+    const int64_t rest = i / c8n;               // (co * 3 + ky) * 3 + kx
+    const int kx = (int)(rest % 3);
+    const int ky = (int)((rest / 3) % 3);
+    const int co = (int)(rest / 9);
+    const int64_t o = ((((int64_t)ky * (Cin / 32) + c8 / 4) * 3 + kx) * Cout + co) * 4 + (c8 % 4);
+    wp[o] = w[i];
+}
+
 ConvPlan plan_conv(const Geom& g, int Cout, bool bf16) {
     ConvPlan p{};
     if (!bf16) {
@@ -581,8 +608,16 @@ ConvPlan plan_conv(const Geom& g, int Cout, bool bf16) {
     return p;
 }
 
+hipError_t launch_conv_pack(int Cin, int Cout, const void* w, void* w_packed, hipStream_t stream) {
+    const int64_t total = (int64_t)Cout * 9 * (Cin / 8);
+    if (total == 0) return hipSuccess;
+    conv_pack_weights_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>((const uint4*)w, (uint4*)w_packed,
+                                                                                Cin, Cout);
+    return hipGetLastError();
+}
+
 hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout, const void* x_patch,
-                       const void* x_stale, const void* w, const float* bias, void* y, void* ws,
+                       const void* x_stale, const void* w, bool w_packed, const float* bias, void* y, void* ws,
                        hipStream_t stream) {
     if (!bf16) {
         const int64_t total = (int64_t)g.B * g.h * g.W * Cout;
@@ -614,6 +649,7 @@ hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout,
     a.ntiles = plan.ntiles;
     a.kstages = plan.ktiles;
     a.ksplit = plan.ksplit;
+    a.wpacked = w_packed ? 1 : 0;
     const unsigned grid = (unsigned)(plan.mtiles * plan.ntiles * plan.ksplit);
     if (plan.kind == 3)
         conv3x3_bf16_halo_tile8_kernel<<<grid, 512, 0, stream>>>(a);

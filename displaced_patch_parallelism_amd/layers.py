@@ -21,8 +21,9 @@ from typing import Dict, List, Optional, Sequence, Tuple
 
 import torch
 
-from . import (Patch, _dtype_code, dp_attention_splice, dp_conv3x3_halo, dp_groupnorm_async, dp_linear,
-               dp_stale_update, dp_stats_update, workspace_bytes)
+from . import (Patch, _dtype_code, dp_attention_splice, dp_conv3x3_halo, dp_conv3x3_halo_packed,
+               dp_conv3x3_pack_weights, dp_groupnorm_async, dp_linear, dp_stale_update, dp_stats_update,
+               workspace_bytes)
 
 
 def torch_dtype(name):
@@ -51,6 +52,8 @@ class DisplacedLayer:
         self.dt = torch_dtype(cfg.dtype)
         self.convs = [(torch.as_tensor(w).to(self.device, self.dt).contiguous(),
                        torch.as_tensor(b).to(self.device, torch.float32).contiguous()) for w, b in convs]
+        # bf16 conv weights are packed once into the layout the kernels read as whole cache lines
+        self.wpacked = [dp_conv3x3_pack_weights(w) if self.dt == torch.bfloat16 else None for w, _ in self.convs]
         # per attn_proj step: (wq, bq, wk, bk, wv, bv, wo, bo), weights in the storage type
         self.projs = [tuple(torch.as_tensor(a).to(self.device, self.dt if j % 2 == 0 else torch.float32).contiguous()
                             for j, a in enumerate(pr)) for pr in (projs or [])]
@@ -95,6 +98,13 @@ class DisplacedLayer:
     def _tok(self, t):
         return t.reshape(t.shape[0], -1, t.shape[-1])
 
+    def _conv(self, p, x_patch, stale, j, y_patch=None, ws=None):
+        """The layer's j-th conv (on its packed weights when they exist)."""
+        w, b = self.convs[j]
+        if self.wpacked[j] is not None:
+            return dp_conv3x3_halo_packed(p, x_patch, stale, self.wpacked[j], b, y_patch=y_patch, ws=ws)
+        return dp_conv3x3_halo(p, x_patch, stale, w, b, y_patch=y_patch, ws=ws)
+
     # ---- one patch, displaced ------------------------------------------------
     def calls(self, x_patch, i, gn_mode="corrected", update_state=True):
         """Patch i's displaced layer step as a list of (name, launch, output): each launch
@@ -120,10 +130,9 @@ class DisplacedLayer:
                 fn = (lambda h=h, out=out, stats=stats, act=act: dp_groupnorm_async(
                     p, h, c.G, self.table, c.eps, gn_mode, act, fresh_stats_out=stats, y_patch=out, ws=self.ws))
             elif s == "conv":
-                w, b = self.convs[conv_i]
+                fn = (lambda h=h, out=out, k=k, j=conv_i: self._conv(p, h, self.maps[k], j, y_patch=out,
+                                                                  ws=self.ws))
                 conv_i += 1
-                fn = (lambda h=h, out=out, k=k, w=w, b=b: dp_conv3x3_halo(
-                    p, h, self.maps[k], w, b, y_patch=out, ws=self.ws))
             elif s == "attn":
                 tok, st, o = self._tok(h), self._tok(self.maps[k]), self._tok(out)
                 fn = (lambda tok=tok, st=st, o=o: dp_attention_splice(
@@ -286,19 +295,18 @@ class DisplacedLayer:
             else:
                 for j in range(c.P):
                     dp_stale_update(self.patch(j), self.band(h_full, j), self.maps[k])
-                if s == "conv":
-                    w, b = self.convs[conv_i]
-                    conv_i += 1
                 for j in range(c.P):
                     pj = self.patch(j)
                     xb = self.band(h_full, j)
                     if s == "conv":
-                        o = dp_conv3x3_halo(pj, xb, self.maps[k], w, b)
+                        o = self._conv(pj, xb, self.maps[k], conv_i)
                     else:
                         tok = self._tok(xb)
                         st = self._tok(self.maps[k])
                         o = dp_attention_splice(pj, c.heads, tok, tok, tok, st, st).reshape(xb.shape)
                     dp_stale_update(pj, o, out_full)
+                if s == "conv":
+                    conv_i += 1
             outs.append(out_full)
             h_full = out_full
         return outs

@@ -12,7 +12,8 @@
  *   dp_groupnorm_async   corrected asynchronous GroupNorm (fresh local
  *                        statistics + stale statistics of the other patches)
  *   dp_conv3x3_halo      3x3 conv whose rows above/below the patch come from
- *                        the previous step's (stale) map
+ *                        the previous step's (stale) map (and a variant on
+ *                        weights packed once by dp_conv3x3_pack_weights)
  *   dp_attention_splice  attention: queries from the fresh patch, keys and
  *                        values from the full stale map with the patch
  *                        spliced in
@@ -155,6 +156,37 @@ dp_status dp_conv3x3_halo_ws(const dp_patch* p, dp_dtype dtype, int32_t Cout, si
 dp_status dp_conv3x3_halo(const dp_patch* p, dp_dtype dtype, int32_t Cout, const void* x_patch,
                           const void* x_stale, const void* w, const float* bias, void* y_patch,
                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * dp_conv3x3_pack_weights / dp_conv3x3_halo_packed -- the same convolution
+ * with the weights in a packed layout the kernels read as whole cache lines.
+ *
+ * Source: as dp_conv3x3_halo (study.space page, Method); the layout is an
+ * implementation detail of the bf16 kernels and does not change the result:
+ * dp_conv3x3_halo_packed(w_packed) is bitwise equal to dp_conv3x3_halo(w).
+ * Packed layout (bf16): element (co, ky, kx, ci) of w[Cout][3][3][Cin] at
+ *   w_packed[ky][ci / 32][kx][co][ci % 32],
+ * i.e. each (kernel row, 32-channel chunk) is one contiguous block of
+ * 3 x Cout rows of 64 bytes.  Weights are constant across steps, so a layer
+ * packs them once.
+ *
+ *   dp_conv3x3_packed_weights_bytes  bytes of w_packed (9*Cin*Cout*2), or 0
+ *                                    when Cin or Cout < 1
+ *   dp_conv3x3_pack_weights          w [Cout][3][3][Cin] bf16 -> w_packed
+ *                                    (caller-owned, that many bytes, must not
+ *                                    overlap w); enqueued on `stream`
+ *   dp_conv3x3_halo_packed           arguments and errors as dp_conv3x3_halo,
+ *                                    with w_packed in place of w
+ * bf16 only (DP_ERR_UNSUPPORTED for DP_F32); Cin % 64 == 0, Cout % 32 == 0.
+ * ---------------------------------------------------------------------- */
+size_t dp_conv3x3_packed_weights_bytes(int32_t Cin, int32_t Cout);
+
+dp_status dp_conv3x3_pack_weights(dp_dtype dtype, int32_t Cin, int32_t Cout, const void* w, void* w_packed,
+                                  hipStream_t stream);
+
+dp_status dp_conv3x3_halo_packed(const dp_patch* p, dp_dtype dtype, int32_t Cout, const void* x_patch,
+                                 const void* x_stale, const void* w_packed, const float* bias, void* y_patch,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * dp_attention_splice -- self-attention of patch i over spliced K/V.

@@ -142,6 +142,31 @@ def test_conv_and_attention_overlap_errors():
                                  FAKE2 * 2, FAKE2 * 4, 1 << 24, None) == dp.DP_ERR_ARG
 
 
+def test_packed_conv_weights_rejects():
+    L = dp.lib()
+    assert L.dp_conv3x3_packed_weights_bytes(320, 640) == 9 * 320 * 640 * 2
+    assert L.dp_conv3x3_packed_weights_bytes(0, 640) == 0
+    # bf16 only; Cin % 64, Cout % 32; pointers; overlap
+    assert L.dp_conv3x3_pack_weights(dp.DP_F32, 64, 64, FAKE, FAKE2, None) == dp.DP_ERR_UNSUPPORTED
+    assert L.dp_conv3x3_pack_weights(dp.DP_BF16, 96, 64, FAKE, FAKE2, None) == dp.DP_ERR_UNSUPPORTED
+    assert L.dp_conv3x3_pack_weights(dp.DP_BF16, 64, 48, FAKE, FAKE2, None) == dp.DP_ERR_UNSUPPORTED
+    assert L.dp_conv3x3_pack_weights(dp.DP_BF16, 0, 64, FAKE, FAKE2, None) == dp.DP_ERR_ARG
+    assert L.dp_conv3x3_pack_weights(dp.DP_BF16, 64, 64, None, FAKE2, None) == dp.DP_ERR_ARG
+    assert L.dp_conv3x3_pack_weights(dp.DP_BF16, 64, 64, FAKE, None, None) == dp.DP_ERR_ARG
+    assert L.dp_conv3x3_pack_weights(dp.DP_BF16, 64, 64, FAKE, FAKE + 64, None) == dp.DP_ERR_ARG
+    assert "overlap" in L.dp_last_error().decode()
+    # the packed conv validates like the plain one, and is bf16 only
+    p = dp._cpatch(dp.Patch(1, 8, 8, 64, 2, 0))
+    assert L.dp_conv3x3_halo_packed(p, dp.DP_F32, 64, FAKE, FAKE2, FAKE2 * 2, None, FAKE2 * 3, FAKE2 * 4,
+                                    1 << 24, None) == dp.DP_ERR_UNSUPPORTED
+    assert L.dp_conv3x3_halo_packed(p, dp.DP_BF16, 64, FAKE, FAKE2, FAKE2 * 2, None, FAKE2 + 64, FAKE2 * 4,
+                                    1 << 24, None) == dp.DP_ERR_ARG
+    assert "overlap" in L.dp_last_error().decode()
+    assert L.dp_conv3x3_halo_packed(p, dp.DP_BF16, 64, FAKE, FAKE2, None, None, FAKE2 * 3, FAKE2 * 4,
+                                    1 << 24, None) == dp.DP_ERR_ARG
+    assert "w_packed" in L.dp_last_error().decode()
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)

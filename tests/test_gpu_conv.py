@@ -16,16 +16,37 @@ pytestmark = pytest.mark.gpu
 
 
 def run_case(B, H, W, cin, cout, P, i, dtype, seed=0, bias=True):
+    """Both entry points (plain weights; for bf16 also the packed layout) against the oracle; the
+    packed call must give bitwise the plain call's output."""
     case = synth.conv_case(B, H, W, cin, cout, dtype, seed)
     h = H // P
     xb = case.fresh[:, i * h:(i + 1) * h]
     b = case.bias if bias else None
     ref = oracle.conv3x3_halo(xb, case.stale, case.w, b, P, i)
-    y = dp.dp_conv3x3_halo(dp.Patch(B, H, W, cin, P, i), gpu(xb, dtype), gpu(case.stale, dtype),
-                           gpu(case.w, dtype), None if b is None else gpu(b, "f32"))
+    patch = dp.Patch(B, H, W, cin, P, i)
+    xg, sg, wg = gpu(xb, dtype), gpu(case.stale, dtype), gpu(case.w, dtype)
+    bg = None if b is None else gpu(b, "f32")
+    y = dp.dp_conv3x3_halo(patch, xg, sg, wg, bg)
     torch.cuda.synchronize()
     assert_parity(host(y), ref, dtype, f"conv {dtype} B{B} {H}x{W} {cin}->{cout} P{P} i{i}")
+    if dtype == "bf16":
+        yp = dp.dp_conv3x3_halo_packed(patch, xg, sg, dp.dp_conv3x3_pack_weights(wg), bg)
+        torch.cuda.synchronize()
+        assert torch.equal(yp.view(torch.int16), y.view(torch.int16)), "packed-weight conv differs"
     return y
+
+
+@pytest.mark.parametrize("cin,cout", [(64, 32), (320, 320), (128, 352)])
+def test_pack_weights_layout(cin, cout):
+    """w_packed[ky][ci // 32][kx][co][ci % 32] = w[co][ky][kx][ci], bit for bit."""
+    rng = np.random.default_rng(cin + cout)
+    w = rng.standard_normal((cout, 3, 3, cin), dtype=np.float32)
+    wg = gpu(w, "bf16")
+    wp = dp.dp_conv3x3_pack_weights(wg)
+    torch.cuda.synchronize()
+    bits = wg.view(torch.int16).cpu().numpy()
+    expect = bits.reshape(cout, 3, 3, cin // 32, 32).transpose(1, 3, 2, 0, 4)
+    assert np.array_equal(wp.view(torch.int16).cpu().numpy(), expect)
 
 
 @pytest.mark.parametrize("name", [n for n, c in CONFIGS.items() if c.has_conv])
