@@ -59,7 +59,8 @@ def call_flops(cfg, name):
 
 def kernel_name(op, cfg, cout=None):
     """Main kernel of a call: the bf16 conv picks its tile kernel from the map size (the
-    library's plan: 128x160 tiles when at least 384 of them exist, else 64x80 tiles)."""
+    library's plan: 256x160 tiles when at least 384 128x160 tiles exist and the larger tiles
+    need no more rounds, else 128x160 tiles, else 64x80 tiles)."""
     if op == "attn":
         return "attn_bf16_d64_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel"
     if op in PROJ_CALLS:
@@ -69,7 +70,10 @@ def kernel_name(op, cfg, cout=None):
             return "conv3x3_f32_direct_kernel"
         cout = cout or cfg.C
         big = cfg.B * -(-cfg.h // 4) * -(-cfg.W // 32) * -(-cout // 160)
-        return "conv3x3_bf16_halo_tile_kernel" if big >= 384 else "conv3x3_bf16_halo_wave_kernel"
+        big8 = cfg.B * -(-cfg.h // 8) * -(-cfg.W // 32) * -(-cout // 160)
+        if big >= 384 and -(-big8 // 256) <= -(-big // 512):
+            return "conv3x3_bf16_halo_tile8_kernel"
+        return "conv3x3_bf16_halo_tile_kernel" if big >= 384 else "conv3x3_bf16_halo_wave8_kernel"
     return op
 
 

@@ -103,6 +103,10 @@ dp_status check_conv(const dp_patch* p, dp_dtype dt, int32_t Cout, dp::Geom* g) 
     if (dt == DP_BF16 && (g->C % 64 != 0 || Cout % 32 != 0))
         return fail(DP_ERR_UNSUPPORTED, "bf16 conv needs Cin %% 64 == 0 and Cout %% 32 == 0 (Cin=%d Cout=%d)",
                     g->C, Cout);
+    // the bf16 kernels address one batch image and the weights with 32-bit offsets
+    if (dt == DP_BF16 && ((int64_t)g->H * g->W * g->C >= (int64_t)1 << 31 ||
+                          (int64_t)9 * g->C * Cout * 2 >= (int64_t)1 << 31))
+        return fail(DP_ERR_UNSUPPORTED, "bf16 conv needs H*W*Cin < 2^31 elements and weights < 2 GiB");
     return DP_OK;
 }
 

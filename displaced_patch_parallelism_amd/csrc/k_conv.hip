@@ -30,12 +30,12 @@
 //   Large maps: 128x160 tiles (4 rows x 32 columns), one LDS ring shared by
 //   4 waves (2x2 of 64 pixels x 80 channels), two workgroups per CU; or, when
 //   they fill the GPU in no more rounds, 256x160 tiles (8 rows) with 8 waves,
-//   one workgroup per CU and a 3-stage ring.  Small
-//   maps: 64x80 tiles (2 rows x 32 columns) whose 4 waves each take a quarter
-//   of K through a private ring and are summed through LDS in wave order; K is
-//   also split across workgroups until about 256 of them run, the fp32
-//   partials summed in split order by a second kernel.  Every sum has a fixed
-//   order, so results are deterministic.
+//   one workgroup per CU and a 3-stage ring.  Small maps: 64x80 tiles (2 rows
+//   x 32 columns) whose 8 waves each take an eighth of K through a private
+//   buffer and are summed through LDS in wave order; K is also split across
+//   workgroups until about 256 of them run, the fp32 partials summed in split
+//   order by a second kernel.  Every sum has a fixed order, so results are
+//   deterministic.
 // f32 path: one thread per output element (correctness path for small maps).
 
 #include "dp_device.h"
@@ -99,7 +99,8 @@ __device__ __forceinline__ int xcd_order(int b, int total) {
 }
 
 // Source of A slot s of a stage of tile (bb, ty0, tx0), for kernel rows ky = 0, 1, 2:
-// pointer to channel chunk c of the pixel, or null where the pixel is zero padding.
+// pointer to channel chunk c of the pixel, or null where the pixel is zero padding.  Offsets
+// inside one batch image are 32-bit (the host rejects images of 2^31 or more elements).
 template <int TR>
 __device__ __forceinline__ void resolve_a_slot(const ConvArgs& a, int bb, int ty0, int tx0, int s,
                                                const uint16_t*& p0, const uint16_t*& p1,
@@ -109,31 +110,37 @@ __device__ __forceinline__ void resolve_a_slot(const ConvArgs& a, int bb, int ty
     const int t = p / HWC, u = p - t * HWC;
     const int c = (s & 3) ^ slot_swz(p);
     const int x = tx0 + u - 1;
+    const bool xok = s < TR * HWC * 4 && x >= 0 && x < a.W;
+    const uint16_t* fb = a.xp + (int64_t)bb * a.h * a.W * a.Cin;     // this batch image's band
+    const uint16_t* sb = a.xs + (int64_t)bb * a.H * a.W * a.Cin;     // and stale map
     const uint16_t* q[3];
 #pragma unroll
     for (int ky = 0; ky < 3; ++ky) {
         const int r = a.r0 + ty0 + t + ky - 1;    // image row feeding tile row t through kernel row ky
-        const bool ok = s < TR * HWC * 4 && x >= 0 && x < a.W && r >= 0 && r < a.H;
+        const bool ok = xok && r >= 0 && r < a.H;
         const bool fresh = r >= a.r0 && r < a.r0 + a.h;
-        const int64_t fo = (((int64_t)bb * a.h + (r - a.r0)) * a.W + x) * a.Cin;
-        const int64_t so = (((int64_t)bb * a.H + r) * a.W + x) * a.Cin;
-        q[ky] = ok ? (fresh ? a.xp + fo : a.xs + so) + c * 8 : nullptr;
+        const uint32_t pix = (uint32_t)((fresh ? r - a.r0 : r) * a.W + x);
+        const uint32_t off = pix * (uint32_t)a.Cin + (uint32_t)(c * 8);
+        q[ky] = ok ? (fresh ? fb : sb) + off : nullptr;
     }
     p0 = q[0];
     p1 = q[1];
     p2 = q[2];
 }
 
-// Byte offset of B slot s (tap row kx*BN + n, chunk) from the weights of kernel row 0, channel 0.
+// Byte offset of this lane's slot in B load j (tap rows 16j .. 16j+15, 4 chunks each) from the
+// stage's weights.  BN is a multiple of 16, so the load's tap kx and the rows' swizzle
+// ((16j + lane/4) >> 1) & 3 = (lane >> 3) & 3 do not depend on the row.
 template <int BN>
-__device__ __forceinline__ uint32_t b_slot_offset(const ConvArgs& a, int n0, int s) {
-    const int nr = s >> 2;
-    const int kx = nr / BN, n = nr - kx * BN;
-    const int c = (s & 3) ^ slot_swz(nr);
+__device__ __forceinline__ uint32_t b_slot_offset(const ConvArgs& a, int n0, int j, int lane) {
+    static_assert(BN % 16 == 0, "B loads cover whole 16-row groups of one tap");
+    const int kx = (16 * j) / BN;
+    const int n = 16 * j - kx * BN + (lane >> 2);
+    const int c = (lane & 3) ^ ((lane >> 3) & 3);
     int co = n0 + n;
     if (co >= a.Cout) co = a.Cout - 1;      // clamped rows feed columns that are never stored
-    if (a.wpacked) return (uint32_t)((((int64_t)kx * a.Cout + co) * 32 + c * 8) * 2);
-    return (uint32_t)((((int64_t)co * 9 + kx) * a.Cin + c * 8) * 2);
+    if (a.wpacked) return (uint32_t)(((kx * a.Cout + co) * 32 + c * 8) * 2);
+    return (uint32_t)(((co * 9 + kx) * a.Cin + c * 8) * 2);
 }
 
 // First byte of stage (cc, ky)'s weights; b_slot_offset is relative to it.  In the packed
@@ -232,7 +239,7 @@ __device__ __forceinline__ void conv_tile_body(const ConvArgs& a, char* smem) {
     }
     uint32_t bo[BQ];
 #pragma unroll
-    for (int q = 0; q < BQ; ++q) bo[q] = b_slot_offset<BN>(a, n0, (wave + NW * q) * 64 + lane);
+    for (int q = 0; q < BQ; ++q) bo[q] = b_slot_offset<BN>(a, n0, wave + NW * q, lane);
     // this wave's loads per stage (the deal is uneven when NW does not divide the load counts)
     const int nloads = (S::A_LOADS - wave + NW - 1) / NW + (S::B_LOADS - wave + NW - 1) / NW;
 
@@ -343,17 +350,20 @@ __global__ __launch_bounds__(512, 1) void conv3x3_bf16_halo_tile8_kernel(ConvArg
 }
 
 // ---------------------------------------------------------------------------
-// Small maps: tile 2 rows x 32 columns x 80 channels.  Each of the 4 waves takes a quarter of
-// the workgroup's stages and streams them through its own 2-stage ring (2 x 19.25 KB) -- no
-// barrier in the main loop; the four accumulators are then added through LDS in wave order
-// and written as bf16 (+bias) or, when K is also split across workgroups, as fp32 partials.
+// Small maps: tile 2 rows x 32 columns x 80 channels with K split over 8 waves (two per SIMD),
+// and across workgroups until about 256 of them run (fp32 partials, summed in split order by
+// conv_splitk_reduce_kernel).  Each wave streams its stages through a single private buffer: it reads all of
+// a stage's operand fragments into registers, then issues the next stage's loads into the freed
+// buffer and runs the stage's 60 MFMAs.  A wave stalls while the CU's vector memory path takes
+// its loads; the other wave on its SIMD multiplies meanwhile.  The 8 accumulators are summed
+// through LDS in wave order (the whole 160 KB holds 8 x 64 x 80 fp32).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void conv3x3_bf16_halo_wave_kernel(ConvArgs a) {
-    constexpr int TR = 2, BN = 80;
+__global__ __launch_bounds__(512) void conv3x3_bf16_halo_wave8_kernel(ConvArgs a) {
+    constexpr int TR = 2, BN = 80, NW = 8;
     using S = Stage<TR, BN>;
-    constexpr int WAVE_LDS = 2 * S::BYTES;
-    static_assert(4 * WAVE_LDS >= 4 * 64 * BN * 4 + 64 * BN * 2, "reduction area");
-    __shared__ __attribute__((aligned(1024))) char smem[4 * WAVE_LDS];
+    constexpr int RED = 64 * BN * 4;                 // one wave's fp32 partial tile
+    static_assert(S::BYTES <= RED, "a wave's stage buffer lies inside its reduction slot");
+    __shared__ __attribute__((aligned(1024))) char smem[NW * RED];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -369,10 +379,10 @@ __global__ __launch_bounds__(256) void conv3x3_bf16_halo_wave_kernel(ConvArgs a)
     const int n0 = nt * BN;
     const int k0 = (int)((int64_t)a.kstages * split / a.ksplit);
     const int k1 = (int)((int64_t)a.kstages * (split + 1) / a.ksplit);
-    const int kb = k0 + (k1 - k0) * wave / 4;
-    const int nk = k0 + (k1 - k0) * (wave + 1) / 4 - kb;
+    const int kb = k0 + (k1 - k0) * wave / NW;
+    const int nk = k0 + (k1 - k0) * (wave + 1) / NW - kb;
     const uint16_t* zero = (const uint16_t*)g_zero_line;
-    char* ring = smem + wave * WAVE_LDS;
+    char* buf = smem + wave * RED;
 
     const uint16_t* ap0[S::A_LOADS];
     const uint16_t* ap1[S::A_LOADS];
@@ -381,28 +391,27 @@ __global__ __launch_bounds__(256) void conv3x3_bf16_halo_wave_kernel(ConvArgs a)
     for (int j = 0; j < S::A_LOADS; ++j) resolve_a_slot<TR>(a, bb, ty0, tx0, j * 64 + lane, ap0[j], ap1[j], ap2[j]);
     uint32_t bo[S::B_LOADS];
 #pragma unroll
-    for (int j = 0; j < S::B_LOADS; ++j) bo[j] = b_slot_offset<BN>(a, n0, j * 64 + lane);
+    for (int j = 0; j < S::B_LOADS; ++j) bo[j] = b_slot_offset<BN>(a, n0, j, lane);
 
-#define DPW_ISSUE_KY(CC, KY, SRC, BUF)                                                              \
+#define DP8_ISSUE_KY(CC, KY, SRC)                                                                  \
     do {                                                                                            \
-        char* st_ = ring + (BUF) * S::BYTES;                                                        \
         _Pragma("unroll") for (int j = 0; j < S::A_LOADS; ++j) {                                    \
             const uint16_t* g_ = SRC[j] ? SRC[j] + (CC) * 32 : zero;                                \
             if (j < S::A_LOADS - 1 || lane < S::A_TAIL)                                             \
-                __builtin_amdgcn_global_load_lds((const void*)g_, (lds_void*)(st_ + j * 1024), 16, 0, 0); \
+                __builtin_amdgcn_global_load_lds((const void*)g_, (lds_void*)(buf + j * 1024), 16, 0, 0); \
         }                                                                                           \
-        const char* wk_ = stage_weights(a, (CC), (KY));                                           \
+        const char* wk_ = stage_weights(a, (CC), (KY));                                             \
         _Pragma("unroll") for (int j = 0; j < S::B_LOADS; ++j)                                      \
             __builtin_amdgcn_global_load_lds((const void*)(wk_ + bo[j]),                           \
-                                             (lds_void*)(st_ + S::B_OFF + j * 1024), 16, 0, 0);     \
+                                             (lds_void*)(buf + S::B_OFF + j * 1024), 16, 0, 0);     \
     } while (0)
-#define DPW_ISSUE(K, BUF)                                                                           \
+#define DP8_ISSUE(K)                                                                                \
     do {                                                                                            \
         const int cc_ = (K) / 3;                                                                    \
         switch ((K) - 3 * cc_) {                                                                    \
-            case 0: DPW_ISSUE_KY(cc_, 0, ap0, BUF); break;                                          \
-            case 1: DPW_ISSUE_KY(cc_, 1, ap1, BUF); break;                                          \
-            default: DPW_ISSUE_KY(cc_, 2, ap2, BUF); break;                                         \
+            case 0: DP8_ISSUE_KY(cc_, 0, ap0); break;                                               \
+            case 1: DP8_ISSUE_KY(cc_, 1, ap1); break;                                               \
+            default: DP8_ISSUE_KY(cc_, 2, ap2); break;                                              \
         }                                                                                           \
     } while (0)
 
@@ -414,18 +423,36 @@ __global__ __launch_bounds__(256) void conv3x3_bf16_halo_wave_kernel(ConvArgs a)
     int aoff[2][3], boff;
     operand_offsets<TR, BN>(lane, 0, 0, aoff, boff);
 
-    if (nk > 0) DPW_ISSUE(kb, 0);
+    if (nk > 0) DP8_ISSUE(kb);
     for (int it = 0; it < nk; ++it) {
-        wait_vmcnt<0>();     // stage it has landed; stage it-1's reads finished before this point
-        if (it + 1 < nk) DPW_ISSUE(kb + it + 1, (it + 1) & 1);
-        stage_mfma<BN>(ring + (it & 1) * S::BYTES, aoff, boff, acc);
+        wait_vmcnt<0>();     // stage it has landed in this wave's buffer
+#pragma unroll
+        for (int kx = 0; kx < 3; ++kx) {
+            bf16x8 af[4], bfr[5];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8*)(buf + aoff[i >> 1][kx] + (i & 1) * 1024);
+#pragma unroll
+            for (int n = 0; n < 5; ++n) bfr[n] = *(const bf16x8*)(buf + boff + (kx * BN + n * 16) * 64);
+            if (kx == 2) {
+                // the stage's last fragments are in registers: the buffer may take the next stage
+                __builtin_amdgcn_s_waitcnt(0xc07f);     // lgkmcnt(0): every read above has returned
+                __builtin_amdgcn_sched_barrier(0);
+                if (it + 1 < nk) DP8_ISSUE(kb + it + 1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int n = 0; n < 5; ++n)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[n], acc[i][n], 0, 0, 0);
+        }
     }
-#undef DPW_ISSUE
-#undef DPW_ISSUE_KY
-    __syncthreads();   // every wave is done with its ring: reuse the LDS for the reduction
+#undef DP8_ISSUE
+#undef DP8_ISSUE_KY
+    __syncthreads();   // every wave is done with its buffer: the LDS holds the partial tiles
 
     // acc[i][n][r] = D[pixel 16i + 4(l>>4) + r][channel 16n + (l&15)], pixel = tile row * 32 + column
-    float* red = (float*)smem;                   // [4 waves][64][80] fp32
+    float* red = (float*)smem;                   // [8 waves][64][80] fp32
     const int ecol = lane & 15;
     const int erow = 4 * (lane >> 4);
 #pragma unroll
@@ -436,47 +463,31 @@ __global__ __launch_bounds__(256) void conv3x3_bf16_halo_wave_kernel(ConvArgs a)
             for (int r = 0; r < 4; ++r)
                 red[(wave * 64 + i * 16 + erow + r) * BN + n * 16 + ecol] = acc[i][n][r];
     __syncthreads();
-    if (a.ksplit == 1) {
-        uint16_t* tile = (uint16_t*)(smem + 4 * 64 * BN * 4);   // [64][80] bf16 after the fp32 area
-        for (int q = tid; q < 64 * BN / 4; q += kThreads) {
-            const int px = q / (BN / 4), c4 = (q - px * (BN / 4)) * 4;
-            float4 v = *(const float4*)(red + px * BN + c4);
+    // sum the 8 partials in wave order, 4 channels of one pixel per thread and step
+    constexpr int G4 = 64 * BN / 4;
+    for (int q = tid; q < G4; q += 64 * NW) {
+        const int px = q / (BN / 4), c4 = (q - px * (BN / 4)) * 4;
+        float4 v = *(const float4*)(red + px * BN + c4);
 #pragma unroll
-            for (int w = 1; w < 4; ++w) {
-                const float4 u = *(const float4*)(red + (w * 64 + px) * BN + c4);
-                v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
-            }
-            const int co = n0 + c4;
-            if (a.bias && co < a.Cout) {
-                v.x += a.bias[co]; v.y += a.bias[co + 1]; v.z += a.bias[co + 2]; v.w += a.bias[co + 3];
-            }
-            uint2 o;
-            o.x = pack_bf16x2(v.x, v.y);
-            o.y = pack_bf16x2(v.z, v.w);
-            *(uint2*)(tile + px * BN + c4) = o;
+        for (int w = 1; w < NW; ++w) {
+            const float4 u = *(const float4*)(red + (w * 64 + px) * BN + c4);
+            v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
         }
-        __syncthreads();
-        constexpr int CPR = BN * 2 / 16;       // 10 chunks of 16 bytes per pixel
-        for (int q = tid; q < 64 * CPR; q += kThreads) {
-            const int px = q / CPR, c16 = q - px * CPR;
-            const int y = ty0 + (px >> 5), x = tx0 + (px & 31), co = n0 + c16 * 8;
-            if (y < a.h && x < a.W && co < a.Cout)
-                *(uint4*)(a.y + (((int64_t)bb * a.h + y) * a.W + x) * a.Cout + co) =
-                    *(const uint4*)(tile + px * BN + c16 * 8);
-        }
-    } else {
-        float* part = a.part + (int64_t)split * a.M * a.Cout;
-        for (int q = tid; q < 64 * BN / 4; q += kThreads) {
-            const int px = q / (BN / 4), c4 = (q - px * (BN / 4)) * 4;
-            float4 v = *(const float4*)(red + px * BN + c4);
-#pragma unroll
-            for (int w = 1; w < 4; ++w) {
-                const float4 u = *(const float4*)(red + (w * 64 + px) * BN + c4);
-                v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+        const int y = ty0 + (px >> 5), x = tx0 + (px & 31), co = n0 + c4;
+        if (y < a.h && x < a.W && co < a.Cout) {
+            const int64_t o = (((int64_t)bb * a.h + y) * a.W + x) * a.Cout + co;
+            if (a.ksplit == 1) {
+                if (a.bias) {
+                    const float4 bv = *(const float4*)(a.bias + co);
+                    v.x += bv.x; v.y += bv.y; v.z += bv.z; v.w += bv.w;
+                }
+                uint2 ov;
+                ov.x = pack_bf16x2(v.x, v.y);
+                ov.y = pack_bf16x2(v.z, v.w);
+                *(uint2*)(a.y + o) = ov;
+            } else {
+                *(float4*)(a.part + (int64_t)split * a.M * a.Cout + o) = v;
             }
-            const int y = ty0 + (px >> 5), x = tx0 + (px & 31), co = n0 + c4;
-            if (y < a.h && x < a.W && co < a.Cout)
-                *(float4*)(part + (((int64_t)bb * a.h + y) * a.W + x) * a.Cout + co) = v;
         }
     }
 }
@@ -656,7 +667,7 @@ hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout,
     else if (plan.kind == 1)
         conv3x3_bf16_halo_tile_kernel<<<grid, kThreads, 0, stream>>>(a);
     else
-        conv3x3_bf16_halo_wave_kernel<<<grid, kThreads, 0, stream>>>(a);
+        conv3x3_bf16_halo_wave8_kernel<<<grid, 512, 0, stream>>>(a);
     if (plan.ksplit > 1) {
         const int64_t total4 = (int64_t)a.M * Cout / 4;
         conv_splitk_reduce_kernel<<<(unsigned)((total4 + 255) / 256), 256, 0, stream>>>(

@@ -148,8 +148,9 @@ dp_status dp_groupnorm_async(const dp_patch* p, dp_dtype dtype, int32_t G, float
  *   bias     [Cout] float or NULL
  *   y_patch  [B][h][W][Cout] dtype; must not overlap any input
  *   ws       >= dp_conv3x3_halo_ws bytes
- * bf16 requires Cin % 64 == 0 and Cout % 32 == 0 (MFMA path); f32 takes any
- * Cin, Cout >= 1.
+ * bf16 requires Cin % 64 == 0 and Cout % 32 == 0 (MFMA path), fewer than
+ * 2^31 elements per batch image (H*W*Cin) and weights under 2 GiB; f32 takes
+ * any Cin, Cout >= 1.
  * ---------------------------------------------------------------------- */
 dp_status dp_conv3x3_halo_ws(const dp_patch* p, dp_dtype dtype, int32_t Cout, size_t* ws_bytes);
 
