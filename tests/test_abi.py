@@ -142,6 +142,16 @@ def test_conv_and_attention_overlap_errors():
                                  FAKE2 * 2, FAKE2 * 4, 1 << 24, None) == dp.DP_ERR_ARG
 
 
+def test_conv_rejects_images_beyond_32bit_offsets():
+    # a bf16 image of 2^31 elements (16384 x 2048 x 64) cannot be addressed with 32-bit offsets
+    big = dp.Patch(1, 16384, 2048, 64, 2, 0)
+    assert ws_query("conv", big, dp.DP_BF16, 64)[0] == dp.DP_ERR_UNSUPPORTED
+    assert "2^31" in dp.lib().dp_last_error().decode()
+    assert ws_query("conv", dp.Patch(1, 16384, 2047, 64, 2, 0), dp.DP_BF16, 64)[0] == dp.DP_OK
+    # the f32 direct path has no such limit
+    assert ws_query("conv", big, dp.DP_F32, 64)[0] == dp.DP_OK
+
+
 def test_packed_conv_weights_rejects():
     L = dp.lib()
     assert L.dp_conv3x3_packed_weights_bytes(320, 640) == 9 * 320 * 640 * 2
