@@ -241,7 +241,6 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
         else if (STAGES >= 3 && ahead >= 1) wait_vmcnt<LOADS>();
         else wait_vmcnt<0>();
         __syncthreads();
-        if (it + STAGES - 1 < nt) DPA_ISSUE(t + STAGES - 1, (it + STAGES - 1) % STAGES);
         const char* st = smem + (it % STAGES) * STAGE;
 
         // S^T[key][query], keys kb*32 + 8q + 4*hsel + r in s_kb[4q + r]
@@ -335,6 +334,11 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
         DPA_PV(2, p2);
         DPA_PV(3, p3);
 #undef DPA_PV
+        // Tile t+3 goes into the stage tile t-1 left (every wave passed this iteration's barrier
+        // after its last read of it).  Issued after this tile's V^T reads: the compiler makes the
+        // transposing LDS reads wait for every direct-to-LDS load in flight, so loads issued
+        // earlier in the iteration would be waited for here.
+        if (it + STAGES - 1 < nt) DPA_ISSUE(t + STAGES - 1, (it + STAGES - 1) % STAGES);
     }
 #undef DPA_ISSUE
 
