@@ -20,10 +20,14 @@
 //     Each source pixel is fetched once per stage instead of once per tap.
 //   * Stages are streamed global -> LDS with direct-to-LDS loads
 //     (global_load_lds_dwordx4: lane l of a load fills the l-th 16-byte slot of
-//     a 1 KB run), double-buffered.  Slot layout: chunk c (8 channels) of pixel
-//     or tap row p sits at slot 4p + (c ^ ((p >> 1) & 3)), so the 16
-//     consecutive rows of an MFMA operand read hit distinct banks at any
-//     column offset.
+//     a 1 KB run) through rings of one to three stages.  Slot layout: chunk c
+//     (8 channels) of pixel or tap row p sits at slot 4p + (c ^ ((p >> 1) & 3)),
+//     which spreads the 16 rows of an MFMA operand read over the banks except
+//     that rows p and p + 8 share them (a 2-way conflict; a conflict-free
+//     permutation measured no faster).
+//   * Weights are read either as given ([Cout][3][3][Cin]) or packed once into
+//     [3][Cin/32][3][Cout][32], where a stage's taps are one contiguous block
+//     and each 1 KB load reads whole cache lines.
 //   * Workgroups are dispatched round-robin over the 8 XCDs; tiles are renumbered
 //     so each XCD walks a contiguous run of pixel tiles, keeping the inputs those
 //     tiles share in one L2.
