@@ -25,8 +25,10 @@ hipError_t launch_band_copy(const void* src, void* dst, const Geom& g, size_t el
 struct GnPlan {
     int vec;          // elements per 16-byte vector
     int vpt;          // vectors per token (C / vec)
-    int rows;         // tokens a stats block reads in parallel
-    int threads;      // stats block size = vpt * rows
+    int rows;         // tokens a normalising block reads in parallel
+    int threads;      // normalising block size = vpt * rows (>= G)
+    int rows_stats;   // tokens a statistics block reads in parallel (<= rows)
+    int threads_stats;  // statistics block size = vpt * rows_stats
     int nblk;         // statistics blocks per batch
     int tok_per_blk;  // tokens per statistics block (the same split for every path, so the
                       // fresh moments are bitwise identical however they are computed)

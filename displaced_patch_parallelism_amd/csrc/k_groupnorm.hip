@@ -15,7 +15,8 @@
 // per-channel state stays in registers.
 //   1. gn_stats: rounds of 8 token loads in flight per thread; fp32 per-channel sums, reduced through LDS in a fixed order
 //      to per-group (sum, sum of squares) partials [block][B][G]; at most 128
-//      blocks per batch, so the partials stay small.
+//      blocks per batch, so the partials stay small; a small band takes blocks
+//      of fewer rows so that it still spreads over ~128 CUs.
 //   2. gn_apply: each block owns 4 token rows per thread (one round).  It issues the loads
 //      of its tokens, gamma/beta and the stale moments first; then adds the
 //      statistics partials of its batch (every partial load in flight at
@@ -128,7 +129,8 @@ struct GnApplyArgs {
     float* fresh_out;        // [B][G][2] or null
 };
 
-template <bool BF16, bool SILU>
+// PR: partial loads in flight per lane (8, or 16 for blocks whose lanes sum more than 8)
+template <bool BF16, bool SILU, int PR>
 __global__ void gn_apply_kernel(GnApplyArgs a) {
     constexpr int VEC = BF16 ? 8 : 4;
     constexpr int TPT = kApplyTokensPerThread;
@@ -169,21 +171,21 @@ __global__ void gn_apply_kernel(GnApplyArgs a) {
         }
     }
 
-    // (2) fresh moments: lane j0 of group g sums partials j0, j0+L, ... in order (8 loads in
+    // (2) fresh moments: lane j0 of group g sums partials j0, j0+L, ... in order (PR loads in
     // flight), then the L lane sums are added in lane order
     const int L = blockDim.x / G;            // >= 1: the plan gives blocks of >= G threads
     if (tid < L * G) {
         const int g = tid % G, j0 = tid / G;
         float sa = 0.f, sq = 0.f;
-        for (int jb = j0; jb < a.nblk; jb += 8 * L) {
-            float2 pv[8];
+        for (int jb = j0; jb < a.nblk; jb += PR * L) {
+            float2 pv[PR];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < PR; ++u) {
                 const int j = jb + u * L;
                 pv[u] = j < a.nblk ? a.partial[((int64_t)j * a.B + b) * G + g] : make_float2(0.f, 0.f);
             }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < PR; ++u) {
                 sa += pv[u].x;
                 sq += pv[u].y;
             }
@@ -262,8 +264,9 @@ hipError_t launch_gn_typed(const Geom& g, const GnPlan& plan, GnApplyArgs a, flo
     // statistics over the plan's token split
     {
         dim3 grid((unsigned)plan.nblk, (unsigned)g.B);
-        const size_t shmem = (size_t)2 * plan.rows * g.C * sizeof(float);
-        gn_stats_kernel<BF16><<<grid, plan.threads, shmem, stream>>>(a.x, a.tokens, g.C, a.G, plan.vpt, plan.rows,
+        const size_t shmem = (size_t)2 * plan.rows_stats * g.C * sizeof(float);
+        gn_stats_kernel<BF16><<<grid, plan.threads_stats, shmem, stream>>>(a.x, a.tokens, g.C, a.G, plan.vpt,
+                                                                          plan.rows_stats,
                                                                     plan.tok_per_blk, partial);
     }
     // apply: the plan's rounds of rows * 4 tokens per block; a moments-only call runs one
@@ -271,7 +274,11 @@ hipError_t launch_gn_typed(const Geom& g, const GnPlan& plan, GnApplyArgs a, flo
     a.tok_per_blk = plan.tok_per_blk_apply;
     const int64_t nb = a.y ? plan.nblk_apply : 1;
     const size_t shmem = ((size_t)(plan.threads / a.G) * a.G + a.G) * sizeof(float2);
-    gn_apply_kernel<BF16, SILU><<<dim3((unsigned)nb, (unsigned)g.B), plan.threads, shmem, stream>>>(a);
+    const dim3 grid_a((unsigned)nb, (unsigned)g.B);
+    if (plan.nblk > 8 * (plan.threads / a.G))
+        gn_apply_kernel<BF16, SILU, 16><<<grid_a, plan.threads, shmem, stream>>>(a);
+    else
+        gn_apply_kernel<BF16, SILU, 8><<<grid_a, plan.threads, shmem, stream>>>(a);
     return hipGetLastError();
 }
 
@@ -289,9 +296,15 @@ GnPlan plan_groupnorm(const Geom& g, int G, bool bf16) {
         p.threads = p.vpt * p.rows;
     }
     const int64_t tokens = g.band_tokens();
+    // Statistics blocks: as few token rows as give up to 128 blocks of one round each (a small
+    // band then spreads over more CUs), at most the normalising blocks' rows.
+    p.rows_stats = (int)((tokens + 128 * 8 - 1) / (128 * 8));
+    if (p.rows_stats > p.rows) p.rows_stats = p.rows;
+    if (p.rows_stats < 1) p.rows_stats = 1;
+    p.threads_stats = p.vpt * p.rows_stats;
     // Statistics split (depends only on the geometry): whole rounds of 8 token rows per thread,
     // at most 128 blocks per batch.
-    const int64_t round = (int64_t)p.rows * 8;
+    const int64_t round = (int64_t)p.rows_stats * 8;
     int64_t tpb = round;
     if ((tokens + tpb - 1) / tpb > 128) tpb = ((tokens + 127) / 128 + round - 1) / round * round;
     p.tok_per_blk = (int)tpb;
