@@ -13,17 +13,19 @@
 // A block is vpt x R threads: thread (cv, r) owns channel vector cv (8 bf16
 // or 4 f32 channels) and token rows r, r+R, ... of the block's range, so
 // per-channel state stays in registers.
-//   1. gn_stats: rounds of 8 token loads in flight per thread; fp32 per-channel sums, reduced through LDS in a fixed order
-//      to per-group (sum, sum of squares) partials [block][B][G]; at most 128
-//      blocks per batch, so the partials stay small; a small band takes blocks
-//      of fewer rows so that it still spreads over ~128 CUs.
+//   1. gn_stats: each thread sums one round of up to 8 token loads in flight (a band too
+//      large for that takes whole rounds); fp32 per-channel sums, reduced through LDS in a
+//      fixed order to per-group (sum, sum of squares) partials [block][B][G].  The band is cut
+//      into as many blocks as a normalising block can sum partials in one round of loads (at
+//      most 256), so even a small band spreads over the GPU.
 //   2. gn_apply: each block owns 4 token rows per thread (one round).  It issues the loads
-//      of its tokens, gamma/beta and the stale moments first; then adds the
-//      statistics partials of its batch (every partial load in flight at
-//      once, each lane summing its share in a fixed order, lanes combined in
-//      order through LDS), forms the fresh moments (block 0 stores them),
-//      combines them with the stale table into (mean, rstd), and writes
+//      of its tokens and the stale moments first; then adds the statistics partials of its
+//      batch (every partial load in flight at once, each lane summing its share in a fixed
+//      order, lanes combined in order through LDS), loads gamma/beta, forms the fresh moments
+//      (block 0 stores them), combines them with the stale table into (mean, rstd), and writes
 //      y = x*scale + shift (+ SiLU) rounded to the storage type.
+// LDS sums that run over a runtime count read 8 values ahead and add them in order, so the
+// order of every floating-point sum is fixed by the geometry.
 // The statistics split depends only on the geometry, so the fresh moments are
 // bitwise identical whichever entry path computes them.  No atomics.
 
@@ -44,6 +46,30 @@ __device__ __forceinline__ void to_f32(const uint4& v, float* f) {
         f[1] = __uint_as_float(v.y);
         f[2] = __uint_as_float(v.z);
         f[3] = __uint_as_float(v.w);
+    }
+}
+
+// x0 += p[k*stride].x, x1 += p[k*stride].y (or the two float arrays) for k < n, in k order,
+// with 8 reads in flight at a time (a plain loop waits out every LDS read).
+__device__ __forceinline__ void sum_lds_in_order(const float* ps, const float* pq, int stride, int n, float& x0,
+                                                 float& x1) {
+    int k = 0;
+    for (; k + 8 <= n; k += 8) {
+        float ts[8], tq[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            ts[u] = ps[(k + u) * stride];
+            tq[u] = pq[(k + u) * stride];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            x0 += ts[u];
+            x1 += tq[u];
+        }
+    }
+    for (; k < n; ++k) {
+        x0 += ps[k * stride];
+        x1 += pq[k * stride];
     }
 }
 
@@ -105,10 +131,7 @@ __global__ void gn_stats_kernel(const void* __restrict__ x, int64_t tokens, int 
     const int cg = C / G;
     for (int g = tid; g < G; g += blockDim.x) {
         float a = 0.f, aq = 0.f;
-        for (int c = g * cg; c < (g + 1) * cg; ++c) {
-            a += sh_s[c];
-            aq += sh_q[c];
-        }
+        sum_lds_in_order(sh_s + g * cg, sh_q + g * cg, 1, cg, a, aq);
         partial[((int64_t)blockIdx.x * gridDim.y + b) * G + g] = make_float2(a, aq);
     }
 }
@@ -130,8 +153,11 @@ struct GnApplyArgs {
 };
 
 // PR: partial loads in flight per lane (8, or 16 for blocks whose lanes sum more than 8)
+// At most 80 VGPRs (6 waves per SIMD): three blocks of up to 512 threads per CU, so a band of
+// ~768 blocks is resident at once (at 85 the 16-load instance held two, and a large band ran
+// its blocks in two waves).
 template <bool BF16, bool SILU, int PR>
-__global__ void gn_apply_kernel(GnApplyArgs a) {
+__global__ __attribute__((amdgpu_waves_per_eu(6))) void gn_apply_kernel(GnApplyArgs a) {
     constexpr int VEC = BF16 ? 8 : 4;
     constexpr int TPT = kApplyTokensPerThread;
     extern __shared__ float2 gsh[];          // [lanes_per_g][G] partial sums, then [G] (mean, rstd)
@@ -142,25 +168,18 @@ __global__ void gn_apply_kernel(GnApplyArgs a) {
     const int r = tid / a.vpt;
     const bool data = a.y != nullptr && r < a.rows;
 
-    // (1) independent loads first: this thread's tokens, its channels' gamma/beta, and (one
-    // thread per group) the stale moments the mode combines with the fresh ones
+    // (1) independent loads first: this thread's tokens and (one thread per group) the stale
+    // moments the mode combines with the fresh ones
     const int64_t t0 = (int64_t)blockIdx.x * a.tok_per_blk + r;
     const int64_t base = (int64_t)b * a.tokens * a.vpt + cv;
     const uint4* xv = (const uint4*)a.x + base;
     uint4 v[TPT];
-    float ga[VEC], be[VEC];
     if (data) {
         const int64_t t_end = (int64_t)(blockIdx.x + 1) * a.tok_per_blk < a.tokens
                                   ? (int64_t)(blockIdx.x + 1) * a.tok_per_blk : a.tokens;
 #pragma unroll
         for (int u = 0; u < TPT; ++u)
             if (t0 + u * a.rows < t_end) v[u] = xv[(t0 + u * a.rows) * a.vpt];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const int c = cv * VEC + e;
-            ga[e] = a.gamma ? a.gamma[c] : 1.f;
-            be[e] = a.beta ? a.beta[c] : 0.f;
-        }
     }
     float st_e = 0.f, st_q = 0.f;            // sum of the other bands' stale moments (thread g)
     if (tid < G && a.mode != 1) {
@@ -192,15 +211,24 @@ __global__ void gn_apply_kernel(GnApplyArgs a) {
         }
         gsh[j0 * G + g] = make_float2(sa, sq);
     }
+    // gamma/beta (L2-resident): issued here, so they hold no registers during the partial loads
+    // and arrive while the lanes are combined
+    float ga[VEC], be[VEC];
+    if (data) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const int c = cv * VEC + e;
+            ga[e] = a.gamma ? a.gamma[c] : 1.f;
+            be[e] = a.beta ? a.beta[c] : 0.f;
+        }
+    }
     __syncthreads();
     float2* mr = gsh + L * G;
     if (tid < G) {
         const int g = tid;
         float sa = 0.f, sq = 0.f;
-        for (int j = 0; j < L; ++j) {
-            sa += gsh[j * G + g].x;
-            sq += gsh[j * G + g].y;
-        }
+        const float* gf = (const float*)gsh;     // float2 [L][G] as floats: x at 2k, y at 2k+1
+        sum_lds_in_order(gf + 2 * g, gf + 2 * g + 1, 2 * G, L, sa, sq);
         const float m = sa * a.inv_count, qm = sq * a.inv_count;
         if (a.fresh_out && blockIdx.x == 0) {
             a.fresh_out[(b * G + g) * 2 + 0] = m;
@@ -296,23 +324,32 @@ GnPlan plan_groupnorm(const Geom& g, int G, bool bf16) {
         p.threads = p.vpt * p.rows;
     }
     const int64_t tokens = g.band_tokens();
-    // Statistics blocks: as few token rows as give up to 128 blocks of one round each (a small
-    // band then spreads over more CUs), at most the normalising blocks' rows.
-    p.rows_stats = (int)((tokens + 128 * 8 - 1) / (128 * 8));
-    if (p.rows_stats > p.rows) p.rows_stats = p.rows;
-    if (p.rows_stats < 1) p.rows_stats = 1;
-    p.threads_stats = p.vpt * p.rows_stats;
-    // Statistics split (depends only on the geometry): whole rounds of 8 token rows per thread,
-    // at most 128 blocks per batch.
-    const int64_t round = (int64_t)p.rows_stats * 8;
-    int64_t tpb = round;
-    if ((tokens + tpb - 1) / tpb > 128) tpb = ((tokens + 127) / 128 + round - 1) / round * round;
-    p.tok_per_blk = (int)tpb;
-    p.nblk = (int)((tokens + tpb - 1) / tpb);
     // Apply split: one round of 4 token rows per thread, so every block's loads are in flight
     // together (a whole band is a few MB to a few tens of MB).
     p.tok_per_blk_apply = p.rows * 4;
     p.nblk_apply = (int)((tokens + p.tok_per_blk_apply - 1) / p.tok_per_blk_apply);
+    // Statistics split (depends only on the geometry).  Up to nb_max blocks per batch: at most
+    // 256, at most what a normalising block sums in one round of loads (16 in flight on each of
+    // its threads / G lanes per group), and few enough that the partials all normalising blocks
+    // read stay near 64 Ki (blocks x partials) -- a small band spreads over the whole GPU, a
+    // large one keeps its partials few.  Each block takes its tokens in rows of R (token rows
+    // r, r+R, ...), R the fewest (at most the normalising block's rows) that keep every thread
+    // to one round of 8 loads; past that, whole rounds.
+    int nb_max = 16 * (p.threads / G);
+    if (nb_max > 256) nb_max = 256;
+    int nb_vol = (int)(65536 / (p.nblk_apply > 0 ? p.nblk_apply : 1));
+    if (nb_vol < 64) nb_vol = 64;
+    if (nb_max > nb_vol) nb_max = nb_vol;
+    const int64_t tpb0 = (tokens + nb_max - 1) / nb_max;           // tokens per block
+    int64_t rs = (tpb0 + 7) / 8;
+    if (rs > p.rows) rs = p.rows;
+    if (rs < 1) rs = 1;
+    p.rows_stats = (int)rs;
+    p.threads_stats = p.vpt * p.rows_stats;
+    int64_t tpb = (tpb0 + rs - 1) / rs * rs;
+    if (tpb > 8 * rs) tpb = (tpb0 + 8 * rs - 1) / (8 * rs) * (8 * rs);   // whole rounds
+    p.tok_per_blk = (int)tpb;
+    p.nblk = (int)((tokens + tpb - 1) / tpb);
     p.partial_floats = (size_t)p.nblk * g.B * G * 2;
     p.ws_bytes = p.partial_floats * sizeof(float);
     return p;
