@@ -91,7 +91,9 @@ dp_status check_gn(const dp_patch* p, dp_dtype dt, int32_t G, dp::Geom* g) {
     const int vec = dt == DP_BF16 ? 8 : 4;
     if (g->C % vec != 0)
         return fail(DP_ERR_UNSUPPORTED, "GroupNorm needs C %% %d == 0 for this dtype (C=%d)", vec, g->C);
-    if (g->C > 8192) return fail(DP_ERR_UNSUPPORTED, "GroupNorm supports C <= 8192 (C=%d)", g->C);
+    // a block holds one thread per 16-byte channel vector of a token: at most 1024 of them
+    if (g->C / vec > 1024)
+        return fail(DP_ERR_UNSUPPORTED, "GroupNorm supports C <= %d for this dtype (C=%d)", 1024 * vec, g->C);
     return DP_OK;
 }
 

@@ -119,7 +119,8 @@ typedef struct {
  *                   (the first pass of a synchronous warm-up step); may equal
  *                   x_patch (in place) but must not otherwise overlap it
  *   ws              >= dp_groupnorm_async_ws bytes
- * Requires C % G == 0, C % 8 == 0 (bf16) or C % 4 == 0 (f32), eps > 0.
+ * Requires C % G == 0, C % 8 == 0 and C <= 8192 (bf16) or C % 4 == 0 and
+ * C <= 4096 (f32), eps > 0; other channel counts give DP_ERR_UNSUPPORTED.
  * After the call, fresh_stats_out is what dp_stale_update copies into slot i
  * of the table for the next step (see dp_stale_update).
  * ---------------------------------------------------------------------- */

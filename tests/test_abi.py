@@ -98,6 +98,11 @@ def test_workspace_queries():
 def test_unsupported_shapes():
     assert ws_query("gn", dp.Patch(1, 8, 8, 30, 2, 0), dp.DP_BF16, 3)[0] == dp.DP_ERR_UNSUPPORTED
     assert ws_query("gn", dp.Patch(1, 8, 8, 32, 2, 0), dp.DP_BF16, 5)[0] == dp.DP_ERR_ARG
+    # one thread per 16-byte channel vector, at most 1024 a block: C <= 8192 bf16, 4096 f32
+    assert ws_query("gn", dp.Patch(1, 8, 8, 8192, 2, 0), dp.DP_BF16, 32)[0] == dp.DP_OK
+    assert ws_query("gn", dp.Patch(1, 8, 8, 8200, 2, 0), dp.DP_BF16, 8)[0] == dp.DP_ERR_UNSUPPORTED
+    assert ws_query("gn", dp.Patch(1, 8, 8, 4096, 2, 0), dp.DP_F32, 32)[0] == dp.DP_OK
+    assert ws_query("gn", dp.Patch(1, 8, 8, 8192, 2, 0), dp.DP_F32, 32)[0] == dp.DP_ERR_UNSUPPORTED
     assert ws_query("conv", dp.Patch(1, 8, 8, 32, 2, 0), dp.DP_BF16, 64)[0] == dp.DP_ERR_UNSUPPORTED
     assert ws_query("attn", dp.Patch(1, 8, 8, 256, 2, 0), dp.DP_BF16, 2, 128)[0] == dp.DP_ERR_UNSUPPORTED
     assert ws_query("attn", dp.Patch(1, 8, 8, 64, 2, 0), dp.DP_BF16, 2, 64)[0] == dp.DP_ERR_ARG

@@ -87,3 +87,10 @@ def test_warmup_table_gives_exact_group_norm():
                                      c.G, table)
         assert_parity(host(y), ref[:, j * c.h:(j + 1) * c.h], "bf16", f"warm-up band {j}")
 
+
+
+def test_widest_channel_counts():
+    """One thread per 16-byte channel vector: C = 8192 (bf16) and 4096 (f32) fill 1024-thread blocks."""
+    announce("groupnorm widest channels")
+    run_case(1, 6, 5, 8192, 32, 2, 1, "bf16", act="silu", affine=True, seed=8)
+    run_case(1, 6, 5, 4096, 64, 3, 2, "f32", mode="local", affine=True, seed=8)
