@@ -59,6 +59,7 @@ dp_status check_patch(const dp_patch* p, dp_dtype dt, dp::Geom* g) {
     if (p->i < 0 || p->i >= p->P) return fail(DP_ERR_ARG, "patch index i=%d not in [0, %d)", p->i, p->P);
     const int64_t elems = (int64_t)p->B * p->H * p->W * p->C;
     if (elems > ((int64_t)1 << 40)) return fail(DP_ERR_ARG, "map too large");
+    if (p->B > 65535) return fail(DP_ERR_UNSUPPORTED, "B=%d exceeds 65535 (the batch is a grid dimension)", p->B);
     g->B = p->B; g->H = p->H; g->W = p->W; g->C = p->C; g->P = p->P; g->i = p->i;
     g->h = p->H / p->P;
     g->r0 = p->i * g->h;
@@ -107,8 +108,10 @@ dp_status check_conv(const dp_patch* p, dp_dtype dt, int32_t Cout, dp::Geom* g) 
                     g->C, Cout);
     // the bf16 kernels address one batch image and the weights with 32-bit offsets
     if (dt == DP_BF16 && ((int64_t)g->H * g->W * g->C >= (int64_t)1 << 31 ||
-                          (int64_t)9 * g->C * Cout * 2 >= (int64_t)1 << 31))
-        return fail(DP_ERR_UNSUPPORTED, "bf16 conv needs H*W*Cin < 2^31 elements and weights < 2 GiB");
+                          (int64_t)9 * g->C * Cout * 2 >= (int64_t)1 << 31 ||
+                          (int64_t)g->B * g->h * g->W >= (int64_t)1 << 31))
+        return fail(DP_ERR_UNSUPPORTED,
+                    "bf16 conv needs H*W*Cin < 2^31 elements, weights < 2 GiB and B*h*W < 2^31 output pixels");
     return DP_OK;
 }
 
@@ -119,6 +122,8 @@ dp_status check_attn(const dp_patch* p, dp_dtype dt, int32_t heads, int32_t head
     if (heads < 1 || head_dim < 1) return fail(DP_ERR_ARG, "heads and head_dim must be >= 1");
     if ((int64_t)heads * head_dim != g->C)
         return fail(DP_ERR_ARG, "heads*head_dim=%d does not equal C=%d", heads * head_dim, g->C);
+    if ((int64_t)g->H * g->W >= ((int64_t)1 << 31))
+        return fail(DP_ERR_UNSUPPORTED, "attention needs H*W < 2^31 tokens (H=%d W=%d)", g->H, g->W);
     if (dt == DP_BF16 && head_dim != 64)
         return fail(DP_ERR_UNSUPPORTED, "bf16 attention is built for head_dim 64 (got %d)", head_dim);
     if (dt == DP_F32 && !(head_dim == 4 || head_dim == 8 || head_dim == 16 || head_dim == 32 ||

@@ -8,6 +8,10 @@
 
 namespace dp {
 
+// A 1-D grid of n blocks is launchable (at most 2^31 - 1 blocks); launches return
+// hipErrorInvalidConfiguration otherwise, never a truncated grid.
+inline bool grid_fits(int64_t n) { return n >= 1 && n <= 0x7fffffffLL; }
+
 // Geometry of one patch of an NHWC map split into P equal row bands.
 struct Geom {
     int B, H, W, C, P, i;

@@ -515,6 +515,7 @@ hipError_t launch_attention(const Geom& g, const AttnPlan& plan, bool bf16, int 
     const int band0 = g.r0 * g.W;
     if (!bf16) {
         const int64_t total = (int64_t)g.B * heads * Nq;
+        if (!grid_fits((total + 63) / 64)) return hipErrorInvalidConfiguration;
         const unsigned blocks = (unsigned)((total + 63) / 64);
         const float sc = scale * kLog2e;
 #define DP_F32_ATTN(HD)                                                                                  \
@@ -553,11 +554,13 @@ hipError_t launch_attention(const Geom& g, const AttnPlan& plan, bool bf16, int 
     a.kvsplit = plan.kvsplit;
     a.sc = scale * kLog2e;
     a.qtiles = plan.qtiles;
-    const unsigned grid = (unsigned)((int64_t)plan.qtiles * g.B * heads * plan.kvsplit);
+    const int64_t nwg = (int64_t)plan.qtiles * g.B * heads * plan.kvsplit;
+    const int64_t merge_threads = (int64_t)g.B * heads * Nq * (D / 4);
+    if (!grid_fits(nwg) || !grid_fits((merge_threads + 255) / 256)) return hipErrorInvalidConfiguration;
+    const unsigned grid = (unsigned)nwg;
     attn_bf16_d64_kernel<kStages, 8><<<grid, 512, 0, stream>>>(a);
     if (plan.kvsplit > 1) {
-        const int64_t threads = (int64_t)g.B * heads * Nq * (D / 4);
-        attn_merge_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(
+        attn_merge_kernel<<<(unsigned)((merge_threads + 255) / 256), 256, 0, stream>>>(
             a.part_o, a.part_ml, (uint16_t*)o, g.B, heads, g.C, Nq, plan.kvsplit);
     }
     return hipGetLastError();

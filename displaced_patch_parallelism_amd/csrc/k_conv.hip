@@ -626,6 +626,7 @@ ConvPlan plan_conv(const Geom& g, int Cout, bool bf16) {
 hipError_t launch_conv_pack(int Cin, int Cout, const void* w, void* w_packed, hipStream_t stream) {
     const int64_t total = (int64_t)Cout * 9 * (Cin / 8);
     if (total == 0) return hipSuccess;
+    if (!grid_fits((total + 255) / 256)) return hipErrorInvalidConfiguration;
     conv_pack_weights_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>((const uint4*)w, (uint4*)w_packed,
                                                                                 Cin, Cout);
     return hipGetLastError();
@@ -637,6 +638,7 @@ hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout,
     if (!bf16) {
         const int64_t total = (int64_t)g.B * g.h * g.W * Cout;
         const int64_t blocks = (total + 255) / 256;
+        if (!grid_fits(blocks)) return hipErrorInvalidConfiguration;
         conv3x3_f32_direct_kernel<<<(unsigned)blocks, 256, 0, stream>>>(
             (const float*)x_patch, (const float*)x_stale, (const float*)w, bias, (float*)y, g.B, g.H, g.W, g.C, Cout,
             g.h, g.r0);
@@ -665,7 +667,10 @@ hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout,
     a.kstages = plan.ktiles;
     a.ksplit = plan.ksplit;
     a.wpacked = w_packed ? 1 : 0;
-    const unsigned grid = (unsigned)(plan.mtiles * plan.ntiles * plan.ksplit);
+    const int64_t nwg = (int64_t)plan.mtiles * plan.ntiles * plan.ksplit;
+    const int64_t total4 = (int64_t)a.M * Cout / 4;
+    if (!grid_fits(nwg) || (plan.ksplit > 1 && !grid_fits((total4 + 255) / 256))) return hipErrorInvalidConfiguration;
+    const unsigned grid = (unsigned)nwg;
     if (plan.kind == 3)
         conv3x3_bf16_halo_tile8_kernel<<<grid, 512, 0, stream>>>(a);
     else if (plan.kind == 1)
@@ -673,7 +678,6 @@ hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout,
     else
         conv3x3_bf16_halo_wave8_kernel<<<grid, 512, 0, stream>>>(a);
     if (plan.ksplit > 1) {
-        const int64_t total4 = (int64_t)a.M * Cout / 4;
         conv_splitk_reduce_kernel<<<(unsigned)((total4 + 255) / 256), 256, 0, stream>>>(
             (const float*)ws, bias, (uint16_t*)y, total4, Cout, plan.ksplit);
     }

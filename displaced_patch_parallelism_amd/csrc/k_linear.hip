@@ -176,6 +176,7 @@ hipError_t launch_linear(bool bf16, int M, int N, int K, const void* x, int64_t 
     if (M == 0) return hipSuccess;
     if (!bf16) {
         const int64_t total = (int64_t)M * N;
+        if (!grid_fits((total + 255) / 256)) return hipErrorInvalidConfiguration;
         linear_f32_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(
             (const float*)x, ldx, (const float*)w, bias, (float*)y, ldy, M, N, K);
         return hipGetLastError();
@@ -195,10 +196,12 @@ hipError_t launch_linear(bool bf16, int M, int N, int K, const void* x, int64_t 
     if (big >= 256) {
         a.mtiles = (M + 127) / 128;
         a.ntiles = (N + 127) / 128;
+        if (!grid_fits((int64_t)a.mtiles * a.ntiles)) return hipErrorInvalidConfiguration;
         linear_bf16_kernel<128, 128><<<(unsigned)(a.mtiles * a.ntiles), 256, 0, stream>>>(a);
     } else {
         a.mtiles = (M + 63) / 64;
         a.ntiles = (N + 63) / 64;
+        if (!grid_fits((int64_t)a.mtiles * a.ntiles)) return hipErrorInvalidConfiguration;
         linear_bf16_kernel<64, 64><<<(unsigned)(a.mtiles * a.ntiles), 256, 0, stream>>>(a);
     }
     return hipGetLastError();

@@ -48,7 +48,8 @@
  *   DP_ERR_ARG          invalid argument (shape, index, NULL, alignment,
  *                       workspace too small, output overlapping an input)
  *   DP_ERR_UNSUPPORTED  valid but not built (e.g. bf16 attention with a
- *                       head_dim other than 64)
+ *                       head_dim other than 64, or B > 65535: the batch
+ *                       is a grid dimension of several kernels)
  *   DP_ERR_HIP          a HIP launch failed
  * dp_last_error() then describes the failure.  No C++ exception or abort
  * crosses the ABI.  Results are deterministic: repeated calls with the same
@@ -150,8 +151,8 @@ dp_status dp_groupnorm_async(const dp_patch* p, dp_dtype dtype, int32_t G, float
  *   y_patch  [B][h][W][Cout] dtype; must not overlap any input
  *   ws       >= dp_conv3x3_halo_ws bytes
  * bf16 requires Cin % 64 == 0 and Cout % 32 == 0 (MFMA path), fewer than
- * 2^31 elements per batch image (H*W*Cin) and weights under 2 GiB; f32 takes
- * any Cin, Cout >= 1.
+ * 2^31 elements per batch image (H*W*Cin), fewer than 2^31 output pixels
+ * (B*h*W) and weights under 2 GiB; f32 takes any Cin, Cout >= 1.
  * ---------------------------------------------------------------------- */
 dp_status dp_conv3x3_halo_ws(const dp_patch* p, dp_dtype dtype, int32_t Cout, size_t* ws_bytes);
 
@@ -207,8 +208,9 @@ dp_status dp_conv3x3_halo_packed(const dp_patch* p, dp_dtype dtype, int32_t Cout
  *                              overlap any input
  * k_patch / v_patch may point into band i of k_stale / v_stale (an in-place
  * splice done before the call); the result is the same.
- * Requires heads*head_dim == p->C.  bf16: head_dim == 64.  f32:
- * head_dim <= 128 and head_dim % 4 == 0.
+ * Requires heads*head_dim == p->C and H*W < 2^31 tokens.  bf16: head_dim ==
+ * 64.  f32: head_dim in {4, 8, 16, 32, 64, 128}.  Other head sizes give
+ * DP_ERR_UNSUPPORTED.
  * ---------------------------------------------------------------------- */
 dp_status dp_attention_splice_ws(const dp_patch* p, dp_dtype dtype, int32_t heads,
                                  int32_t head_dim, size_t* ws_bytes);

@@ -103,6 +103,12 @@ def test_unsupported_shapes():
     assert ws_query("gn", dp.Patch(1, 8, 8, 8200, 2, 0), dp.DP_BF16, 8)[0] == dp.DP_ERR_UNSUPPORTED
     assert ws_query("gn", dp.Patch(1, 8, 8, 4096, 2, 0), dp.DP_F32, 32)[0] == dp.DP_OK
     assert ws_query("gn", dp.Patch(1, 8, 8, 8192, 2, 0), dp.DP_F32, 32)[0] == dp.DP_ERR_UNSUPPORTED
+    # the batch is a grid dimension (at most 65535)
+    assert ws_query("gn", dp.Patch(65535, 2, 2, 8, 2, 0), dp.DP_BF16, 8)[0] == dp.DP_OK
+    assert ws_query("gn", dp.Patch(65536, 2, 2, 8, 2, 0), dp.DP_BF16, 8)[0] == dp.DP_ERR_UNSUPPORTED
+    # attention indexes tokens with 32-bit integers; the bf16 conv its output pixels
+    assert ws_query("attn", dp.Patch(1, 1 << 16, 1 << 15, 4, 2, 0), dp.DP_F32, 1, 4)[0] == dp.DP_ERR_UNSUPPORTED
+    assert ws_query("conv", dp.Patch(16384, 2048, 128, 64, 2, 0), dp.DP_BF16, 64)[0] == dp.DP_ERR_UNSUPPORTED
     assert ws_query("conv", dp.Patch(1, 8, 8, 32, 2, 0), dp.DP_BF16, 64)[0] == dp.DP_ERR_UNSUPPORTED
     assert ws_query("attn", dp.Patch(1, 8, 8, 256, 2, 0), dp.DP_BF16, 2, 128)[0] == dp.DP_ERR_UNSUPPORTED
     assert ws_query("attn", dp.Patch(1, 8, 8, 64, 2, 0), dp.DP_BF16, 2, 64)[0] == dp.DP_ERR_ARG
