@@ -37,7 +37,8 @@ struct GnPlan {
     int tok_per_blk;  // tokens per statistics block (the same split for every path, so the
                       // fresh moments are bitwise identical however they are computed)
     int nblk_apply;   // normalising blocks per batch
-    int tok_per_blk_apply;  // tokens per normalising block (a multiple of 4 * rows)
+    int tpt_apply;    // token rows per normalising thread (4, or 2 or 1 for small bands)
+    int tok_per_blk_apply;  // tokens per normalising block (rows * tpt_apply)
     size_t partial_floats;  // B * nblk * G * 2
     size_t ws_bytes;
 };

@@ -18,7 +18,8 @@
 //      fixed order to per-group (sum, sum of squares) partials [block][B][G].  The band is cut
 //      into as many blocks as a normalising block can sum partials in one round of loads (at
 //      most 256), so even a small band spreads over the GPU.
-//   2. gn_apply: each block owns 4 token rows per thread (one round).  It issues the loads
+//   2. gn_apply: each block owns 4 token rows per thread (one round; 2 or 1 rows for a band
+//      too small to give 256 such blocks, so that it still spreads over the GPU).  It issues the loads
 //      of its tokens and the stale moments first; then adds the statistics partials of its
 //      batch (every partial load in flight at once, each lane summing its share in a fixed
 //      order, lanes combined in order through LDS), loads gamma/beta, forms the fresh moments
@@ -136,7 +137,6 @@ __global__ void gn_stats_kernel(const void* __restrict__ x, int64_t tokens, int 
     }
 }
 
-constexpr int kApplyTokensPerThread = 4;
 
 struct GnApplyArgs {
     const void* x;
@@ -152,14 +152,14 @@ struct GnApplyArgs {
     float* fresh_out;        // [B][G][2] or null
 };
 
-// PR: partial loads in flight per lane (8, or 16 for blocks whose lanes sum more than 8)
+// PR: partial loads in flight per lane (8, or 16 for blocks whose lanes sum more than 8).
+// TPT: token rows per thread (4, or 2 or 1 for a band too small to give 256 blocks of 4).
 // At most 80 VGPRs (6 waves per SIMD): three blocks of up to 512 threads per CU, so a band of
 // ~768 blocks is resident at once (at 85 the 16-load instance held two, and a large band ran
 // its blocks in two waves).
-template <bool BF16, bool SILU, int PR>
+template <bool BF16, bool SILU, int PR, int TPT>
 __global__ __attribute__((amdgpu_waves_per_eu(6))) void gn_apply_kernel(GnApplyArgs a) {
     constexpr int VEC = BF16 ? 8 : 4;
-    constexpr int TPT = kApplyTokensPerThread;
     extern __shared__ float2 gsh[];          // [lanes_per_g][G] partial sums, then [G] (mean, rstd)
     const int tid = threadIdx.x;
     const int b = blockIdx.y;
@@ -297,16 +297,23 @@ hipError_t launch_gn_typed(const Geom& g, const GnPlan& plan, GnApplyArgs a, flo
                                                                           plan.rows_stats,
                                                                     plan.tok_per_blk, partial);
     }
-    // apply: the plan's rounds of rows * 4 tokens per block; a moments-only call runs one
+    // apply: one round of rows * tpt_apply tokens per block; a moments-only call runs one
     // block per batch
     a.tok_per_blk = plan.tok_per_blk_apply;
     const int64_t nb = a.y ? plan.nblk_apply : 1;
     const size_t shmem = ((size_t)(plan.threads / a.G) * a.G + a.G) * sizeof(float2);
     const dim3 grid_a((unsigned)nb, (unsigned)g.B);
-    if (plan.nblk > 8 * (plan.threads / a.G))
-        gn_apply_kernel<BF16, SILU, 16><<<grid_a, plan.threads, shmem, stream>>>(a);
-    else
-        gn_apply_kernel<BF16, SILU, 8><<<grid_a, plan.threads, shmem, stream>>>(a);
+    const bool pr16 = plan.nblk > 8 * (plan.threads / a.G);
+    if (plan.tpt_apply == 1) {
+        if (pr16) gn_apply_kernel<BF16, SILU, 16, 1><<<grid_a, plan.threads, shmem, stream>>>(a);
+        else gn_apply_kernel<BF16, SILU, 8, 1><<<grid_a, plan.threads, shmem, stream>>>(a);
+    } else if (plan.tpt_apply == 2) {
+        if (pr16) gn_apply_kernel<BF16, SILU, 16, 2><<<grid_a, plan.threads, shmem, stream>>>(a);
+        else gn_apply_kernel<BF16, SILU, 8, 2><<<grid_a, plan.threads, shmem, stream>>>(a);
+    } else {
+        if (pr16) gn_apply_kernel<BF16, SILU, 16, 4><<<grid_a, plan.threads, shmem, stream>>>(a);
+        else gn_apply_kernel<BF16, SILU, 8, 4><<<grid_a, plan.threads, shmem, stream>>>(a);
+    }
     return hipGetLastError();
 }
 
@@ -325,8 +332,13 @@ GnPlan plan_groupnorm(const Geom& g, int G, bool bf16) {
     }
     const int64_t tokens = g.band_tokens();
     // Apply split: one round of 4 token rows per thread, so every block's loads are in flight
-    // together (a whole band is a few MB to a few tens of MB).
-    p.tok_per_blk_apply = p.rows * 4;
+    // together (a whole band is a few MB to a few tens of MB); a band that gives fewer than 256
+    // such blocks takes 2 or 1 rows per thread instead -- the most that still give 128 blocks
+    // -- spreading its loads, stores and SiLU over more CUs.
+    p.tpt_apply = 4;
+    if ((tokens + p.rows * 4 - 1) / (p.rows * 4) < 256)
+        p.tpt_apply = (tokens + p.rows * 2 - 1) / (p.rows * 2) >= 128 ? 2 : 1;
+    p.tok_per_blk_apply = p.rows * p.tpt_apply;
     p.nblk_apply = (int)((tokens + p.tok_per_blk_apply - 1) / p.tok_per_blk_apply);
     // Statistics split (depends only on the geometry).  Up to nb_max blocks per batch: at most
     // 256, at most what a normalising block sums in one round of loads (16 in flight on each of
