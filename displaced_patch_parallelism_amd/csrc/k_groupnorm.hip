@@ -152,6 +152,9 @@ struct GnApplyArgs {
     float* fresh_out;        // [B][G][2] or null
 };
 
+// Stale-table entries ([P][G] of one batch) an apply block parks in LDS (32 KB).
+constexpr int kStaleLds = 4096;
+
 // PR: partial loads in flight per lane (8, or 16 for blocks whose lanes sum more than 8).
 // TPT: token rows per thread (4, or 2 or 1 for a band too small to give 256 blocks of 4).
 // At most 80 VGPRs (6 waves per SIMD): three blocks of up to 512 threads per CU, so a band of
@@ -160,7 +163,7 @@ struct GnApplyArgs {
 template <bool BF16, bool SILU, int PR, int TPT>
 __global__ __attribute__((amdgpu_waves_per_eu(6))) void gn_apply_kernel(GnApplyArgs a) {
     constexpr int VEC = BF16 ? 8 : 4;
-    extern __shared__ float2 gsh[];          // [lanes_per_g][G] partial sums, then [G] (mean, rstd)
+    extern __shared__ float2 gsh[];          // [lanes_per_g][G] partial sums, [G] (mean, rstd), [P][G] stale
     const int tid = threadIdx.x;
     const int b = blockIdx.y;
     const int G = a.G;
@@ -181,14 +184,14 @@ __global__ __attribute__((amdgpu_waves_per_eu(6))) void gn_apply_kernel(GnApplyA
         for (int u = 0; u < TPT; ++u)
             if (t0 + u * a.rows < t_end) v[u] = xv[(t0 + u * a.rows) * a.vpt];
     }
-    float st_e = 0.f, st_q = 0.f;            // sum of the other bands' stale moments (thread g)
-    if (tid < G && a.mode != 1) {
-        for (int j = 0; j < a.P; ++j) {
-            if (a.mode == 0 && j == a.i) continue;
-            st_e += a.stale[((int64_t)j * a.B + b) * G * 2 + tid * 2 + 0];
-            st_q += a.stale[((int64_t)j * a.B + b) * G * 2 + tid * 2 + 1];
-        }
-    }
+    // the stale table's [P][G] moments of this batch, one entry per thread (a table larger than
+    // kStaleLds entries is summed from memory by the group threads instead); each entry is
+    // parked in LDS after the partial loads, so no thread waits on it before they are issued
+    const bool stale_lds = a.mode != 1 && (int64_t)a.P * G <= kStaleLds;
+    const int PG = stale_lds ? a.P * G : 0;
+    float2 stv = make_float2(0.f, 0.f);
+    if (stale_lds && tid < PG)
+        stv = *(const float2*)(a.stale + (((int64_t)(tid / G) * a.B + b) * G + tid % G) * 2);
 
     // (2) fresh moments: lane j0 of group g sums partials j0, j0+L, ... in order (PR loads in
     // flight), then the L lane sums are added in lane order
@@ -211,24 +214,60 @@ __global__ __attribute__((amdgpu_waves_per_eu(6))) void gn_apply_kernel(GnApplyA
         }
         gsh[j0 * G + g] = make_float2(sa, sq);
     }
-    // gamma/beta (L2-resident): issued here, so they hold no registers during the partial loads
-    // and arrive while the lanes are combined
-    float ga[VEC], be[VEC];
-    if (data) {
+    float2* mr = gsh + L * G;
+    float2* stl = mr + G;
+    if (stale_lds) {
+        if (tid < PG) stl[tid] = stv;
+        for (int k = tid + blockDim.x; k < PG; k += blockDim.x)
+            stl[k] = *(const float2*)(a.stale + (((int64_t)(k / G) * a.B + b) * G + k % G) * 2);
+    }
+    // gamma/beta (L2-resident, 16-byte vectors): issued here, so they hold no registers during
+    // the partial loads and arrive while the lanes are combined
+    float4 gv[VEC / 4], bv[VEC / 4];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const int c = cv * VEC + e;
-            ga[e] = a.gamma ? a.gamma[c] : 1.f;
-            be[e] = a.beta ? a.beta[c] : 0.f;
-        }
+    for (int e4 = 0; e4 < VEC / 4; ++e4) {
+        gv[e4] = make_float4(1.f, 1.f, 1.f, 1.f);
+        bv[e4] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (data && a.gamma) {
+        const float4* gp = (const float4*)(a.gamma + cv * VEC);
+#pragma unroll
+        for (int e4 = 0; e4 < VEC / 4; ++e4) gv[e4] = gp[e4];
+    }
+    if (data && a.beta) {
+        const float4* bp = (const float4*)(a.beta + cv * VEC);
+#pragma unroll
+        for (int e4 = 0; e4 < VEC / 4; ++e4) bv[e4] = bp[e4];
     }
     __syncthreads();
-    float2* mr = gsh + L * G;
     if (tid < G) {
         const int g = tid;
         float sa = 0.f, sq = 0.f;
         const float* gf = (const float*)gsh;     // float2 [L][G] as floats: x at 2k, y at 2k+1
         sum_lds_in_order(gf + 2 * g, gf + 2 * g + 1, 2 * G, L, sa, sq);
+        // sum of the other bands' stale moments, in band order
+        float st_e = 0.f, st_q = 0.f;
+        if (stale_lds) {
+            for (int j0 = 0; j0 < a.P; j0 += 8) {
+                float2 t[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) t[u] = j0 + u < a.P ? stl[(j0 + u) * G + g] : make_float2(0.f, 0.f);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int j = j0 + u;
+                    if (j < a.P && !(a.mode == 0 && j == a.i)) {
+                        st_e += t[u].x;
+                        st_q += t[u].y;
+                    }
+                }
+            }
+        } else if (a.mode != 1) {
+            for (int j = 0; j < a.P; ++j) {
+                if (a.mode == 0 && j == a.i) continue;
+                st_e += a.stale[((int64_t)j * a.B + b) * G * 2 + g * 2 + 0];
+                st_q += a.stale[((int64_t)j * a.B + b) * G * 2 + g * 2 + 1];
+            }
+        }
         const float m = sa * a.inv_count, qm = sq * a.inv_count;
         if (a.fresh_out && blockIdx.x == 0) {
             a.fresh_out[(b * G + g) * 2 + 0] = m;
@@ -251,6 +290,12 @@ __global__ __attribute__((amdgpu_waves_per_eu(6))) void gn_apply_kernel(GnApplyA
 
     // (3) normalise: the tokens loaded in (1), then the block's further rounds of 4 rows
     const int cg = a.C / G;
+    float ga[VEC], be[VEC];
+#pragma unroll
+    for (int e4 = 0; e4 < VEC / 4; ++e4) {
+        ga[4 * e4 + 0] = gv[e4].x; ga[4 * e4 + 1] = gv[e4].y; ga[4 * e4 + 2] = gv[e4].z; ga[4 * e4 + 3] = gv[e4].w;
+        be[4 * e4 + 0] = bv[e4].x; be[4 * e4 + 1] = bv[e4].y; be[4 * e4 + 2] = bv[e4].z; be[4 * e4 + 3] = bv[e4].w;
+    }
     float sc[VEC], sf[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
@@ -301,7 +346,9 @@ hipError_t launch_gn_typed(const Geom& g, const GnPlan& plan, GnApplyArgs a, flo
     // block per batch
     a.tok_per_blk = plan.tok_per_blk_apply;
     const int64_t nb = a.y ? plan.nblk_apply : 1;
-    const size_t shmem = ((size_t)(plan.threads / a.G) * a.G + a.G) * sizeof(float2);
+    const size_t pg = (size_t)g.P * a.G;
+    const size_t shmem = ((size_t)(plan.threads / a.G) * a.G + a.G + (pg <= (size_t)kStaleLds ? pg : 0)) *
+                         sizeof(float2);
     const dim3 grid_a((unsigned)nb, (unsigned)g.B);
     const bool pr16 = plan.nblk > 8 * (plan.threads / a.G);
     if (plan.tpt_apply == 1) {

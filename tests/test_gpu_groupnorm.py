@@ -94,3 +94,16 @@ def test_widest_channel_counts():
     announce("groupnorm widest channels")
     run_case(1, 6, 5, 8192, 32, 2, 1, "bf16", act="silu", affine=True, seed=8)
     run_case(1, 6, 5, 4096, 64, 3, 2, "f32", mode="local", affine=True, seed=8)
+
+
+@pytest.mark.parametrize("shape", [
+    # (B, H, W, C, G, P, i): the stale table [P][G] of one batch has more entries than an apply
+    # block has threads (16 x 32 = 512 > 480), and more than the block parks in LDS (65 x 64)
+    (1, 32, 16, 320, 32, 16, 5),
+    (1, 130, 2, 64, 64, 65, 64),
+])
+@pytest.mark.parametrize("mode", ["corrected", "stale"])
+def test_large_stale_tables(shape, mode):
+    B, H, W, C, G, P, i = shape
+    announce("groupnorm stale table", shape, mode)
+    run_case(B, H, W, C, G, P, i, "bf16", mode=mode, act="silu", seed=9)
