@@ -453,6 +453,18 @@ __global__ __launch_bounds__(512) void conv3x3_bf16_halo_wave8_kernel(ConvArgs a
     }
 #undef DP8_ISSUE
 #undef DP8_ISSUE_KY
+    // the bias of the channels this thread stores below, loaded now so that its latency
+    // overlaps the partial-tile exchange (in the loop each load would be waited out in turn)
+    constexpr int G4 = 64 * BN / 4;                  // 4-channel groups of the tile
+    constexpr int NQ = (G4 + 64 * NW - 1) / (64 * NW);
+    float4 bq[NQ];
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+        const int q = tid + k * 64 * NW;
+        const int co = n0 + (q % (BN / 4)) * 4;
+        bq[k] = (a.ksplit == 1 && a.bias && q < G4 && co < a.Cout) ? *(const float4*)(a.bias + co)
+                                                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     __syncthreads();   // every wave is done with its buffer: the LDS holds the partial tiles
 
     // acc[i][n][r] = D[pixel 16i + 4(l>>4) + r][channel 16n + (l&15)], pixel = tile row * 32 + column
@@ -468,8 +480,10 @@ __global__ __launch_bounds__(512) void conv3x3_bf16_halo_wave8_kernel(ConvArgs a
                 red[(wave * 64 + i * 16 + erow + r) * BN + n * 16 + ecol] = acc[i][n][r];
     __syncthreads();
     // sum the 8 partials in wave order, 4 channels of one pixel per thread and step
-    constexpr int G4 = 64 * BN / 4;
-    for (int q = tid; q < G4; q += 64 * NW) {
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+        const int q = tid + k * 64 * NW;
+        if (q >= G4) break;
         const int px = q / (BN / 4), c4 = (q - px * (BN / 4)) * 4;
         float4 v = *(const float4*)(red + px * BN + c4);
 #pragma unroll
@@ -482,8 +496,7 @@ __global__ __launch_bounds__(512) void conv3x3_bf16_halo_wave8_kernel(ConvArgs a
             const int64_t o = (((int64_t)bb * a.h + y) * a.W + x) * a.Cout + co;
             if (a.ksplit == 1) {
                 if (a.bias) {
-                    const float4 bv = *(const float4*)(a.bias + co);
-                    v.x += bv.x; v.y += bv.y; v.z += bv.z; v.w += bv.w;
+                    v.x += bq[k].x; v.y += bq[k].y; v.z += bq[k].z; v.w += bq[k].w;
                 }
                 uint2 ov;
                 ov.x = pack_bf16x2(v.x, v.y);
@@ -496,7 +509,8 @@ __global__ __launch_bounds__(512) void conv3x3_bf16_halo_wave8_kernel(ConvArgs a
     }
 }
 
-// y[m][co] = bf16(bias[co] + sum_s part[s][m][co]), summed in split order.
+// y[m][co] = bf16(bias[co] + sum_s part[s][m][co]), summed in split order.  The splits are
+// loaded 8 at a time, all in flight before any is added (a plain loop waits out every load).
 __global__ __launch_bounds__(256) void conv_splitk_reduce_kernel(const float* __restrict__ part,
                                                                  const float* __restrict__ bias,
                                                                  uint16_t* __restrict__ y, int64_t total4,
@@ -504,20 +518,29 @@ __global__ __launch_bounds__(256) void conv_splitk_reduce_kernel(const float* __
     const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i4 >= total4) return;
     const int64_t i = i4 * 4;
-    float4 s = *(const float4*)(part + i);
-    for (int k = 1; k < ksplit; ++k) {
-        const float4 v = *(const float4*)(part + (int64_t)k * total4 * 4 + i);
-        s.x += v.x;
-        s.y += v.y;
-        s.z += v.z;
-        s.w += v.w;
-    }
     const int co = (int)(i % Cout);
+    const float4 bv = bias ? *(const float4*)(bias + co) : make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 s = *(const float4*)(part + i);
+    for (int k0 = 1; k0 < ksplit; k0 += 8) {
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (k0 + u < ksplit) v[u] = *(const float4*)(part + (int64_t)(k0 + u) * total4 * 4 + i);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (k0 + u < ksplit) {
+                s.x += v[u].x;
+                s.y += v[u].y;
+                s.z += v[u].z;
+                s.w += v[u].w;
+            }
+        }
+    }
     if (bias) {
-        s.x += bias[co];
-        s.y += bias[co + 1];
-        s.z += bias[co + 2];
-        s.w += bias[co + 3];
+        s.x += bv.x;
+        s.y += bv.y;
+        s.z += bv.z;
+        s.w += bv.w;
     }
     uint2 o;
     o.x = pack_bf16x2(s.x, s.y);
