@@ -118,17 +118,16 @@ __global__ void gn_stats_kernel(const void* __restrict__ x, int64_t tokens, int 
         sh_q[r * C + cv * VEC + e] = q[e];
     }
     __syncthreads();
-    // per-channel totals over the rows, in row order; kept in row 0
-    for (int c = tid; c < C; c += blockDim.x) {
-        float a = sh_s[c], aq = sh_q[c];
-        for (int j = 1; j < rows; ++j) {
-            a += sh_s[j * C + c];
-            aq += sh_q[j * C + c];
+    // per-channel totals over the rows, in row order; kept in row 0 (one row: already there)
+    if (rows > 1) {
+        for (int c = tid; c < C; c += blockDim.x) {
+            float a = sh_s[c], aq = sh_q[c];
+            sum_lds_in_order(sh_s + C + c, sh_q + C + c, C, rows - 1, a, aq);
+            sh_s[c] = a;
+            sh_q[c] = aq;
         }
-        sh_s[c] = a;
-        sh_q[c] = aq;
+        __syncthreads();
     }
-    __syncthreads();
     const int cg = C / G;
     for (int g = tid; g < G; g += blockDim.x) {
         float a = 0.f, aq = 0.f;
