@@ -141,16 +141,24 @@ _ws_cache = {}
 
 
 def _workspace(nbytes, device, ws):
-    """Caller workspace if given and large enough, else a cached per-device buffer."""
+    """Caller workspace if given, else a buffer cached per (device, stream).
+
+    Calls on one stream run in order, so they can share scratch; calls on two streams may
+    run at once, so each stream gets its own.  The buffer is allocated on the stream that
+    uses it: when a larger one replaces it, the caching allocator hands the old memory out
+    again only after the work already queued on that stream.  Code captured into a HIP graph
+    should pass `ws` explicitly, so that the graph keeps pointing at memory it owns."""
     torch = _torch()
     if nbytes == 0:
         return None, 0
     if ws is not None:
         return ws.data_ptr(), ws.numel() * ws.element_size()
-    key = (device.type, device.index)
+    stream = torch.cuda.current_stream(device)
+    key = (device.type, device.index, stream.cuda_stream)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(stream):
+            buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _ws_cache[key] = buf
     return buf.data_ptr(), buf.numel()
 
