@@ -141,8 +141,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one patch's layer step on ONE GPU; runs on more than one GPU "
-              "are not part of this build (--gpus must be 1).", file=sys.stderr)
+        print("bench.py measures one patch's layer step on ONE GPU; the exchange between GPUs is "
+              "not implemented, so --gpus must be 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
