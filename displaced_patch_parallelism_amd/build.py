@@ -2,7 +2,8 @@
 
     python -m displaced_patch_parallelism_amd.build
 
-Every call recompiles every translation unit (in parallel) and relinks.
+Every call recompiles every translation unit (in parallel) and relinks, then compiles the
+standalone diagnostics under diag/ into _build/.
 """
 
 import os
@@ -63,7 +64,25 @@ def build(verbose=False):
     if r.returncode != 0:
         raise RuntimeError("link failed\n" + r.stdout + r.stderr)
     os.replace(tmp, LIB)
+    build_diag()
     return LIB
+
+
+def build_diag():
+    """Compiles the standalone diagnostics (diag/*.hip) into _build/, so that every HIP
+    source of the package is checked by a build; returns the executables' paths."""
+    out = []
+    diag = os.path.join(PKG, "diag")
+    for src in sorted(os.listdir(diag)):
+        if not src.endswith(".hip"):
+            continue
+        exe = os.path.join(BUILD, os.path.splitext(src)[0])
+        cmd = [hipcc()] + [f for f in COMMON if f != "-fPIC"] + ["-x", "hip", os.path.join(diag, src), "-o", exe]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compile failed: diag/{src}\n" + r.stdout + r.stderr)
+        out.append(exe)
+    return out
 
 
 if __name__ == "__main__":
