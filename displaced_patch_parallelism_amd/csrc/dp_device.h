@@ -28,6 +28,28 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// Make every word of a kernel's argument block live in SGPRs at this point.  Left to itself
+// the compiler requests argument fields lazily, next to their first use, and may re-request
+// them after register pressure has pushed other values out to scratch; an empty asm that takes
+// every word as an SGPR operand puts all the requests ahead of one wait at kernel entry.
+template <typename T>
+__device__ __forceinline__ void args_in_sgprs(const T& a) {
+    static_assert(sizeof(T) % 4 == 0, "argument block of whole dwords");
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(&a);
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 4); ++i) asm volatile("" ::"s"(w[i]));
+}
+
+// The same for kernels whose arguments are separate parameters.
+template <typename T>
+__device__ __forceinline__ void sgpr_operand(T v) {
+    asm volatile("" ::"s"(v));
+}
+template <typename... T>
+__device__ __forceinline__ void params_in_sgprs(T... v) {
+    (sgpr_operand(v), ...);
+}
+
 // Unpack a 16-byte vector of 8 bf16 into floats.
 __device__ __forceinline__ void unpack8(const uint4& v, float* f) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};

@@ -106,6 +106,9 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
     constexpr int LOADS = 16 / WAVES;         // DMA loads (1 KB chunks) per wave per stage
     constexpr int QTW = 32 * WAVES;           // queries per workgroup
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
+    // all arguments in SGPRs from the start: with them loaded lazily the kernel, at its VGPR
+    // limit, kept reloading spilled values inside the tile loop
+    args_in_sgprs(a);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -378,6 +381,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
                                                          const float2* __restrict__ part_ml,
                                                          uint16_t* __restrict__ o, int B, int heads, int C,
                                                          int Nq, int kvsplit) {
+    params_in_sgprs(part_o, part_ml, o, B, heads, C, Nq, kvsplit);
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t rows = (int64_t)B * heads * Nq;
     if (idx >= rows * (D / 4)) return;
