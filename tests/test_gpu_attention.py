@@ -56,6 +56,8 @@ def test_c4b_sampled_rows():
     (1, 40, 10, 1, 2, 1),    # Nq = 200: ragged query tile
     (1, 8, 24, 4, 1, 0),     # one patch: plain self-attention
     (2, 48, 90, 1, 2, 1),    # Nq = 2160 (8-wave tiles, ragged), N = 4320 (ragged key tiles), batch 2
+    (1, 4, 8, 1, 2, 1),      # N = 32: the whole map is one partial key tile
+    (1, 48, 32, 1, 8, 3),    # one query tile over 24 key tiles: 12 key splits of 2 tiles, merged
 ])
 def test_ragged_bf16(B, H, W, heads, P, i):
     announce("attention ragged", B, H, W, heads, P, i)
