@@ -356,11 +356,13 @@ __global__ __launch_bounds__(512, 1) void conv3x3_bf16_halo_tile8_kernel(ConvArg
 // ---------------------------------------------------------------------------
 // Small maps: tile 2 rows x 32 columns x 80 channels with K split over 8 waves (two per SIMD),
 // and across workgroups until about 256 of them run (fp32 partials, summed in split order by
-// conv_splitk_reduce_kernel).  Each wave streams its stages through a single private buffer: it reads all of
-// a stage's operand fragments into registers, then issues the next stage's loads into the freed
-// buffer and runs the stage's 60 MFMAs.  A wave stalls while the CU's vector memory path takes
-// its loads; the other wave on its SIMD multiplies meanwhile.  The 8 accumulators are summed
-// through LDS in wave order (the whole 160 KB holds 8 x 64 x 80 fp32).
+// conv_splitk_reduce_kernel).  Each wave streams its stages through a single private buffer, refilled
+// tap by tap: once tap kx's fragments are in registers, the next stage's weight rows of tap kx go
+// into the freed rows (and after the last tap, its source pixels), then tap kx's 20 MFMAs run, so
+// two thirds of the refill are in flight a tap or two earlier than a whole-stage refill would be.
+// A wave stalls while the CU's vector memory path takes its loads; the other wave on its SIMD
+// multiplies meanwhile.  The 8 accumulators are summed through LDS in wave order (the whole
+// 160 KB holds 8 x 64 x 80 fp32).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(512) void conv3x3_bf16_halo_wave8_kernel(ConvArgs a) {
     constexpr int TR = 2, BN = 80, NW = 8;
@@ -393,29 +395,37 @@ __global__ __launch_bounds__(512) void conv3x3_bf16_halo_wave8_kernel(ConvArgs a
     const uint16_t* ap2[S::A_LOADS];
 #pragma unroll
     for (int j = 0; j < S::A_LOADS; ++j) resolve_a_slot<TR>(a, bb, ty0, tx0, j * 64 + lane, ap0[j], ap1[j], ap2[j]);
-    uint32_t bo[S::B_LOADS];
+    // B slot offsets of tap 0; tap kx's are kx * kxs further (the clamped row depends on the row only)
+    uint32_t bo[BN / 16];
 #pragma unroll
-    for (int j = 0; j < S::B_LOADS; ++j) bo[j] = b_slot_offset<BN>(a, n0, j, lane);
+    for (int j = 0; j < BN / 16; ++j) bo[j] = b_slot_offset<BN>(a, n0, j, lane);
+    const int64_t kxs = a.wpacked ? (int64_t)a.Cout * 64 : (int64_t)a.Cin * 2;
 
-#define DP8_ISSUE_KY(CC, KY, SRC)                                                                  \
+    // a stage in parts: the B loads of tap KX (tap rows KX*BN .. +BN-1), and the A loads
+#define DP8_ISSUE_B(K, KX)                                                                          \
+    do {                                                                                            \
+        const int cc_ = (K) / 3;                                                                    \
+        const char* wk_ = stage_weights(a, cc_, (K) - 3 * cc_) + (KX) * kxs;                        \
+        _Pragma("unroll") for (int j = 0; j < BN / 16; ++j)                                         \
+            __builtin_amdgcn_global_load_lds((const void*)(wk_ + bo[j]),                           \
+                                             (lds_void*)(buf + S::B_OFF + ((KX) * (BN / 16) + j) * 1024), \
+                                             16, 0, 0);                                             \
+    } while (0)
+#define DP8_ISSUE_A_KY(CC, SRC)                                                                     \
     do {                                                                                            \
         _Pragma("unroll") for (int j = 0; j < S::A_LOADS; ++j) {                                    \
             const uint16_t* g_ = SRC[j] ? SRC[j] + (CC) * 32 : zero;                                \
             if (j < S::A_LOADS - 1 || lane < S::A_TAIL)                                             \
                 __builtin_amdgcn_global_load_lds((const void*)g_, (lds_void*)(buf + j * 1024), 16, 0, 0); \
         }                                                                                           \
-        const char* wk_ = stage_weights(a, (CC), (KY));                                             \
-        _Pragma("unroll") for (int j = 0; j < S::B_LOADS; ++j)                                      \
-            __builtin_amdgcn_global_load_lds((const void*)(wk_ + bo[j]),                           \
-                                             (lds_void*)(buf + S::B_OFF + j * 1024), 16, 0, 0);     \
     } while (0)
-#define DP8_ISSUE(K)                                                                                \
+#define DP8_ISSUE_A(K)                                                                              \
     do {                                                                                            \
         const int cc_ = (K) / 3;                                                                    \
         switch ((K) - 3 * cc_) {                                                                    \
-            case 0: DP8_ISSUE_KY(cc_, 0, ap0); break;                                               \
-            case 1: DP8_ISSUE_KY(cc_, 1, ap1); break;                                               \
-            default: DP8_ISSUE_KY(cc_, 2, ap2); break;                                              \
+            case 0: DP8_ISSUE_A_KY(cc_, ap0); break;                                                \
+            case 1: DP8_ISSUE_A_KY(cc_, ap1); break;                                                \
+            default: DP8_ISSUE_A_KY(cc_, ap2); break;                                               \
         }                                                                                           \
     } while (0)
 
@@ -427,7 +437,12 @@ __global__ __launch_bounds__(512) void conv3x3_bf16_halo_wave8_kernel(ConvArgs a
     int aoff[2][3], boff;
     operand_offsets<TR, BN>(lane, 0, 0, aoff, boff);
 
-    if (nk > 0) DP8_ISSUE(kb);
+    if (nk > 0) {
+        DP8_ISSUE_A(kb);
+        DP8_ISSUE_B(kb, 0);
+        DP8_ISSUE_B(kb, 1);
+        DP8_ISSUE_B(kb, 2);
+    }
     for (int it = 0; it < nk; ++it) {
         wait_vmcnt<0>();     // stage it has landed in this wave's buffer
 #pragma unroll
@@ -437,13 +452,15 @@ __global__ __launch_bounds__(512) void conv3x3_bf16_halo_wave8_kernel(ConvArgs a
             for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8*)(buf + aoff[i >> 1][kx] + (i & 1) * 1024);
 #pragma unroll
             for (int n = 0; n < 5; ++n) bfr[n] = *(const bf16x8*)(buf + boff + (kx * BN + n * 16) * 64);
-            if (kx == 2) {
-                // the stage's last fragments are in registers: the buffer may take the next stage
-                __builtin_amdgcn_s_waitcnt(0xc07f);     // lgkmcnt(0): every read above has returned
-                __builtin_amdgcn_sched_barrier(0);
-                if (it + 1 < nk) DP8_ISSUE(kb + it + 1);
-                __builtin_amdgcn_sched_barrier(0);
+            // tap kx's fragments are in registers: its B rows may take the next stage's (and after
+            // the last tap, so may the A pixels)
+            __builtin_amdgcn_s_waitcnt(0xc07f);     // lgkmcnt(0): every read above has returned
+            __builtin_amdgcn_sched_barrier(0);
+            if (it + 1 < nk) {
+                if (kx == 2) DP8_ISSUE_A(kb + it + 1);
+                DP8_ISSUE_B(kb + it + 1, kx);
             }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int n = 0; n < 5; ++n)
 #pragma unroll
@@ -451,8 +468,9 @@ __global__ __launch_bounds__(512) void conv3x3_bf16_halo_wave8_kernel(ConvArgs a
                     acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[n], acc[i][n], 0, 0, 0);
         }
     }
-#undef DP8_ISSUE
-#undef DP8_ISSUE_KY
+#undef DP8_ISSUE_B
+#undef DP8_ISSUE_A
+#undef DP8_ISSUE_A_KY
     // the bias of the channels this thread stores below, loaded now so that its latency
     // overlaps the partial-tile exchange (in the loop each load would be waited out in turn)
     constexpr int G4 = 64 * BN / 4;                  // 4-channel groups of the tile
