@@ -95,6 +95,28 @@ def test_workspace_queries():
     assert st == dp.DP_OK and n == 0
 
 
+@pytest.mark.parametrize("kind,p,args,expect", [
+    # conv: fp32 partials, one [M][Cout] slab per K split; 64x80 tiles split along K until ~256
+    # workgroups run: c2 has 16 x 8 = 128 tiles -> 2 splits, c3 2 x 16 = 32 tiles -> 8
+    ("conv", dp.Patch(1, 64, 64, 640, 4, 1), (640,), 2 * 1024 * 640 * 4),
+    ("conv", dp.Patch(1, 32, 32, 1280, 8, 1), (1280,), 8 * 128 * 1280 * 4),
+    ("conv", dp.Patch(1, 128, 128, 320, 4, 1), (320,), 0),       # 256 tiles: no split
+    ("conv", dp.Patch(1, 480, 480, 320, 8, 1), (320,), 0),       # large-map tiles: no split
+    # attention: per key split, fp32 O [heads][Nq][64] and (max, sum) per query; 256-query
+    # tiles x heads, split to fill whole rounds of 256 workgroups: c2 40 units -> 6, c3 20 -> 8,
+    # c4b 290 -> 6
+    ("attn", dp.Patch(1, 64, 64, 640, 4, 1), (10, 64), 6 * 10 * 1024 * (64 * 4 + 8)),
+    ("attn", dp.Patch(1, 32, 32, 1280, 8, 1), (20, 64), 8 * 20 * 128 * (64 * 4 + 8)),
+    ("attn", dp.Patch(1, 240, 240, 640, 8, 1), (10, 64), 6 * 10 * 7200 * (64 * 4 + 8)),
+    # GroupNorm: (sum, sum of squares) per statistics block and group; c1 splits its 4096 tokens
+    # into 228 blocks of 18
+    ("gn", dp.Patch(1, 128, 128, 320, 4, 1), (32,), 228 * 32 * 2 * 4),
+])
+def test_workspace_sizes_follow_the_launch_plans(kind, p, args, expect):
+    st, n = ws_query(kind, p, dp.DP_BF16, *args)
+    assert st == dp.DP_OK and n == expect
+
+
 def test_unsupported_shapes():
     assert ws_query("gn", dp.Patch(1, 8, 8, 30, 2, 0), dp.DP_BF16, 3)[0] == dp.DP_ERR_UNSUPPORTED
     assert ws_query("gn", dp.Patch(1, 8, 8, 32, 2, 0), dp.DP_BF16, 5)[0] == dp.DP_ERR_ARG
