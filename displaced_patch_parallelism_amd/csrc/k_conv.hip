@@ -380,21 +380,15 @@ __global__ __launch_bounds__(512) void conv3x3_bf16_halo_wave8_kernel(ConvArgs a
     const int rest = lt / a.mtiles;
     const int split = rest % a.ksplit;
     const int nt = rest / a.ksplit;
-    int bb, ty0, tx0;
-    tile_origin<TR>(a, mt, bb, ty0, tx0);
     const int n0 = nt * BN;
-    const int k0 = (int)((int64_t)a.kstages * split / a.ksplit);
-    const int k1 = (int)((int64_t)a.kstages * (split + 1) / a.ksplit);
+    // kstages * ksplit < 2^31 for every conv the host accepts (weights under 2 GiB, <= 32 splits)
+    const int k0 = a.kstages * split / a.ksplit;
+    const int k1 = a.kstages * (split + 1) / a.ksplit;
     const int kb = k0 + (k1 - k0) * wave / NW;
     const int nk = k0 + (k1 - k0) * (wave + 1) / NW - kb;
     const uint16_t* zero = (const uint16_t*)g_zero_line;
     char* buf = smem + wave * RED;
 
-    const uint16_t* ap0[S::A_LOADS];
-    const uint16_t* ap1[S::A_LOADS];
-    const uint16_t* ap2[S::A_LOADS];
-#pragma unroll
-    for (int j = 0; j < S::A_LOADS; ++j) resolve_a_slot<TR>(a, bb, ty0, tx0, j * 64 + lane, ap0[j], ap1[j], ap2[j]);
     // B slot offsets of tap 0; tap kx's are kx * kxs further (the clamped row depends on the row only)
     uint32_t bo[BN / 16];
 #pragma unroll
@@ -437,12 +431,22 @@ __global__ __launch_bounds__(512) void conv3x3_bf16_halo_wave8_kernel(ConvArgs a
     int aoff[2][3], boff;
     operand_offsets<TR, BN>(lane, 0, 0, aoff, boff);
 
+    // the first stage's weight rows go out before the source pixels are resolved (their
+    // addresses are a few operations; the pixels' take most of the prologue)
     if (nk > 0) {
-        DP8_ISSUE_A(kb);
         DP8_ISSUE_B(kb, 0);
         DP8_ISSUE_B(kb, 1);
         DP8_ISSUE_B(kb, 2);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    int bb, ty0, tx0;
+    tile_origin<TR>(a, mt, bb, ty0, tx0);
+    const uint16_t* ap0[S::A_LOADS];
+    const uint16_t* ap1[S::A_LOADS];
+    const uint16_t* ap2[S::A_LOADS];
+#pragma unroll
+    for (int j = 0; j < S::A_LOADS; ++j) resolve_a_slot<TR>(a, bb, ty0, tx0, j * 64 + lane, ap0[j], ap1[j], ap2[j]);
+    if (nk > 0) DP8_ISSUE_A(kb);
     for (int it = 0; it < nk; ++it) {
         wait_vmcnt<0>();     // stage it has landed in this wave's buffer
 #pragma unroll
