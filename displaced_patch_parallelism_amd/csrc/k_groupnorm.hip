@@ -94,11 +94,16 @@ __global__ void gn_stats_kernel(const void* __restrict__ x, int64_t tokens, int 
     const uint4* xb = (const uint4*)x + (int64_t)b * tokens * vpt + cv;
     // rounds of 8 token rows per thread, all 8 loads in flight (rows past the end read as
     // zeros, which add nothing to either sum)
+    // (one 64-bit base per round; the round's rows are 32-bit offsets of it, rows * vpt = the
+    // block size apart, so the address arithmetic ahead of the first load stays short)
+    const int step = rows * vpt;
     for (int64_t t = t0 + r; t < t1; t += 8 * rows) {
+        const uint4* p = xb + t * vpt;
+        const int64_t left = t1 - t;
+        const int nrow = left < 8 * rows ? (int)left : 8 * rows;
         uint4 v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            v[u] = t + u * rows < t1 ? xb[(t + u * rows) * vpt] : make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < 8; ++u) v[u] = u * rows < nrow ? p[u * step] : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             float f[VEC];
