@@ -11,8 +11,9 @@ Conventions
 -----------
 * Generator: ``numpy.random.default_rng(seed)`` (PCG64), drawing in float32.
 * Draw order for a layer: fresh map ``x``, perturbation ``eps``, then for each
-  conv of the graph its weights and its bias, then for each projected
-  attention step its Q, K, V and O weights and biases (N(0, 1/C)).
+  conv of the graph (``conv`` or ``conv_res``) its weights and its bias, then
+  for each projected attention step (``attn_proj`` or ``attn_proj_res``) its
+  Q, K, V and O weights and biases (N(0, 1/C)).
 * Weights ``[Cout][3][3][Cin]`` and bias ``[Cout]`` are N(0, 1/fan_in) with
   fan_in = 9*Cin.  The bias stays float32; weights are rounded to the
   activation storage type.
@@ -27,6 +28,8 @@ from typing import List, Optional, Tuple
 import numpy as np
 
 PERTURB = 0.05
+CONV_STEPS = ("conv", "conv_res")               # graph steps that own a conv's weights
+PROJ_STEPS = ("attn_proj", "attn_proj_res")     # graph steps that own Q/K/V/O projections
 
 
 def bf16_round(a: np.ndarray) -> np.ndarray:
@@ -90,8 +93,8 @@ def layer_inputs(cfg, seed: int, perturb: float = PERTURB) -> LayerInputs:
     eps = rng.standard_normal(shape, dtype=np.float32)
     x_prev = x + np.float32(perturb) * eps
     convs = [conv_params(rng, cfg.C, cfg.C, cfg.dtype)
-             for s in cfg.graph if s == "conv"]
-    projs = [proj_params(rng, cfg.C, cfg.dtype) for s in cfg.graph if s == "attn_proj"]
+             for s in cfg.graph if s in CONV_STEPS]
+    projs = [proj_params(rng, cfg.C, cfg.dtype) for s in cfg.graph if s in PROJ_STEPS]
     return LayerInputs(to_storage(x, cfg.dtype), to_storage(x_prev, cfg.dtype), convs, projs)
 
 
@@ -116,8 +119,8 @@ def trajectory(cfg, seed: int, steps: int, perturb: float = PERTURB) -> Trajecto
     for _ in range(steps):
         x = x + np.float32(perturb) * rng.standard_normal(shape, dtype=np.float32)
         xs.append(to_storage(x, cfg.dtype))
-    convs = [conv_params(rng, cfg.C, cfg.C, cfg.dtype) for s in cfg.graph if s == "conv"]
-    projs = [proj_params(rng, cfg.C, cfg.dtype) for s in cfg.graph if s == "attn_proj"]
+    convs = [conv_params(rng, cfg.C, cfg.C, cfg.dtype) for s in cfg.graph if s in CONV_STEPS]
+    projs = [proj_params(rng, cfg.C, cfg.dtype) for s in cfg.graph if s in PROJ_STEPS]
     return Trajectory(xs, convs, projs)
 
 

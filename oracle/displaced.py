@@ -256,33 +256,37 @@ def stale_update(stale, x_patch, P, i):
 def displaced_layer(graph, params, x_patch, state, P, i, gn_mode=GN_CORRECTED):
     """Run patch i of a layer graph against the previous step's state.
 
-    graph: sequence of "gn", "gn_silu", "conv", "attn", "attn_proj".
+    graph: sequence of "gn", "gn_silu", "conv", "attn", "attn_proj", and the residual
+           forms "conv_res" / "attn_proj_res", whose output adds the layer's own input
+           patch (the skip connection of a ResNet or transformer block).
     params: dict with G, eps, heads, scale (optional), gamma/beta (optional),
             convs: list of (w, bias) in graph order, projs: list of
             (wq, bq, wk, bk, wv, bv, wo, bo) for the attn_proj steps in order.
-    state: dict with "stats" [P][B][G][2] (GroupNorm moments per band of the
-           previous step) and "maps": {step index: [B][H][W][C] stale input map
-           of that conv or attention step; (step index, "k") / (step index, "v"):
-           the previous step's projected K / V maps of an attn_proj step}.
+    state: dict with "stats" {step index: [P][B][G][2] GroupNorm moments per band of
+           the previous step, one table per GroupNorm step} and "maps": {step index:
+           [B][H][W][C] stale input map of that conv or attention step; (step index,
+           "k") / (step index, "v"): the previous step's projected K / V maps of an
+           attn_proj step}.
     Returns (outputs, new_state): outputs is the list of every step's patch
     output (float64); new_state is the state with patch i's band and
     statistics spliced in.
     """
-    h = np.asarray(x_patch, dtype=F64)
+    x_in = np.asarray(x_patch, dtype=F64)
+    h = x_in
     B, hb, W, C = h.shape
     H = hb * P
     outputs = []
-    new_stats = np.array(state["stats"], dtype=F64, copy=True)
+    new_stats = {k: np.array(t, dtype=F64, copy=True) for k, t in state["stats"].items()}
     new_maps = {k: np.array(v, dtype=F64, copy=True) for k, v in state["maps"].items()}
     conv_iter = iter(params.get("convs", []))
     proj_iter = iter(params.get("projs", []))
     for k, step in enumerate(graph):
         if step in ("gn", "gn_silu"):
-            h, fresh = gn_async(h, state["stats"], P, i, params["G"], params.get("eps", 1e-5),
+            h, fresh = gn_async(h, state["stats"][k], P, i, params["G"], params.get("eps", 1e-5),
                                 gn_mode, params.get("gamma"), params.get("beta"),
                                 "silu" if step == "gn_silu" else None)
-            new_stats[i] = fresh
-        elif step == "attn_proj":
+            new_stats[k][i] = fresh
+        elif step in ("attn_proj", "attn_proj_res"):
             tok = h.reshape(B, hb * W, C)
             ks_ = np.asarray(state["maps"][(k, "k")], dtype=F64).reshape(B, H * W, C)
             vs_ = np.asarray(state["maps"][(k, "v")], dtype=F64).reshape(B, H * W, C)
@@ -291,11 +295,13 @@ def displaced_layer(graph, params, x_patch, state, P, i, gn_mode=GN_CORRECTED):
             new_maps[(k, "k")] = stale_update(new_maps[(k, "k")], kf.reshape(B, hb, W, C), P, i)
             new_maps[(k, "v")] = stale_update(new_maps[(k, "v")], vf.reshape(B, hb, W, C), P, i)
             h = out.reshape(B, hb, W, C)
-        elif step == "conv":
+            if step == "attn_proj_res":
+                h = h + x_in
+        elif step in ("conv", "conv_res"):
             w, bias = next(conv_iter)
             out = conv3x3_halo(h, state["maps"][k], w, bias, P, i)
             new_maps[k] = stale_update(new_maps[k], h, P, i)
-            h = out
+            h = out + x_in if step == "conv_res" else out
         elif step == "attn":
             tok = h.reshape(B, hb * W, C)
             stale_tok = np.asarray(state["maps"][k], dtype=F64).reshape(B, H * W, C)
@@ -318,7 +324,7 @@ def displaced_step_all(graph, params, x_full, state, P, gn_mode=GN_CORRECTED):
     gathered to every device and become the next step's context.  So every
     patch i runs ``displaced_layer`` against the same previous-step ``state``,
     and the next state holds every patch's fresh band of each conv/attention
-    input map and every patch's fresh GroupNorm moments.
+    input map and every patch's fresh GroupNorm moments (per GroupNorm step).
 
     Returns (outputs, next_state): outputs is every graph step's full-map
     output [B][H][W][C] (float64, patches side by side).
@@ -327,20 +333,20 @@ def displaced_step_all(graph, params, x_full, state, P, gn_mode=GN_CORRECTED):
     B, H, W, C = x.shape
     h = H // P
     outputs = [np.empty((B, H, W, C), dtype=F64) for _ in graph]
-    next_stats = None if state["stats"] is None else np.array(state["stats"], dtype=F64, copy=True)
+    next_stats = {k: np.array(t, dtype=F64, copy=True) for k, t in state["stats"].items()}
     for i in range(P):
         outs, new_state = displaced_layer(graph, params, x[:, i * h:(i + 1) * h], state, P, i, gn_mode)
         for k, o in enumerate(outs):
             outputs[k][:, i * h:(i + 1) * h] = o
-        if next_stats is not None:
-            next_stats[i] = new_state["stats"][i]
+        for k in next_stats:
+            next_stats[k][i] = new_state["stats"][k][i]
     inputs = [x] + outputs[:-1]
     next_maps = {}
     proj_iter = iter(params.get("projs", []))
     for k, step in enumerate(graph):
-        if step in ("conv", "attn"):
+        if step in ("conv", "conv_res", "attn"):
             next_maps[k] = np.array(inputs[k], copy=True)
-        elif step == "attn_proj":
+        elif step in ("attn_proj", "attn_proj_res"):
             wq, bq, wk, bk, wv, bv, wo, bo = next(proj_iter)
             next_maps[(k, "k")] = linear(inputs[k], wk, bk)
             next_maps[(k, "v")] = linear(inputs[k], wv, bv)

@@ -111,36 +111,61 @@ def project(x, w, bias):
     return y + np.asarray(bias, dtype=F64) if bias is not None else y
 
 
-def sync_layer(graph, params, x, P):
+def sync_layer(graph, params, x, P, state_only=False):
     """Run the layer on the full map; returns (outputs, state) for the next step.
 
-    outputs: every step's full-map output.  state: "stats" = per-band moments
-    of the GroupNorm input, "maps" = {step index: full input map of that conv
-    or attention step; (step index, "k"/"v"): the projected K / V maps of an
-    attn_proj step}.
+    ``state_only``: stop once the last step's state entries are recorded, without computing
+    its output (the state a displaced step reads never depends on the layer's final output);
+    outputs then holds every step but the last.
+
+    Graph steps: "gn", "gn_silu", "conv", "attn", "attn_proj", and the residual forms
+    "conv_res" / "attn_proj_res" whose output adds the layer's own input x (the skip
+    connection of a ResNet or transformer block).
+    outputs: every step's full-map output.  state: "stats" = {step index: per-band moments
+    [P][B][G][2] of that GroupNorm step's input} (every GroupNorm site keeps its own table),
+    "maps" = {step index: full input map of that conv or attention step; (step index,
+    "k"/"v"): the projected K / V maps of an attn_proj step}.
     """
-    h = np.asarray(x, dtype=F64)
+    x = np.asarray(x, dtype=F64)
+    h = x
     outputs = []
-    state = {"stats": None, "maps": {}}
+    state = {"stats": {}, "maps": {}}
     conv_iter = iter(params.get("convs", []))
     proj_iter = iter(params.get("projs", []))
     for k, step in enumerate(graph):
-        if step == "attn_proj":
+        last = k == len(graph) - 1
+        if state_only and last:
+            if step in ("gn", "gn_silu"):
+                state["stats"][k] = band_moments(h, params["G"], P)
+            elif step in ("attn_proj", "attn_proj_res"):
+                wq, bq, wk, bk, wv, bv, wo, bo = next(proj_iter)
+                state["maps"][(k, "k")] = project(h, wk, bk)
+                state["maps"][(k, "v")] = project(h, wv, bv)
+            elif step in ("conv", "conv_res", "attn"):
+                state["maps"][k] = h
+            else:
+                raise ValueError(f"unknown step {step!r}")
+            break
+        if step in ("attn_proj", "attn_proj_res"):
             wq, bq, wk, bk, wv, bv, wo, bo = next(proj_iter)
             q, kk, vv = project(h, wq, bq), project(h, wk, bk), project(h, wv, bv)
             state["maps"][(k, "k")] = kk
             state["maps"][(k, "v")] = vv
             h = project(attention(q, kk, vv, params["heads"], params.get("scale")), wo, bo)
+            if step == "attn_proj_res":
+                h = h + x
             outputs.append(h)
             continue
         if step in ("gn", "gn_silu"):
-            state["stats"] = band_moments(h, params["G"], P)
+            state["stats"][k] = band_moments(h, params["G"], P)
             h = group_norm(h, params["G"], params.get("eps", 1e-5), params.get("gamma"),
                            params.get("beta"), "silu" if step == "gn_silu" else None)
-        elif step == "conv":
+        elif step in ("conv", "conv_res"):
             w, bias = next(conv_iter)
             state["maps"][k] = h
             h = conv3x3(h, w, bias)
+            if step == "conv_res":
+                h = h + x
         elif step == "attn":
             state["maps"][k] = h
             h = self_attention(h, params["heads"], params.get("scale"))

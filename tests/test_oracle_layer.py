@@ -26,6 +26,12 @@ GRAPHS = {
     "gn-attn": ("gn", "attn"),
     "gn-attn_proj-conv": ("gn", "attn_proj", "conv"),
     "gn-attn_proj": ("gn", "attn_proj"),
+    # SDXL-like blocks: a ResNet block (two GroupNorm sites, two convs, skip connection
+    # added to the second conv) and a transformer block (projected attention whose output
+    # projection adds the block input)
+    "resnet": ("gn_silu", "conv", "gn_silu", "conv_res"),
+    "transformer": ("gn", "attn_proj_res"),
+    "resnet-transformer": ("gn_silu", "conv", "gn_silu", "conv_res", "gn", "attn_proj_res"),
 }
 
 
@@ -39,25 +45,30 @@ def params_of(cfg, inp):
 
 
 def torch_sync(graph, params, x):
-    h = t64(x)
+    x0 = t64(x)
+    h = x0
     outs = []
     convs = iter(params["convs"])
     projs = iter(params.get("projs") or [])
     for step in graph:
-        if step == "attn_proj":
+        if step in ("attn_proj", "attn_proj_res"):
             wq, bq, wk, bk, wv, bv, wo, bo = (t64(a) for a in next(projs))
             B, H, W, C = h.shape
             tok = h.reshape(B, H * W, C)
             lin = torch.nn.functional.linear
             a = sdpa_tokens(lin(tok, wq, bq), lin(tok, wk, bk), lin(tok, wv, bv), params["heads"])
             h = lin(a, wo, bo).reshape(B, H, W, C)
+            if step == "attn_proj_res":
+                h = h + x0
         elif step.startswith("gn"):
             h = group_norm_nhwc(h, params["G"], params["eps"])
             if step == "gn_silu":
                 h = torch.nn.functional.silu(h)
-        elif step == "conv":
+        elif step in ("conv", "conv_res"):
             w, b = next(convs)
             h = conv2d_nhwc(h, w, b)
+            if step == "conv_res":
+                h = h + x0
         else:
             B, H, W, C = h.shape
             tok = h.reshape(B, H * W, C)
@@ -87,10 +98,14 @@ def test_sync_layer_matches_torch(gname):
     outs, state = oracle.sync_layer(cfg.graph, params, inp.x, cfg.P)
     for a, b in zip(outs, torch_sync(cfg.graph, params, inp.x)):
         np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
-    # the state holds every band's moments and each consumer's full input map
-    assert state["stats"].shape == (cfg.P, 1, cfg.G, 2)
-    expected = {k for k, s in enumerate(cfg.graph) if s in ("conv", "attn")}
-    expected |= {(k, kv) for k, s in enumerate(cfg.graph) if s == "attn_proj" for kv in ("k", "v")}
+    # the state holds every band's moments of each GroupNorm input (one table per GroupNorm
+    # step) and each consumer's full input map
+    assert set(state["stats"]) == {k for k, s in enumerate(cfg.graph) if s in ("gn", "gn_silu")}
+    for t in state["stats"].values():
+        assert t.shape == (cfg.P, 1, cfg.G, 2)
+    expected = {k for k, s in enumerate(cfg.graph) if s in ("conv", "conv_res", "attn")}
+    expected |= {(k, kv) for k, s in enumerate(cfg.graph) if s in ("attn_proj", "attn_proj_res")
+                 for kv in ("k", "v")}
     assert set(state["maps"]) == expected
 
 
@@ -132,11 +147,17 @@ def test_displaced_step_reads_stale_context(gname):
     ref = sync_outs[-1][:, i * h:(i + 1) * h]
     err = np.linalg.norm(outs[-1] - ref) / np.linalg.norm(ref)
     assert 1e-4 < err < 0.2, err
-    # the new state carries the fresh band and the fresh statistics of patch i
-    np.testing.assert_array_equal(new_state["stats"][i], oracle.gn_band_stats(inp.x[:, i * h:(i + 1) * h], cfg.G))
-    for j in range(cfg.P):
-        if j != i:
-            np.testing.assert_array_equal(new_state["stats"][j], prev["stats"][j])
+    # the new state carries the fresh band and the fresh statistics of patch i: the first
+    # GroupNorm step's table gets the moments of the layer input's band
+    k0 = min(new_state["stats"])
+    np.testing.assert_array_equal(new_state["stats"][k0][i],
+                                  oracle.gn_band_stats(inp.x[:, i * h:(i + 1) * h], cfg.G))
+    for k, t in new_state["stats"].items():
+        gin = inp.x[:, i * h:(i + 1) * h] if k == 0 else outs[k - 1]
+        np.testing.assert_array_equal(t[i], oracle.gn_band_stats(gin, cfg.G))
+        for j in range(cfg.P):
+            if j != i:
+                np.testing.assert_array_equal(t[j], prev["stats"][k][j])
     for k, m in new_state["maps"].items():
         np.testing.assert_array_equal(m[:, :i * h], prev["maps"][k][:, :i * h])
         np.testing.assert_array_equal(m[:, (i + 1) * h:], prev["maps"][k][:, (i + 1) * h:])
@@ -166,7 +187,9 @@ def test_step_all_with_current_state_is_sync(gname):
     outs, nxt = oracle.displaced_step_all(cfg.graph, params, inp.x, state, cfg.P)
     for k, (o, r) in enumerate(zip(outs, sync_outs)):
         np.testing.assert_allclose(o, r, rtol=1e-11, atol=1e-11, err_msg=f"step {k}")
-    np.testing.assert_allclose(nxt["stats"], state["stats"], rtol=1e-12, atol=1e-12)
+    assert set(nxt["stats"]) == set(state["stats"])
+    for k in state["stats"]:
+        np.testing.assert_allclose(nxt["stats"][k], state["stats"][k], rtol=1e-12, atol=1e-12)
     for k in state["maps"]:
         np.testing.assert_allclose(nxt["maps"][k], state["maps"][k], rtol=1e-11, atol=1e-11)
 
@@ -192,7 +215,7 @@ def test_step_all_next_state_is_gathered_fresh_inputs():
     params = params_of(cfg, inp)
     _, prev = oracle.sync_layer(cfg.graph, params, inp.x_prev, cfg.P)
     outs, nxt = oracle.displaced_step_all(cfg.graph, params, inp.x, prev, cfg.P)
-    np.testing.assert_allclose(nxt["stats"], oracle.band_moments(inp.x, cfg.G, cfg.P), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(nxt["stats"][0], oracle.band_moments(inp.x, cfg.G, cfg.P), rtol=1e-12, atol=1e-12)
     np.testing.assert_array_equal(nxt["maps"][1], outs[0])
     np.testing.assert_array_equal(nxt["maps"][2], outs[1])
     # and it differs from the previous state (the step did advance it)
@@ -237,3 +260,61 @@ def test_identity_projections_reduce_to_plain_attention(P, i):
     for a, b in zip(pouts, outs):
         np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
     np.testing.assert_allclose(pst["maps"][(1, "k")], st["maps"][1], rtol=0, atol=1e-12)
+
+
+def test_two_groupnorm_sites_keep_their_own_tables():
+    """A ResNet block normalises two different maps.  Each GroupNorm step reads and refreshes
+    its own statistics table: swapping the two tables of a warm-up state changes the
+    displaced result, and with the right tables the result is the synchronous one."""
+    graph = GRAPHS["resnet"]
+    cfg = small_cfg(graph)
+    inp = synth.layer_inputs(cfg, seed=31)
+    params = params_of(cfg, inp)
+    sync_outs, state = oracle.sync_layer(graph, params, inp.x, cfg.P)
+    assert set(state["stats"]) == {0, 2}
+    # the two sites normalise different maps, so their moments differ
+    assert np.abs(state["stats"][0] - state["stats"][2]).max() > 1e-3
+    i, h = 1, cfg.h
+    xb = inp.x[:, i * h:(i + 1) * h]
+    outs, _ = oracle.displaced_layer(graph, params, xb, state, cfg.P, i)
+    np.testing.assert_allclose(outs[-1], sync_outs[-1][:, i * h:(i + 1) * h], rtol=0, atol=1e-12)
+    swapped = dict(state, stats={0: state["stats"][2], 2: state["stats"][0]})
+    bad, _ = oracle.displaced_layer(graph, params, xb, swapped, cfg.P, i)
+    assert np.abs(bad[-1] - outs[-1]).max() > 1e-3
+
+
+@pytest.mark.parametrize("gname", ["resnet", "transformer"])
+def test_block_residual_is_the_block_input(gname):
+    """The residual steps add the layer's own input: subtracting it leaves the plain step."""
+    graph = GRAPHS[gname]
+    plain = tuple(s.replace("_res", "") for s in graph)
+    cfg = small_cfg(graph)
+    inp = synth.layer_inputs(cfg, seed=32)
+    params = params_of(cfg, inp)
+    _, prev = oracle.sync_layer(graph, params, inp.x_prev, cfg.P)
+    i, h = 2, cfg.h
+    xb = inp.x[:, i * h:(i + 1) * h]
+    outs, _ = oracle.displaced_layer(graph, params, xb, prev, cfg.P, i)
+    pouts, _ = oracle.displaced_layer(plain, params, xb, prev, cfg.P, i)
+    np.testing.assert_allclose(outs[-1] - xb, pouts[-1], rtol=0, atol=1e-12)
+    for a, b in zip(outs[:-1], pouts[:-1]):
+        np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("gname", list(GRAPHS))
+def test_state_only_sync_layer_gives_the_same_state(gname):
+    """The state-only synchronous pass (used for workloads whose full attention is too large
+    for the oracle) records exactly the state of the full pass."""
+    cfg = small_cfg(GRAPHS[gname])
+    inp = synth.layer_inputs(cfg, seed=33)
+    params = params_of(cfg, inp)
+    outs, state = oracle.sync_layer(cfg.graph, params, inp.x, cfg.P)
+    outs2, state2 = oracle.sync_layer(cfg.graph, params, inp.x, cfg.P, state_only=True)
+    assert len(outs2) == len(outs) - 1
+    for a, b in zip(outs2, outs):
+        np.testing.assert_array_equal(a, b)
+    assert set(state2["stats"]) == set(state["stats"]) and set(state2["maps"]) == set(state["maps"])
+    for k in state["stats"]:
+        np.testing.assert_array_equal(state2["stats"][k], state["stats"][k])
+    for k in state["maps"]:
+        np.testing.assert_array_equal(state2["maps"][k], state["maps"][k])
