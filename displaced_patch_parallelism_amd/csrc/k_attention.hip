@@ -84,6 +84,13 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// A 64-bit value the caller knows is the same in every lane, moved to scalar registers.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
 // 4 bf16 of V^T for the PV operand via the transposing LDS read (see the lane map below).
 __device__ __forceinline__ s16x4 tr_read(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
@@ -105,6 +112,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
     constexpr int STAGE = 16 * 1024;          // K tile 8 KB + V tile 8 KB
     constexpr int LOADS = 16 / WAVES;         // DMA loads (1 KB chunks) per wave per stage
     constexpr int QTW = 32 * WAVES;           // queries per workgroup
+    static_assert(16 % WAVES == 0 && WAVES >= 2 && (8 % LOADS) == 0, "a wave's loads are all K or all V");
     __shared__ __attribute__((aligned(1024))) char smem[STAGES * STAGE];
     // all arguments in SGPRs from the start: with them loaded lazily the kernel, at its VGPR
     // limit, kept reloading spilled values inside the tile loop
@@ -112,26 +120,28 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hsel = lane >> 5;
     // Workgroups are dispatched round-robin over the 8 XCDs (workgroup w on XCD w % 8).  Give
     // XCD x a contiguous run of the order (head, key split, query tile), query tile fastest:
     // the workgroups resident on an XCD then stream the same keys and values through its L2.
+    // Everything derived from the workgroup index is uniform: kept in scalar registers.
     const int total = gridDim.x;
     const int xcd = blockIdx.x & 7, within = blockIdx.x >> 3;
     const int lt = xcd * (total >> 3) + (xcd < (total & 7) ? xcd : (total & 7)) + within;
-    const int qt = lt % a.qtiles;
-    const int rest = lt / a.qtiles;
-    const int split = rest % a.kvsplit;
-    const int bh = rest / a.kvsplit;
-    const int b = bh / a.heads;
+    const int qt = __builtin_amdgcn_readfirstlane(lt % a.qtiles);
+    const int rest = __builtin_amdgcn_readfirstlane(lt / a.qtiles);
+    const int split = __builtin_amdgcn_readfirstlane(rest % a.kvsplit);
+    const int bh = __builtin_amdgcn_readfirstlane(rest / a.kvsplit);
+    const int b = __builtin_amdgcn_readfirstlane(bh / a.heads);
     const int e = bh - b * a.heads;
     const int myq = qt * QTW + wave * 32 + (lane & 31);
     const bool qvalid = myq < a.Nq;
     const int col0 = e * D;
 
-    // Q scaled by scale * log2(e) once (rounded to bf16), so S = K Q^T is already in the
-    // base-2 exponent domain
+    // Q as given (bf16, exact): the scores come out of the MFMAs unscaled and the scale
+    // (times log2 e, for the base-2 exponential) is applied in fp32 with the offset, one FMA
+    // per score, so no rounding is added to the inputs
     bf16x8 q0, q1, q2, q3;
     {
         uint4 r[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
@@ -141,40 +151,39 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
 #pragma unroll
             for (int j = 0; j < 4; ++j) r[j] = *(const uint4*)(qp + 16 * j);
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float f[8];
-            unpack8(r[j], f);
-#pragma unroll
-            for (int u = 0; u < 8; ++u) f[u] *= a.sc;
-            r[j] = pack8(f);
-        }
         q0 = __builtin_bit_cast(bf16x8, r[0]);
         q1 = __builtin_bit_cast(bf16x8, r[1]);
         q2 = __builtin_bit_cast(bf16x8, r[2]);
         q3 = __builtin_bit_cast(bf16x8, r[3]);
     }
+    const float sc = a.sc;
 
     const int t0 = (int)((int64_t)a.kv_tiles * split / a.kvsplit);
     const int t1 = (int)((int64_t)a.kv_tiles * (split + 1) / a.kvsplit);
     const int nt = t1 - t0;
 
-    // DMA lanes: wave w issues chunks w*LOADS+j (0..7 K rows, 8..15 V rows), 8 rows of 128 B per chunk.
-    // A tile wholly inside the fresh band or wholly in the stale map (all but at most two tiles
-    // per split) takes one wave-uniform base pointer plus a fixed per-lane offset; a tile that
-    // straddles a band edge or runs past the last key picks the buffer per row.
+    // DMA lanes: wave w issues chunks w*LOADS+j (0..7 K rows, 8..15 V rows), 8 rows of 128 B per
+    // chunk, so a wave loads only K or only V.  A tile wholly inside the fresh band or wholly in
+    // the stale map (all but at most two tiles per split) takes one wave-uniform base address
+    // (scalar arithmetic) plus a fixed 32-bit per-lane byte offset; a tile that straddles a band
+    // edge or runs past the last key picks the buffer per row.
     const int sub = lane >> 3;
     const int slot = lane & 7;
     const uint16_t* zero = (const uint16_t*)g_attn_zero;
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    int loff[LOADS];
+    const bool is_k = wave * LOADS < 8;
+    const uint16_t* fresh_buf = is_k ? a.k : a.v;
+    const uint16_t* stale_buf = is_k ? a.ks : a.vs;
+    uint32_t loffb[LOADS];
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
-        const int row = ((wave_u * LOADS + j) & 7) * 8 + sub;
-        loff[j] = row * a.C + col0 + (slot ^ (row & 7)) * 8;
+        const int row = ((wave * LOADS + j) & 7) * 8 + sub;
+        loffb[j] = (uint32_t)(row * a.C + col0 + (slot ^ (row & 7)) * 8) * 2u;
     }
-    const int64_t fresh_base = (int64_t)b * a.Nq - a.band0;   // token n of the band at fresh_base + n
-    const int64_t stale_base = (int64_t)b * a.N;
+    // token n of the band at fresh_tok + n (n in [band0, band0 + Nq)), of the map at stale_tok + n;
+    // both wave-uniform, kept in scalar registers
+    const uint64_t fresh_tok = uniform_u64((uint64_t)(fresh_buf + ((int64_t)b * a.Nq - a.band0) * a.C));
+    const uint64_t stale_tok = uniform_u64((uint64_t)(stale_buf + (int64_t)b * a.N * a.C));
+    const uint32_t row_bytes = (uint32_t)a.C * 2u;
 #define DPA_ISSUE(T, BUF)                                                                           \
     do {                                                                                            \
         char* st_ = smem + (BUF) * STAGE;                                                           \
@@ -182,21 +191,18 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
         const bool in_band_ = n0_ >= a.band0 && n0_ + KT <= a.band0 + a.Nq;                         \
         const bool in_stale_ = (n0_ + KT <= a.band0 || n0_ >= a.band0 + a.Nq) && n0_ + KT <= a.N;  \
         if (in_band_ || in_stale_) {                                                                \
-            _Pragma("unroll") for (int j = 0; j < LOADS; ++j) {                                     \
-                const int q_ = wave_u * LOADS + j;                                                  \
-                const uint16_t* buf_ = in_band_ ? (q_ < 8 ? a.k : a.v) : (q_ < 8 ? a.ks : a.vs);    \
-                const uint16_t* g_ = buf_ + ((in_band_ ? fresh_base : stale_base) + n0_) * a.C + loff[j]; \
-                __builtin_amdgcn_global_load_lds((const void*)g_, (lds_void*)(st_ + q_ * 1024), 16, 0, 0); \
-            }                                                                                       \
+            const char* base_ = (const char*)((in_band_ ? fresh_tok : stale_tok) +                  \
+                                              (uint64_t)(uint32_t)n0_ * row_bytes);                 \
+            _Pragma("unroll") for (int j = 0; j < LOADS; ++j)                                       \
+                __builtin_amdgcn_global_load_lds((const void*)(base_ + loffb[j]),                  \
+                                                 (lds_void*)(st_ + (wave * LOADS + j) * 1024), 16, 0, 0); \
         } else {                                                                                    \
             _Pragma("unroll") for (int j = 0; j < LOADS; ++j) {                                     \
-                const int q_ = wave_u * LOADS + j;                                                  \
+                const int q_ = wave * LOADS + j;                                                    \
                 const int row_ = (q_ & 7) * 8 + sub;                                                \
                 const int n_ = n0_ + row_;                                                          \
                 const int ch_ = (slot ^ (row_ & 7)) * 8;                                            \
-                const uint16_t* fr_ = q_ < 8 ? a.k : a.v;                                           \
-                const uint16_t* sl_ = q_ < 8 ? a.ks : a.vs;                                         \
-                const uint16_t* g_ = n_ < a.N ? kv_row(fr_, sl_, b, n_, a, col0 + ch_) : zero;      \
+                const uint16_t* g_ = n_ < a.N ? kv_row(fresh_buf, stale_buf, b, n_, a, col0 + ch_) : zero; \
                 __builtin_amdgcn_global_load_lds((const void*)g_, (lds_void*)(st_ + q_ * 1024), 16, 0, 0); \
             }                                                                                       \
         }                                                                                           \
@@ -220,14 +226,16 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
             voff[h][db] = 8192 + row * 128 + (((d >> 3) ^ (row & 7)) * 16) + (d & 7) * 2;
         }
 
-    // Online softmax with a lazily moved offset: the QK MFMAs start from C = -m_run, so they
-    // produce S - m_run directly and the exponent needs no subtraction.  m_run is set to the
-    // first tile's maximum and moved up to the running maximum only when some score exceeds
-    // it by more than kLazy (p <= 2^kLazy, harmless in fp32 sums and bf16 P); since m_run is
-    // always a score that occurred, the largest p of a row is >= 1.
-    f32x16 o0, o1, negm;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o0[i] = o1[i] = negm[i] = 0.f;
+    // Online softmax with a lazily moved offset m_run (base-2 units of scale * score):
+    // p = 2^(sc * s - m_run), the scale applied in fp32 by one FMA per score.  m_run is set to
+    // the first tile's maximum and moved up to the running maximum only when some score exceeds
+    // it by more than kLazy (p <= 2^kLazy, harmless in the fp32 sums and the bf16 P; the
+    // cross-half exchange happens only then); since m_run is always a score that occurred, the
+    // largest p of a row is >= 1.
+    f32x16 o0, o1;
+    const f32x16 zacc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    o0 = zacc;
+    o1 = zacc;
     float m_run = 0.f;
     float l_run = 0.f;
     bool first = true;
@@ -246,10 +254,11 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
         __syncthreads();
         const char* st = smem + (it % STAGES) * STAGE;
 
-        // S^T[key][query], keys kb*32 + 8q + 4*hsel + r in s_kb[4q + r]
+        // S^T[key][query] = K Q^T (unscaled; the MFMAs start from 0), keys kb*32 + 8q + 4*hsel + r
+        // in s_kb[4q + r]
         f32x16 s0, s1;
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + koff[0]), q0, negm, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + 4096 + koff[0]), q0, negm, 0, 0, 0);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + koff[0]), q0, zacc, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + 4096 + koff[0]), q0, zacc, 0, 0, 0);
         s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + koff[1]), q1, s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + 4096 + koff[1]), q1, s1, 0, 0, 0);
         s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + koff[2]), q2, s0, 0, 0, 0);
@@ -267,59 +276,58 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
                 if (off + 32 >= kvalid) s1[i] = -INFINITY;
             }
         }
-        // Exponentials against the current offset; the tile maximum (two independent chains of
-        // 3-input maxima, v_max3_f32, over this lane's half of the keys) only decides whether
-        // the offset must move, which is rare after the first tile: then the exponentials are
-        // taken from the kept scores against the moved offset instead.
-        f32x16 p0f, p1f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            p0f[i] = __builtin_amdgcn_exp2f(s0[i]);
-            p1f[i] = __builtin_amdgcn_exp2f(s1[i]);
-        }
+        // the tile maximum (two independent chains of 3-input maxima, v_max3_f32, over this
+        // lane's half of the keys) only decides whether the offset must move, which is rare after
+        // the first tile
         float mx0 = fmaxf(s0[0], s0[1]), mx1 = fmaxf(s1[0], s1[1]);
 #pragma unroll
         for (int i = 2; i < 16; i += 2) {
             mx0 = fmaxf(fmaxf(mx0, s0[i]), s0[i + 1]);
             mx1 = fmaxf(fmaxf(mx1, s1[i]), s1[i + 1]);
         }
-        float mx = fmaxf(mx0, mx1);
-        if (__builtin_amdgcn_ballot_w64(first || mx > kLazy)) {
-            mx = fmaxf(mx, __shfl_xor(mx, 32));     // max of S - m_run over the tile's keys
-            const float delta = first ? mx : fmaxf(mx, 0.f);
-            const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(-delta);
+        float mx = fmaxf(mx0, mx1) * sc;
+        if (__builtin_amdgcn_ballot_w64(first || mx > m_run + kLazy)) {
+            mx = fmaxf(mx, __shfl_xor(mx, 32));     // max of sc * s over the tile's keys
+            const float mnew = first ? mx : fmaxf(m_run, mx);
+            const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(m_run - mnew);
             l_run *= alpha;
             o0 *= alpha;
             o1 *= alpha;
-            m_run += delta;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                p0f[i] = __builtin_amdgcn_exp2f(s0[i] - delta);
-                p1f[i] = __builtin_amdgcn_exp2f(s1[i] - delta);
-                negm[i] = -m_run;
-            }
+            m_run = mnew;
             first = false;
         }
-        s0 = p0f;
-        s1 = p1f;
+        {
+            const float nm = -m_run;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], sc, nm));
+                s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], sc, nm));
+            }
+        }
         // P^T operands (keys 16u + 4*hsel + {0..3, 8..11}); the row sum adds the same bf16 values
         const bf16x8 p0 = pack_probs<0>(s0);
         const bf16x8 p1 = pack_probs<2>(s0);
         const bf16x8 p2 = pack_probs<0>(s1);
         const bf16x8 p3 = pack_probs<2>(s1);
-#define DPA_SUM(PV)                                                                                 \
+        float l_t;
+        {
+            float la = 0.f, lb = 0.f;
+#define DPA_SUM(PV, L)                                                                              \
     do {                                                                                            \
         const uint4 w_ = __builtin_bit_cast(uint4, PV);                                             \
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w_.x), ones, l_run, false); \
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w_.y), ones, l_run, false); \
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w_.z), ones, l_run, false); \
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w_.w), ones, l_run, false); \
+        L = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w_.x), ones, L, false);      \
+        L = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w_.y), ones, L, false);      \
+        L = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w_.z), ones, L, false);      \
+        L = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w_.w), ones, L, false);      \
     } while (0)
-        DPA_SUM(p0);
-        DPA_SUM(p1);
-        DPA_SUM(p2);
-        DPA_SUM(p3);
+            DPA_SUM(p0, la);
+            DPA_SUM(p1, lb);
+            DPA_SUM(p2, la);
+            DPA_SUM(p3, lb);
 #undef DPA_SUM
+            l_t = la + lb;
+        }
+        l_run += l_t;
 #define DPA_PV(U, PU)                                                                               \
     do {                                                                                            \
         const char* vb_ = st + (U) * 16 * 128;                                                      \
