@@ -76,6 +76,9 @@ def lib():
             "dp_attention_splice": [pp, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, sz, vp],
             "dp_stale_update": [pp, i32, vp, vp, vp],
             "dp_linear": [i32, i32, i32, i32, vp, ctypes.c_int64, vp, vp, vp, ctypes.c_int64, vp],
+            "dp_conv3x3_halo_residual": [pp, i32, i32, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp],
+            "dp_linear_residual": [i32, i32, i32, i32, vp, ctypes.c_int64, vp, vp, vp, ctypes.c_int64, vp,
+                                   ctypes.c_int64, vp],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -249,8 +252,9 @@ def dp_conv3x3_pack_weights(w, w_packed=None):
     torch = _torch()
     cout, cin = int(w.shape[0]), int(w.shape[3])
     _ptr(w, "w", (cout, 3, 3, cin))
-    if cin % 32:
-        raise DpError(DP_ERR_UNSUPPORTED, f"packed weights need Cin % 64 == 0 (Cin={cin})")
+    if cin % 64 or cout % 32:
+        raise DpError(DP_ERR_UNSUPPORTED, f"packed weights need Cin % 64 == 0 and Cout % 32 == 0 "
+                                          f"(Cin={cin}, Cout={cout})")
     shape = (3, cin // 32, 3, cout, 32)
     if w_packed is None:
         w_packed = torch.empty(shape, dtype=w.dtype, device=w.device)
@@ -282,6 +286,36 @@ def dp_conv3x3_halo_packed(patch: Patch, x_patch, x_stale, w_packed, bias=None, 
     return y_patch
 
 
+def dp_conv3x3_halo_residual(patch: Patch, x_patch, x_stale, w, bias=None, residual=None, y_patch=None,
+                             packed=None, ws=None):
+    """3x3 conv of patch i with stale halo rows plus a residual [B][h][W][Cout] added before
+    rounding.  ``w`` is [Cout][3][3][Cin], or the packed layout of dp_conv3x3_pack_weights
+    (detected from its 5-d shape unless ``packed`` says)."""
+    torch = _torch()
+    p = Patch(*patch)
+    dt = _dtype_code(x_patch)
+    dev = x_patch.device
+    if packed is None:
+        packed = w.dim() == 5
+    cout = int(w.shape[3]) if packed else int(w.shape[0])
+    wshape = (3, p.C // 32, 3, cout, 32) if packed else (cout, 3, 3, p.C)
+    _ptr(x_patch, "x_patch", (p.B, p.h, p.W, p.C))
+    _ptr(x_stale, "x_stale", (p.B, p.H, p.W, p.C), x_patch.dtype, dev)
+    _ptr(w, "w", wshape, x_patch.dtype, dev)
+    _ptr(bias, "bias", (cout,), torch.float32, dev)
+    _ptr(residual, "residual", (p.B, p.h, p.W, cout), x_patch.dtype, dev)
+    if y_patch is None:
+        y_patch = torch.empty((p.B, p.h, p.W, cout), dtype=x_patch.dtype, device=dev)
+    _ptr(y_patch, "y_patch", (p.B, p.h, p.W, cout), x_patch.dtype, dev)
+    need = workspace_bytes("conv", p, dt, cout)
+    wptr, wbytes = _workspace(need, dev, ws)
+    gp = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    _check(lib().dp_conv3x3_halo_residual(_cpatch(p), dt, cout, x_patch.data_ptr(), x_stale.data_ptr(),
+                                          w.data_ptr(), 1 if packed else 0, gp(bias), gp(residual),
+                                          y_patch.data_ptr(), wptr, wbytes, _stream(dev)))
+    return y_patch
+
+
 def dp_attention_splice(patch: Patch, heads, q_patch, k_patch, v_patch, k_stale, v_stale, o_patch=None,
                         scale=0.0, ws=None):
     """Attention of patch i's queries over spliced K/V; tensors are token-major [B][tokens][C]."""
@@ -310,6 +344,15 @@ def dp_linear(x, w, bias=None, y=None):
     """y = x W^T + bias over the last axis.  x: [..., K] whose rows may be strided (the last axis
     contiguous, the leading axes collapsible to one row stride), w: [N][K] contiguous, bias: [N]
     float32 or None; y: [..., N] with the same row structure, allocated if None."""
+    return _linear(x, w, bias, None, y)
+
+
+def dp_linear_residual(x, w, bias=None, r=None, y=None):
+    """y = x W^T + bias + r, the residual r [..., N] (rows as y) added before rounding."""
+    return _linear(x, w, bias, r, y)
+
+
+def _linear(x, w, bias, r, y):
     torch = _torch()
     dt = _dtype_code(x)
     dev = x.device
@@ -339,8 +382,17 @@ def dp_linear(x, w, bias=None, y=None):
     My, ldy = rows(y, "y", N)
     if My != M:
         raise ValueError(f"y has {My} rows, x has {M}")
-    _check(lib().dp_linear(dt, M, N, K, x.data_ptr(), ldx, w.data_ptr(),
-                           None if bias is None else bias.data_ptr(), y.data_ptr(), ldy, _stream(dev)))
+    bp = None if bias is None else bias.data_ptr()
+    if r is None:
+        _check(lib().dp_linear(dt, M, N, K, x.data_ptr(), ldx, w.data_ptr(), bp, y.data_ptr(), ldy, _stream(dev)))
+        return y
+    if r.dtype != x.dtype or r.device != dev:
+        raise TypeError("r must have x's dtype and device")
+    Mr, ldr = rows(r, "r", N)
+    if Mr != M:
+        raise ValueError(f"r has {Mr} rows, x has {M}")
+    _check(lib().dp_linear_residual(dt, M, N, K, x.data_ptr(), ldx, w.data_ptr(), bp, r.data_ptr(), ldr,
+                                    y.data_ptr(), ldy, _stream(dev)))
     return y
 
 

@@ -10,6 +10,11 @@ steps:
 * ``conv``     3x3 convolution whose halo rows come from the stale map
 * ``attn``     self-attention, queries from the fresh patch, keys/values from
                the stale map with the fresh patch spliced in
+* ``attn_proj`` the same with learned Q/K/V/O projections (the stale context is
+               the previous step's projected K/V cache)
+* ``conv_res`` / ``attn_proj_res``  the conv / projected attention with the
+               layer's own input added to the output (the skip connection of a
+               ResNet or transformer block of the U-Net)
 
 Shapes follow the SDXL-like levels the method is applied to (DistriFusion
 summary on atlas.scime.ai, "Experimental setup"; the 1024px and 3840px
@@ -51,34 +56,40 @@ class LayerConfig:
         return self.h * self.W
 
     @property
+    def n_conv(self) -> int:
+        return sum(s in ("conv", "conv_res") for s in self.graph)
+
+    @property
+    def n_proj(self) -> int:
+        return sum(s in ("attn_proj", "attn_proj_res") for s in self.graph)
+
+    @property
+    def n_attn(self) -> int:
+        return sum(s == "attn" for s in self.graph) + self.n_proj
+
+    @property
     def has_attn(self) -> bool:
-        return "attn" in self.graph or "attn_proj" in self.graph
+        return self.n_attn > 0
 
     @property
     def has_proj(self) -> bool:
-        return "attn_proj" in self.graph
+        return self.n_proj > 0
 
     @property
     def has_conv(self) -> bool:
-        return "conv" in self.graph
+        return self.n_conv > 0
 
     def conv_flops(self) -> float:
-        """Multiply-adds x2 of the patch's 3x3 conv (Cout = Cin = C)."""
-        if not self.has_conv:
-            return 0.0
-        return 2.0 * self.B * self.Nq * self.C * 9 * self.C
+        """Multiply-adds x2 of the patch's 3x3 convs (Cout = Cin = C), all of them."""
+        return self.n_conv * 2.0 * self.B * self.Nq * self.C * 9 * self.C
 
     def attn_flops(self) -> float:
-        """QK^T plus PV, 2 flops per multiply-add, every (query, key) pair."""
-        if not self.has_attn:
-            return 0.0
-        return 4.0 * self.B * self.heads * self.Nq * self.N * self.head_dim
+        """QK^T plus PV, 2 flops per multiply-add, every (query, key) pair, every attention."""
+        return self.n_attn * 4.0 * self.B * self.heads * self.Nq * self.N * self.head_dim
 
     def proj_flops(self) -> float:
-        """The four C x C projections (Q, K, V, O) of the patch's tokens."""
-        if not self.has_proj:
-            return 0.0
-        return 4 * 2.0 * self.B * self.Nq * self.C * self.C
+        """The four C x C projections (Q, K, V, O) of the patch's tokens, every projected attention."""
+        return self.n_proj * 4 * 2.0 * self.B * self.Nq * self.C * self.C
 
     def band_bytes(self) -> int:
         """Bytes of one activation band [B][h][W][C]."""
@@ -120,4 +131,23 @@ CONFIGS = {
         "c4bp", "bf16", B=1, H=240, W=240, C=640, G=32, P=8,
         graph=("gn", "attn_proj"), heads=10, head_dim=64,
         note="c4b with Q/K/V/O projections 640->640 and a projected K/V cache"),
+    # SDXL-like blocks of the U-Net: a ResNet block (two GroupNorm+SiLU -> conv pairs, the
+    # second conv adding the block input) and a transformer block's attention (GroupNorm,
+    # Q/K/V projections, attention over the projected K/V cache, output projection adding
+    # the block input)
+    "c1r": LayerConfig(
+        "c1r", "bf16", B=1, H=128, W=128, C=320, G=32, P=4,
+        graph=("gn_silu", "conv", "gn_silu", "conv_res"),
+        note="SDXL level-1 ResNet block at 1024px: (GN+SiLU, conv3x3 320->320) x 2, skip added"),
+    "c2t": LayerConfig(
+        "c2t", "bf16", B=1, H=64, W=64, C=640, G=32, P=4,
+        graph=("gn", "attn_proj_res"), heads=10, head_dim=64,
+        note="SDXL level-2 transformer-block attention: GN, Q/K/V 640->640, 10x64 attention, "
+             "O projection with the block input added"),
+}
+
+# Workloads made of several layers, each a patch step of its own (the one-GPU share of one
+# denoising step at that resolution touches every layer once).
+COMPOSITES = {
+    "c4": ("c4a", "c4b"),
 }

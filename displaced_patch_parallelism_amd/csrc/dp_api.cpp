@@ -95,6 +95,13 @@ dp_status check_gn(const dp_patch* p, dp_dtype dt, int32_t G, dp::Geom* g) {
     // a block holds one thread per 16-byte channel vector of a token: at most 1024 of them
     if (g->C / vec > 1024)
         return fail(DP_ERR_UNSUPPORTED, "GroupNorm supports C <= %d for this dtype (C=%d)", 1024 * vec, g->C);
+    // the normalising block holds at least one thread per group, and both kernels' blocks must
+    // fit 1024 threads and their LDS; rejected here, so nothing is enqueued
+    const dp::GnPlan plan = dp::plan_groupnorm(*g, G, dt == DP_BF16);
+    if (G > 1024 || plan.threads > 1024 || plan.threads_stats > 1024 ||
+        dp::gn_stats_lds_bytes(*g, plan) > dp::kMaxGnLds || dp::gn_apply_lds_bytes(*g, plan, G) > dp::kMaxGnLds)
+        return fail(DP_ERR_UNSUPPORTED, "GroupNorm with G=%d groups over C=%d channels needs a block of more "
+                    "than 1024 threads or more than 64 KB of LDS (G <= 1024 is required)", G, g->C);
     return DP_OK;
 }
 
@@ -226,8 +233,8 @@ dp_status dp_conv3x3_halo_ws(const dp_patch* p, dp_dtype dtype, int32_t Cout, si
 namespace {
 
 dp_status conv_call(const dp_patch* p, dp_dtype dtype, int32_t Cout, const void* x_patch, const void* x_stale,
-                    const void* w, bool w_packed, const float* bias, void* y_patch, void* ws, size_t ws_bytes,
-                    hipStream_t stream, const char* name) {
+                    const void* w, bool w_packed, const float* bias, const void* residual, void* y_patch,
+                    void* ws, size_t ws_bytes, hipStream_t stream, const char* name) {
     dp::Geom g;
     DP_TRY(check_conv(p, dtype, Cout, &g));
     if (w_packed && dtype != DP_BF16) return fail(DP_ERR_UNSUPPORTED, "%s: packed weights are bf16 only", name);
@@ -235,6 +242,7 @@ dp_status conv_call(const dp_patch* p, dp_dtype dtype, int32_t Cout, const void*
     DP_NEED(x_stale, "x_stale");
     DP_NEED(w, w_packed ? "w_packed" : "w");
     DP_OPT(bias, "bias");
+    DP_OPT(residual, "residual");
     DP_NEED(y_patch, "y_patch");
     const dp::ConvPlan plan = dp::plan_conv(g, Cout, dtype == DP_BF16);
     if (ws_bytes < plan.ws_bytes)
@@ -247,13 +255,13 @@ dp_status conv_call(const dp_patch* p, dp_dtype dtype, int32_t Cout, const void*
     const size_t w_bytes = (size_t)Cout * 9 * g.C * es;
     if (overlaps(y_patch, out_band, x_patch, in_band) || overlaps(y_patch, out_band, x_stale, in_map) ||
         overlaps(y_patch, out_band, w, w_bytes) || overlaps(y_patch, out_band, bias, Cout * sizeof(float)) ||
-        overlaps(y_patch, out_band, ws, plan.ws_bytes))
+        overlaps(y_patch, out_band, ws, plan.ws_bytes) || overlaps(y_patch, out_band, residual, out_band))
         return fail(DP_ERR_ARG, "y_patch overlaps an input or the workspace");
     if (plan.ws_bytes && (overlaps(ws, plan.ws_bytes, x_patch, in_band) || overlaps(ws, plan.ws_bytes, x_stale, in_map) ||
-                          overlaps(ws, plan.ws_bytes, w, w_bytes)))
+                          overlaps(ws, plan.ws_bytes, w, w_bytes) || overlaps(ws, plan.ws_bytes, residual, out_band)))
         return fail(DP_ERR_ARG, "workspace overlaps an input");
     return hip_status(dp::launch_conv(g, plan, dtype == DP_BF16, Cout, x_patch, x_stale, w, w_packed, bias,
-                                      y_patch, ws, stream),
+                                      residual, y_patch, ws, stream),
                       name);
 }
 
@@ -264,7 +272,7 @@ extern "C" {
 dp_status dp_conv3x3_halo(const dp_patch* p, dp_dtype dtype, int32_t Cout, const void* x_patch,
                           const void* x_stale, const void* w, const float* bias, void* y_patch,
                           void* ws, size_t ws_bytes, hipStream_t stream) {
-    return conv_call(p, dtype, Cout, x_patch, x_stale, w, false, bias, y_patch, ws, ws_bytes, stream,
+    return conv_call(p, dtype, Cout, x_patch, x_stale, w, false, bias, nullptr, y_patch, ws, ws_bytes, stream,
                      "dp_conv3x3_halo launch");
 }
 
@@ -290,8 +298,17 @@ dp_status dp_conv3x3_pack_weights(dp_dtype dtype, int32_t Cin, int32_t Cout, con
 dp_status dp_conv3x3_halo_packed(const dp_patch* p, dp_dtype dtype, int32_t Cout, const void* x_patch,
                                  const void* x_stale, const void* w_packed, const float* bias, void* y_patch,
                                  void* ws, size_t ws_bytes, hipStream_t stream) {
-    return conv_call(p, dtype, Cout, x_patch, x_stale, w_packed, true, bias, y_patch, ws, ws_bytes, stream,
+    return conv_call(p, dtype, Cout, x_patch, x_stale, w_packed, true, bias, nullptr, y_patch, ws, ws_bytes, stream,
                      "dp_conv3x3_halo_packed launch");
+}
+
+dp_status dp_conv3x3_halo_residual(const dp_patch* p, dp_dtype dtype, int32_t Cout, const void* x_patch,
+                                   const void* x_stale, const void* w, int32_t w_packed, const float* bias,
+                                   const void* residual, void* y_patch, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+    if (w_packed != 0 && w_packed != 1) return fail(DP_ERR_ARG, "w_packed must be 0 or 1 (got %d)", w_packed);
+    return conv_call(p, dtype, Cout, x_patch, x_stale, w, w_packed == 1, bias, residual, y_patch, ws, ws_bytes,
+                     stream, "dp_conv3x3_halo_residual launch");
 }
 
 dp_status dp_attention_splice_ws(const dp_patch* p, dp_dtype dtype, int32_t heads, int32_t head_dim,
@@ -337,30 +354,55 @@ dp_status dp_attention_splice(const dp_patch* p, dp_dtype dtype, int32_t heads, 
                       "dp_attention_splice launch");
 }
 
-dp_status dp_linear(dp_dtype dtype, int32_t M, int32_t N, int32_t K, const void* x, int64_t ldx, const void* w,
-                    const float* bias, void* y, int64_t ldy, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+dp_status linear_call(dp_dtype dtype, int32_t M, int32_t N, int32_t K, const void* x, int64_t ldx, const void* w,
+                      const float* bias, const void* r, int64_t ldr, void* y, int64_t ldy, hipStream_t stream,
+                      const char* name) {
     if (dtype != DP_F32 && dtype != DP_BF16) return fail(DP_ERR_ARG, "unknown dtype %d", (int)dtype);
     if (M < 0 || N < 1 || K < 1) return fail(DP_ERR_ARG, "need M >= 0, N >= 1, K >= 1 (got %d, %d, %d)", M, N, K);
     if (ldx < K || ldy < N) return fail(DP_ERR_ARG, "row strides must cover a row (ldx=%lld K=%d ldy=%lld N=%d)",
                                         (long long)ldx, K, (long long)ldy, N);
-    if ((int64_t)M * ldx > ((int64_t)1 << 40) || (int64_t)M * ldy > ((int64_t)1 << 40))
+    if (r && ldr < N) return fail(DP_ERR_ARG, "residual row stride must cover a row (ldr=%lld N=%d)",
+                                  (long long)ldr, N);
+    if ((int64_t)M * ldx > ((int64_t)1 << 40) || (int64_t)M * ldy > ((int64_t)1 << 40) ||
+        (r && (int64_t)M * ldr > ((int64_t)1 << 40)))
         return fail(DP_ERR_ARG, "matrix too large");
-    if (dtype == DP_BF16 && (K % 64 != 0 || N % 8 != 0 || ldx % 8 != 0 || ldy % 8 != 0))
-        return fail(DP_ERR_UNSUPPORTED, "bf16 linear needs K %% 64 == 0 and N, ldx, ldy multiples of 8 "
+    if (dtype == DP_BF16 && (K % 64 != 0 || N % 8 != 0 || ldx % 8 != 0 || ldy % 8 != 0 || (r && ldr % 8 != 0)))
+        return fail(DP_ERR_UNSUPPORTED, "bf16 linear needs K %% 64 == 0 and N, ldx, ldy (and ldr) multiples of 8 "
                     "(K=%d N=%d ldx=%lld ldy=%lld)", K, N, (long long)ldx, (long long)ldy);
-    if (M == 0) return ok();   // nothing to compute; x and y may be NULL
+    if (M == 0) return ok();   // nothing to compute; x, y and r may be NULL
     DP_NEED(x, "x");
     DP_NEED(w, "w");
     DP_OPT(bias, "bias");
+    DP_OPT(r, "residual");
     DP_NEED(y, "y");
     const size_t es = elem_size(dtype);
-    const size_t xb = M ? ((size_t)(M - 1) * ldx + K) * es : 0;
-    const size_t yb = M ? ((size_t)(M - 1) * ldy + N) * es : 0;
+    const size_t xb = ((size_t)(M - 1) * ldx + K) * es;
+    const size_t yb = ((size_t)(M - 1) * ldy + N) * es;
+    const size_t rb = r ? ((size_t)(M - 1) * ldr + N) * es : 0;
     const size_t wb = (size_t)N * K * es;
-    if (overlaps(y, yb, x, xb) || overlaps(y, yb, w, wb) || overlaps(y, yb, bias, bias ? (size_t)N * 4 : 0))
+    if (overlaps(y, yb, x, xb) || overlaps(y, yb, w, wb) || overlaps(y, yb, bias, bias ? (size_t)N * 4 : 0) ||
+        overlaps(y, yb, r, rb))
         return fail(DP_ERR_ARG, "y overlaps an input");
-    return hip_status(dp::launch_linear(dtype == DP_BF16, M, N, K, x, ldx, w, bias, y, ldy, stream),
-                      "dp_linear launch");
+    return hip_status(dp::launch_linear(dtype == DP_BF16, M, N, K, x, ldx, w, bias, r, ldr, y, ldy, stream), name);
+}
+
+}  // namespace
+
+extern "C" {
+
+dp_status dp_linear(dp_dtype dtype, int32_t M, int32_t N, int32_t K, const void* x, int64_t ldx, const void* w,
+                    const float* bias, void* y, int64_t ldy, hipStream_t stream) {
+    return linear_call(dtype, M, N, K, x, ldx, w, bias, nullptr, 0, y, ldy, stream, "dp_linear launch");
+}
+
+dp_status dp_linear_residual(dp_dtype dtype, int32_t M, int32_t N, int32_t K, const void* x, int64_t ldx,
+                             const void* w, const float* bias, const void* r, int64_t ldr, void* y, int64_t ldy,
+                             hipStream_t stream) {
+    return linear_call(dtype, M, N, K, x, ldx, w, bias, r, ldr, y, ldy, stream, "dp_linear_residual launch");
 }
 
 }  // extern "C"

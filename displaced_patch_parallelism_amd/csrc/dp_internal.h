@@ -43,6 +43,11 @@ struct GnPlan {
     size_t ws_bytes;
 };
 GnPlan plan_groupnorm(const Geom& g, int G, bool bf16);
+// Dynamic LDS bytes of the two GroupNorm kernels under a plan (the host rejects plans whose
+// blocks exceed 1024 threads or whose LDS exceeds kMaxGnLds before anything is enqueued).
+constexpr size_t kMaxGnLds = 64 * 1024;
+size_t gn_stats_lds_bytes(const Geom& g, const GnPlan& plan);
+size_t gn_apply_lds_bytes(const Geom& g, const GnPlan& plan, int G);
 hipError_t launch_groupnorm(const Geom& g, const GnPlan& plan, bool bf16, int G, float eps, int mode,
                             int act, const void* x, const float* stale_stats, const float* gamma,
                             const float* beta, float* fresh_stats_out, void* y, void* ws,
@@ -59,9 +64,10 @@ struct ConvPlan {
     size_t ws_bytes;
 };
 ConvPlan plan_conv(const Geom& g, int Cout, bool bf16);
+// res: optional residual [B][h][W][Cout] added before the output is rounded.
 hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout, const void* x_patch,
-                       const void* x_stale, const void* w, bool w_packed, const float* bias, void* y, void* ws,
-                       hipStream_t stream);
+                       const void* x_stale, const void* w, bool w_packed, const float* bias, const void* res,
+                       void* y, void* ws, hipStream_t stream);
 // bf16 weights [Cout][3][3][Cin] -> packed [3][Cin/32][3][Cout][32] (Cin % 32 == 0)
 hipError_t launch_conv_pack(int Cin, int Cout, const void* w, void* w_packed, hipStream_t stream);
 
@@ -80,7 +86,9 @@ hipError_t launch_attention(const Geom& g, const AttnPlan& plan, bool bf16, int 
                             hipStream_t stream);
 
 // ---- learned projections: y = x W^T + bias ----------------------------------
+// r: optional residual [M][N] (row stride ldr) added before the output is rounded.
 hipError_t launch_linear(bool bf16, int M, int N, int K, const void* x, int64_t ldx, const void* w,
-                         const float* bias, void* y, int64_t ldy, hipStream_t stream);
+                         const float* bias, const void* r, int64_t ldr, void* y, int64_t ldy,
+                         hipStream_t stream);
 
 }  // namespace dp

@@ -40,6 +40,8 @@
 //   workgroups until about 256 of them run, the fp32 partials summed in split
 //   order by a second kernel.  Every sum has a fixed order, so results are
 //   deterministic.
+//   An optional residual (the skip connection of a ResNet block's second conv) is added
+//   to acc + bias in fp32 before the single rounding to bf16.
 // f32 path: one thread per output element (correctness path for small maps).
 
 #include "dp_device.h"
@@ -57,6 +59,7 @@ struct ConvArgs {
     const uint16_t* xs;
     const uint16_t* w;
     const float* bias;
+    const uint16_t* res;   // residual [B][h][W][Cout] added before rounding, or null
     uint16_t* y;
     float* part;
     int B, H, W, Cin, Cout, h, r0;
@@ -313,9 +316,47 @@ __device__ __forceinline__ void conv_tile_body(const ConvArgs& a, char* smem) {
     __syncthreads();   // ring no longer read: reuse it for the output tile
 
     // acc[i][n][r] = D[pixel 16i + 4(l>>4) + r of the wave][channel 16n + (l&15) of the wave]
-    uint16_t* tile = (uint16_t*)smem;    // [PX pixels][BN] bf16, pixel = tile row * 32 + column
     const int ecol = lane & 15;
     const int erow = 4 * (lane >> 4);
+    if (a.res) {
+        // acc + bias staged in fp32, one channel half (the waves of wn = pass) at a time (the
+        // whole fp32 tile would not fit the ring); the residual is added before rounding
+        float* ft = (float*)smem;            // [PX pixels][80 + 4] fp32 (padded pitch)
+        constexpr int FP = 84;
+        static_assert(PX * FP * 4 <= STAGES * S::BYTES, "fp32 half tile fits the ring");
+        for (int pass = 0; pass < 2; ++pass) {
+            if (pass) __syncthreads();       // the previous half has been read
+            if (wn == pass) {
+#pragma unroll
+                for (int n = 0; n < 5; ++n) {
+                    const int ch = n * 16 + ecol;
+                    const float bv = (a.bias && n0 + pass * 80 + ch < a.Cout) ? a.bias[n0 + pass * 80 + ch] : 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) ft[(wm * 64 + i * 16 + erow + r) * FP + ch] = acc[i][n][r] + bv;
+                }
+            }
+            __syncthreads();
+            for (int q = tid; q < PX * 10; q += 64 * NW) {
+                const int px = q / 10, c8 = q - px * 10;
+                const int y = ty0 + (px >> 5), x = tx0 + (px & 31), co = n0 + pass * 80 + c8 * 8;
+                if (y < a.h && x < a.W && co < a.Cout) {
+                    const int64_t o = (((int64_t)bb * a.h + y) * a.W + x) * a.Cout + co;
+                    const float4 lo = *(const float4*)(ft + px * FP + c8 * 8);
+                    const float4 hi = *(const float4*)(ft + px * FP + c8 * 8 + 4);
+                    float f[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                    float rv[8];
+                    unpack8(*(const uint4*)(a.res + o), rv);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) f[e] += rv[e];
+                    *(uint4*)(a.y + o) = pack8(f);
+                }
+            }
+        }
+        return;
+    }
+    uint16_t* tile = (uint16_t*)smem;    // [PX pixels][BN] bf16, pixel = tile row * 32 + column
 #pragma unroll
     for (int n = 0; n < 5; ++n) {
         const int ch = wn * 80 + n * 16 + ecol;
@@ -520,6 +561,13 @@ __global__ __launch_bounds__(512) void conv3x3_bf16_halo_wave8_kernel(ConvArgs a
                 if (a.bias) {
                     v.x += bq[k].x; v.y += bq[k].y; v.z += bq[k].z; v.w += bq[k].w;
                 }
+                if (a.res) {
+                    const uint2 rv = *(const uint2*)(a.res + o);
+                    v.x += __uint_as_float(rv.x << 16);
+                    v.y += __uint_as_float(rv.x & 0xffff0000u);
+                    v.z += __uint_as_float(rv.y << 16);
+                    v.w += __uint_as_float(rv.y & 0xffff0000u);
+                }
                 uint2 ov;
                 ov.x = pack_bf16x2(v.x, v.y);
                 ov.y = pack_bf16x2(v.z, v.w);
@@ -531,10 +579,12 @@ __global__ __launch_bounds__(512) void conv3x3_bf16_halo_wave8_kernel(ConvArgs a
     }
 }
 
-// y[m][co] = bf16(bias[co] + sum_s part[s][m][co]), summed in split order.  The splits are
-// loaded 8 at a time, all in flight before any is added (a plain loop waits out every load).
+// y[m][co] = bf16(bias[co] + sum_s part[s][m][co] (+ res[m][co])), summed in split order.  The
+// splits are loaded 8 at a time, all in flight before any is added (a plain loop waits out
+// every load).
 __global__ __launch_bounds__(256) void conv_splitk_reduce_kernel(const float* __restrict__ part,
                                                                  const float* __restrict__ bias,
+                                                                 const uint16_t* __restrict__ res,
                                                                  uint16_t* __restrict__ y, int64_t total4,
                                                                  int Cout, int ksplit) {
     const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -564,6 +614,13 @@ __global__ __launch_bounds__(256) void conv_splitk_reduce_kernel(const float* __
         s.z += bv.z;
         s.w += bv.w;
     }
+    if (res) {
+        const uint2 rv = *(const uint2*)(res + i);
+        s.x += __uint_as_float(rv.x << 16);
+        s.y += __uint_as_float(rv.x & 0xffff0000u);
+        s.z += __uint_as_float(rv.y << 16);
+        s.w += __uint_as_float(rv.y & 0xffff0000u);
+    }
     uint2 o;
     o.x = pack_bf16x2(s.x, s.y);
     o.y = pack_bf16x2(s.z, s.w);
@@ -574,6 +631,7 @@ __global__ __launch_bounds__(256) void conv3x3_f32_direct_kernel(const float* __
                                                                  const float* __restrict__ xs,
                                                                  const float* __restrict__ w,
                                                                  const float* __restrict__ bias,
+                                                                 const float* __restrict__ res,
                                                                  float* __restrict__ y, int B, int H, int W,
                                                                  int Cin, int Cout, int h, int r0) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -597,6 +655,7 @@ __global__ __launch_bounds__(256) void conv3x3_f32_direct_kernel(const float* __
             for (int c = 0; c < Cin; ++c) acc = fmaf(wp[c], src[c], acc);
         }
     }
+    if (res) acc += res[idx];
     y[idx] = acc;
 }
 
@@ -678,15 +737,15 @@ hipError_t launch_conv_pack(int Cin, int Cout, const void* w, void* w_packed, hi
 }
 
 hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout, const void* x_patch,
-                       const void* x_stale, const void* w, bool w_packed, const float* bias, void* y, void* ws,
-                       hipStream_t stream) {
+                       const void* x_stale, const void* w, bool w_packed, const float* bias, const void* res,
+                       void* y, void* ws, hipStream_t stream) {
     if (!bf16) {
         const int64_t total = (int64_t)g.B * g.h * g.W * Cout;
         const int64_t blocks = (total + 255) / 256;
         if (!grid_fits(blocks)) return hipErrorInvalidConfiguration;
         conv3x3_f32_direct_kernel<<<(unsigned)blocks, 256, 0, stream>>>(
-            (const float*)x_patch, (const float*)x_stale, (const float*)w, bias, (float*)y, g.B, g.H, g.W, g.C, Cout,
-            g.h, g.r0);
+            (const float*)x_patch, (const float*)x_stale, (const float*)w, bias, (const float*)res, (float*)y, g.B,
+            g.H, g.W, g.C, Cout, g.h, g.r0);
         return hipGetLastError();
     }
     ConvArgs a;
@@ -694,6 +753,7 @@ hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout,
     a.xs = (const uint16_t*)x_stale;
     a.w = (const uint16_t*)w;
     a.bias = bias;
+    a.res = (const uint16_t*)res;
     a.y = (uint16_t*)y;
     a.part = (float*)ws;
     a.B = g.B;
@@ -724,7 +784,7 @@ hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout,
         conv3x3_bf16_halo_wave8_kernel<<<grid, 512, 0, stream>>>(a);
     if (plan.ksplit > 1) {
         conv_splitk_reduce_kernel<<<(unsigned)((total4 + 255) / 256), 256, 0, stream>>>(
-            (const float*)ws, bias, (uint16_t*)y, total4, Cout, plan.ksplit);
+            (const float*)ws, bias, (const uint16_t*)res, (uint16_t*)y, total4, Cout, plan.ksplit);
     }
     return hipGetLastError();
 }

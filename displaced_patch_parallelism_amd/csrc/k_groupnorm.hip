@@ -341,7 +341,7 @@ hipError_t launch_gn_typed(const Geom& g, const GnPlan& plan, GnApplyArgs a, flo
     // statistics over the plan's token split
     {
         dim3 grid((unsigned)plan.nblk, (unsigned)g.B);
-        const size_t shmem = (size_t)2 * plan.rows_stats * g.C * sizeof(float);
+        const size_t shmem = gn_stats_lds_bytes(g, plan);
         gn_stats_kernel<BF16><<<grid, plan.threads_stats, shmem, stream>>>(a.x, a.tokens, g.C, a.G, plan.vpt,
                                                                           plan.rows_stats,
                                                                     plan.tok_per_blk, partial);
@@ -350,9 +350,7 @@ hipError_t launch_gn_typed(const Geom& g, const GnPlan& plan, GnApplyArgs a, flo
     // block per batch
     a.tok_per_blk = plan.tok_per_blk_apply;
     const int64_t nb = a.y ? plan.nblk_apply : 1;
-    const size_t pg = (size_t)g.P * a.G;
-    const size_t shmem = ((size_t)(plan.threads / a.G) * a.G + a.G + (pg <= (size_t)kStaleLds ? pg : 0)) *
-                         sizeof(float2);
+    const size_t shmem = gn_apply_lds_bytes(g, plan, a.G);
     const dim3 grid_a((unsigned)nb, (unsigned)g.B);
     const bool pr16 = plan.nblk > 8 * (plan.threads / a.G);
     if (plan.tpt_apply == 1) {
@@ -369,6 +367,15 @@ hipError_t launch_gn_typed(const Geom& g, const GnPlan& plan, GnApplyArgs a, flo
 }
 
 }  // namespace
+
+size_t gn_stats_lds_bytes(const Geom& g, const GnPlan& plan) {
+    return (size_t)2 * plan.rows_stats * g.C * sizeof(float);
+}
+
+size_t gn_apply_lds_bytes(const Geom& g, const GnPlan& plan, int G) {
+    const size_t pg = (size_t)g.P * G;
+    return ((size_t)(plan.threads / G) * G + G + (pg <= (size_t)kStaleLds ? pg : 0)) * sizeof(float2);
+}
 
 GnPlan plan_groupnorm(const Geom& g, int G, bool bf16) {
     GnPlan p{};

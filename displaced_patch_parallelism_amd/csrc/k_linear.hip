@@ -11,8 +11,10 @@
 // tile of 64 is one 128-byte line per row; tiles stream global -> LDS with
 // direct-to-LDS loads (global_load_lds_dwordx4, lane l fills the l-th 16-byte
 // slot of a 1 KB run; chunk c of row r at slot c ^ (r & 7)) through a 2-stage
-// ring.  4 waves in a 2 x 2 grid; the output tile is staged in LDS for
-// coalesced 16-byte stores with the bias added.  Workgroups are renumbered so
+// ring.  4 waves in a 2 x 2 grid; the output tile (acc + bias, fp32) is staged in
+// LDS for coalesced 16-byte stores; an optional residual r (the skip connection
+// of a transformer block's output projection) is added there before the single
+// rounding to bf16.  Workgroups are renumbered so
 // each XCD walks a contiguous run of row tiles (consecutive tiles share W).
 // f32 path: one thread per output element.
 
@@ -36,8 +38,9 @@ struct LinArgs {
     const uint16_t* x;
     const uint16_t* w;
     const float* bias;
+    const uint16_t* r;       // residual [M][N] (row stride ldr) or null
     uint16_t* y;
-    int64_t ldx, ldy;
+    int64_t ldx, ldy, ldr;
     int M, N, K;
     int mtiles, ntiles;
 };
@@ -52,7 +55,9 @@ __global__ __launch_bounds__(256) void linear_bf16_kernel(LinArgs a) {
     constexpr int STAGE = LOADS * 1024;
     constexpr int WM = BM / 2, WN = BN / 2;       // wave tile
     constexpr int FM = WM / 16, FN = WN / 16;     // 16x16 blocks per wave
-    constexpr int SMEM = 2 * STAGE > BM * BN * 2 ? 2 * STAGE : BM * BN * 2;
+    constexpr int TP = BN + 4;                    // fp32 output-tile pitch (padded: rows 4 apart
+                                                  // would share banks)
+    constexpr int SMEM = 2 * STAGE > BM * TP * 4 ? 2 * STAGE : BM * TP * 4;
     __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
     const int tid = threadIdx.x;
@@ -135,7 +140,7 @@ __global__ __launch_bounds__(256) void linear_bf16_kernel(LinArgs a) {
     __syncthreads();   // ring no longer read: reuse it for the output tile
 
     // acc[i][n][r] = D[row 16i + 4(l>>4) + r of the wave][column 16n + (l&15) of the wave]
-    uint16_t* tile = (uint16_t*)smem;   // [BM][BN] bf16
+    float* tile = (float*)smem;   // [BM][TP] fp32: acc + bias
     const int ecol = lane & 15, erow = 4 * (lane >> 4);
 #pragma unroll
     for (int n = 0; n < FN; ++n) {
@@ -144,21 +149,33 @@ __global__ __launch_bounds__(256) void linear_bf16_kernel(LinArgs a) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) tile[(wm * WM + i * 16 + erow + r) * BN + c] = f32_to_bf16(acc[i][n][r] + bv);
+            for (int r = 0; r < 4; ++r) tile[(wm * WM + i * 16 + erow + r) * TP + c] = acc[i][n][r] + bv;
     }
     __syncthreads();
-    constexpr int CPR = BN * 2 / 16;   // 16-byte chunks per output row
+    constexpr int CPR = BN / 8;   // 8-column (16-byte) output chunks per row
     for (int q = tid; q < BM * CPR; q += 256) {
-        const int r = q / CPR, c16 = q - r * CPR;
-        const int m = m0 + r, n = n0 + c16 * 8;
-        if (m < a.M && n < a.N) *(uint4*)(a.y + (int64_t)m * a.ldy + n) = *(const uint4*)(tile + r * BN + c16 * 8);
+        const int r = q / CPR, c8 = q - r * CPR;
+        const int m = m0 + r, n = n0 + c8 * 8;
+        if (m < a.M && n < a.N) {
+            const float4 lo = *(const float4*)(tile + r * TP + c8 * 8);
+            const float4 hi = *(const float4*)(tile + r * TP + c8 * 8 + 4);
+            float f[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            if (a.r) {
+                float rv[8];
+                unpack8(*(const uint4*)(a.r + (int64_t)m * a.ldr + n), rv);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[e] += rv[e];
+            }
+            *(uint4*)(a.y + (int64_t)m * a.ldy + n) = pack8(f);
+        }
     }
 }
 
 __global__ __launch_bounds__(256) void linear_f32_kernel(const float* __restrict__ x, int64_t ldx,
                                                          const float* __restrict__ w,
-                                                         const float* __restrict__ bias, float* __restrict__ y,
-                                                         int64_t ldy, int M, int N, int K) {
+                                                         const float* __restrict__ bias,
+                                                         const float* __restrict__ r, int64_t ldr,
+                                                         float* __restrict__ y, int64_t ldy, int M, int N, int K) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (int64_t)M * N) return;
     const int m = (int)(idx / N), n = (int)(idx - (int64_t)(idx / N) * N);
@@ -166,28 +183,32 @@ __global__ __launch_bounds__(256) void linear_f32_kernel(const float* __restrict
     const float* wr = w + (int64_t)n * K;
     float s = bias ? bias[n] : 0.f;
     for (int k = 0; k < K; ++k) s = fmaf(xr[k], wr[k], s);
+    if (r) s += r[(int64_t)m * ldr + n];
     y[(int64_t)m * ldy + n] = s;
 }
 
 }  // namespace
 
 hipError_t launch_linear(bool bf16, int M, int N, int K, const void* x, int64_t ldx, const void* w,
-                         const float* bias, void* y, int64_t ldy, hipStream_t stream) {
+                         const float* bias, const void* r, int64_t ldr, void* y, int64_t ldy,
+                         hipStream_t stream) {
     if (M == 0) return hipSuccess;
     if (!bf16) {
         const int64_t total = (int64_t)M * N;
         if (!grid_fits((total + 255) / 256)) return hipErrorInvalidConfiguration;
         linear_f32_kernel<<<(unsigned)((total + 255) / 256), 256, 0, stream>>>(
-            (const float*)x, ldx, (const float*)w, bias, (float*)y, ldy, M, N, K);
+            (const float*)x, ldx, (const float*)w, bias, (const float*)r, ldr, (float*)y, ldy, M, N, K);
         return hipGetLastError();
     }
     LinArgs a;
     a.x = (const uint16_t*)x;
     a.w = (const uint16_t*)w;
     a.bias = bias;
+    a.r = (const uint16_t*)r;
     a.y = (uint16_t*)y;
     a.ldx = ldx;
     a.ldy = ldy;
+    a.ldr = ldr;
     a.M = M;
     a.N = N;
     a.K = K;

@@ -1,12 +1,18 @@
 """One layer's GPU state and its steps, composed from the four C-ABI calls.
 
 A layer (``configs.LayerConfig``) owns, on the GPU:
-  * the GroupNorm statistics table [P][B][G][2] of the previous step,
+  * for every GroupNorm step of its graph, that step's statistics table
+    [P][B][G][2] of the previous step (each GroupNorm site normalises a
+    different map, so each keeps its own table),
   * for every conv or attention step of its graph, the previous step's full
     input map [B][H][W][C] (the stale context; for attention it is the K/V
     map, since Q = K = V = the step's input), and
-  * for every attention step with learned projections ("attn_proj"), the
-    previous step's projected K and V maps (the K/V cache).
+  * for every attention step with learned projections ("attn_proj",
+    "attn_proj_res"), the previous step's projected K and V maps (the K/V
+    cache).
+The residual steps "conv_res" and "attn_proj_res" add the layer's own input
+patch to their output (the skip connection of a ResNet or transformer block),
+inside the conv's or the output projection's epilogue.
 
 ``warmup(x)`` runs a synchronous step on the full map, patch by patch, and
 leaves the state equal to that step's statistics and maps (warm-up steps are
@@ -22,8 +28,13 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import torch
 
 from . import (Patch, _dtype_code, dp_attention_splice, dp_conv3x3_halo, dp_conv3x3_halo_packed,
-               dp_conv3x3_pack_weights, dp_groupnorm_async, dp_linear, dp_stale_update, dp_stats_update,
-               workspace_bytes)
+               dp_conv3x3_halo_residual, dp_conv3x3_pack_weights, dp_groupnorm_async, dp_linear,
+               dp_linear_residual, dp_stale_update, dp_stats_update, workspace_bytes)
+
+GN_STEPS = ("gn", "gn_silu")
+CONV_STEPS = ("conv", "conv_res")
+PROJ_STEPS = ("attn_proj", "attn_proj_res")
+MAP_STEPS = CONV_STEPS + ("attn",)     # steps whose stale context is their own input map
 
 
 def torch_dtype(name):
@@ -58,22 +69,25 @@ class DisplacedLayer:
         self.projs = [tuple(torch.as_tensor(a).to(self.device, self.dt if j % 2 == 0 else torch.float32).contiguous()
                             for j, a in enumerate(pr)) for pr in (projs or [])]
         c = cfg
-        self.table = torch.zeros((c.P, c.B, c.G, 2), dtype=torch.float32, device=self.device)
+        # one statistics table and one fresh-moments buffer per GroupNorm step
+        self.tables: Dict = {k: torch.zeros((c.P, c.B, c.G, 2), dtype=torch.float32, device=self.device)
+                             for k, s in enumerate(c.graph) if s in GN_STEPS}
+        self.fresh = {k: torch.empty((c.B, c.G, 2), dtype=torch.float32, device=self.device)
+                      for k in self.tables}
         full = (c.B, c.H, c.W, c.C)
         self.maps: Dict = {k: torch.zeros(full, dtype=self.dt, device=self.device)
-                           for k, s in enumerate(c.graph) if s in ("conv", "attn")}
+                           for k, s in enumerate(c.graph) if s in MAP_STEPS}
         for k, s in enumerate(c.graph):
-            if s == "attn_proj":
+            if s in PROJ_STEPS:
                 self.maps[(k, "k")] = torch.zeros(full, dtype=self.dt, device=self.device)
                 self.maps[(k, "v")] = torch.zeros(full, dtype=self.dt, device=self.device)
-        self.fresh_stats = torch.empty((c.B, c.G, 2), dtype=torch.float32, device=self.device)
         # patch-sized intermediates, reused by every step
         band = (c.B, c.h, c.W, c.C)
         self.bufs = [torch.empty(band, dtype=self.dt, device=self.device) for _ in c.graph]
         # attn_proj scratch bands: projected queries, attention output, fresh K and V (when
         # they are not written straight into the cache)
         self.pbufs = {k: {n: torch.empty(band, dtype=self.dt, device=self.device) for n in "qakv"}
-                      for k, s in enumerate(c.graph) if s == "attn_proj"}
+                      for k, s in enumerate(c.graph) if s in PROJ_STEPS}
         # one workspace for every call of a step (calls are ordered on one stream); owned by the
         # layer so a captured graph keeps pointing at live memory
         code = _dtype_code(self.bufs[0])
@@ -81,9 +95,9 @@ class DisplacedLayer:
         for w, _ in self.convs:
             need = max(need, workspace_bytes("conv", self.patch(0), code, int(w.shape[0])))
         for s in c.graph:
-            if s in ("gn", "gn_silu"):
+            if s in GN_STEPS:
                 need = max(need, workspace_bytes("groupnorm", self.patch(0), code, c.G))
-            elif s in ("attn", "attn_proj"):
+            elif s == "attn" or s in PROJ_STEPS:
                 need = max(need, workspace_bytes("attention", self.patch(0), code, c.heads, c.C // c.heads))
         self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
 
@@ -98,9 +112,18 @@ class DisplacedLayer:
     def _tok(self, t):
         return t.reshape(t.shape[0], -1, t.shape[-1])
 
-    def _conv(self, p, x_patch, stale, j, y_patch=None, ws=None):
-        """The layer's j-th conv (on its packed weights when they exist)."""
+    @property
+    def table(self):
+        """The statistics table of the graph's first GroupNorm step."""
+        return self.tables[min(self.tables)]
+
+    def _conv(self, p, x_patch, stale, j, y_patch=None, ws=None, residual=None):
+        """The layer's j-th conv (on its packed weights when they exist), plus a residual."""
         w, b = self.convs[j]
+        if residual is not None:
+            wp = self.wpacked[j]
+            return dp_conv3x3_halo_residual(p, x_patch, stale, w if wp is None else wp, b, residual,
+                                            y_patch=y_patch, packed=wp is not None, ws=ws)
         if self.wpacked[j] is not None:
             return dp_conv3x3_halo_packed(p, x_patch, stale, self.wpacked[j], b, y_patch=y_patch, ws=ws)
         return dp_conv3x3_halo(p, x_patch, stale, w, b, y_patch=y_patch, ws=ws)
@@ -124,14 +147,16 @@ class DisplacedLayer:
                 out = self.maps[nxt][:, i * c.h:(i + 1) * c.h]      # contiguous for B == 1
             else:
                 out = self.bufs[k]
-            if s in ("gn", "gn_silu"):
-                stats = self.table[i] if in_place else self.fresh_stats
+            if s in GN_STEPS:
+                table = self.tables[k]
+                stats = table[i] if in_place else self.fresh[k]
                 act = "silu" if s == "gn_silu" else None
-                fn = (lambda h=h, out=out, stats=stats, act=act: dp_groupnorm_async(
-                    p, h, c.G, self.table, c.eps, gn_mode, act, fresh_stats_out=stats, y_patch=out, ws=self.ws))
-            elif s == "conv":
-                fn = (lambda h=h, out=out, k=k, j=conv_i: self._conv(p, h, self.maps[k], j, y_patch=out,
-                                                                  ws=self.ws))
+                fn = (lambda h=h, out=out, stats=stats, act=act, table=table: dp_groupnorm_async(
+                    p, h, c.G, table, c.eps, gn_mode, act, fresh_stats_out=stats, y_patch=out, ws=self.ws))
+            elif s in CONV_STEPS:
+                res = x_patch if s == "conv_res" else None
+                fn = (lambda h=h, out=out, k=k, j=conv_i, res=res: self._conv(p, h, self.maps[k], j, y_patch=out,
+                                                                           ws=self.ws, residual=res))
                 conv_i += 1
             elif s == "attn":
                 tok, st, o = self._tok(h), self._tok(self.maps[k]), self._tok(out)
@@ -153,10 +178,18 @@ class DisplacedLayer:
                 out_list.append(("proj_v", lambda tok=tok, y=vb, w=wv, b=bv: dp_linear(tok, w, b, y=y), None))
                 out_list.append(("attn", lambda q=q, kb=kb, vb=vb, a=a, ks=self._tok(kcache), vs=self._tok(vcache):
                                  dp_attention_splice(p, c.heads, q, kb, vb, ks, vs, o_patch=a, ws=self.ws), None))
-                fn = (lambda a=a, o=self._tok(out), w=wo, b=bo: dp_linear(a, w, b, y=o))
+                if s == "attn_proj_res":
+                    fn = (lambda a=a, o=self._tok(out), w=wo, b=bo, r=self._tok(x_patch):
+                          dp_linear_residual(a, w, b, r, y=o))
+                else:
+                    fn = (lambda a=a, o=self._tok(out), w=wo, b=bo: dp_linear(a, w, b, y=o))
                 s = "proj_o"
             out_list.append((s, fn, out))
             h = out
+        if in_place and 0 in self.maps:
+            # a graph that starts with a conv or attention: its stale map's band i is the layer
+            # input itself, which no earlier call wrote in place
+            out_list.append(("stale_update", lambda: dp_stale_update(p, x_patch, self.maps[0]), None))
         return out_list
 
     def step(self, x_patch, i, gn_mode="corrected", update_state=True, events=None) -> List[torch.Tensor]:
@@ -217,8 +250,7 @@ class DisplacedLayer:
         c = self.cfg
         full = (c.B, c.H, c.W, c.C)
         outs_full = [torch.empty(full, dtype=self.dt, device=self.device) for _ in c.graph]
-        has_gn = any(s in ("gn", "gn_silu") for s in c.graph)
-        next_table = torch.empty_like(self.table)
+        next_tables = {k: torch.empty_like(t) for k, t in self.tables.items()}
         next_kv = {key: torch.empty(full, dtype=self.dt, device=self.device)
                    for key in self.maps if isinstance(key, tuple)}
         for i in range(c.P):
@@ -228,10 +260,10 @@ class DisplacedLayer:
                 dp_stale_update(p, o, outs_full[k])
             for (k, kv), m in next_kv.items():
                 dp_stale_update(p, self.pbufs[k][kv], m)
-            if has_gn:
-                dp_stats_update(c.P, i, self.fresh_stats, next_table)
-        if has_gn:
-            self.table.copy_(next_table)
+            for k, t in next_tables.items():
+                dp_stats_update(c.P, i, self.fresh[k], t)
+        for k, t in next_tables.items():
+            self.tables[k].copy_(t)
         inputs = [x_full] + outs_full[:-1]
         for key, m in self.maps.items():
             m.copy_(next_kv[key] if isinstance(key, tuple) else inputs[key])
@@ -243,10 +275,10 @@ class DisplacedLayer:
         p = self.patch(i)
         inputs = [x_patch] + outs[:-1]
         for k, s in enumerate(c.graph):
-            if s in ("gn", "gn_silu"):
+            if s in GN_STEPS:
                 ev = _mark(events, "stats_update")
-                dp_stats_update(c.P, i, self.fresh_stats, self.table)
-            elif s == "attn_proj":
+                dp_stats_update(c.P, i, self.fresh[k], self.tables[k])
+            elif s in PROJ_STEPS:
                 ev = _mark(events, "stale_update")
                 dp_stale_update(p, self.pbufs[k]["k"], self.maps[(k, "k")])
                 dp_stale_update(p, self.pbufs[k]["v"], self.maps[(k, "v")])
@@ -267,17 +299,18 @@ class DisplacedLayer:
         proj_i = 0
         for k, s in enumerate(c.graph):
             out_full = torch.empty((c.B, c.H, c.W, c.C), dtype=self.dt, device=self.device)
-            if s in ("gn", "gn_silu"):
+            if s in GN_STEPS:
+                table, fresh = self.tables[k], self.fresh[k]
                 for j in range(c.P):
                     dp_groupnorm_async(self.patch(j), self.band(h_full, j), c.G, None, c.eps, "local",
-                                       fresh_stats_out=self.fresh_stats, stats_only=True)
-                    dp_stats_update(c.P, j, self.fresh_stats, self.table)
+                                       fresh_stats_out=fresh, stats_only=True)
+                    dp_stats_update(c.P, j, fresh, table)
                 for j in range(c.P):
-                    y, _ = dp_groupnorm_async(self.patch(j), self.band(h_full, j), c.G, self.table, c.eps,
+                    y, _ = dp_groupnorm_async(self.patch(j), self.band(h_full, j), c.G, table, c.eps,
                                               "corrected", "silu" if s == "gn_silu" else None,
-                                              fresh_stats_out=self.fresh_stats)
+                                              fresh_stats_out=fresh)
                     dp_stale_update(self.patch(j), y, out_full)
-            elif s == "attn_proj":
+            elif s in PROJ_STEPS:
                 wq, bq, wk, bk, wv, bv, wo, bo = self.projs[proj_i]
                 proj_i += 1
                 tok = self._tok(h_full)
@@ -291,21 +324,25 @@ class DisplacedLayer:
                     qj, kj, vj = (self._tok(self.band(m, j)) for m in (q_full, kc, vc))
                     a = dp_attention_splice(pj, c.heads, qj, kj, vj, self._tok(kc), self._tok(vc))
                     dp_stale_update(pj, a.reshape(qj.shape[0], c.h, c.W, c.C), a_full)
-                dp_linear(self._tok(a_full), wo, bo, y=self._tok(out_full))
+                if s == "attn_proj_res":
+                    dp_linear_residual(self._tok(a_full), wo, bo, self._tok(x_full), y=self._tok(out_full))
+                else:
+                    dp_linear(self._tok(a_full), wo, bo, y=self._tok(out_full))
             else:
                 for j in range(c.P):
                     dp_stale_update(self.patch(j), self.band(h_full, j), self.maps[k])
                 for j in range(c.P):
                     pj = self.patch(j)
                     xb = self.band(h_full, j)
-                    if s == "conv":
-                        o = self._conv(pj, xb, self.maps[k], conv_i)
+                    if s in CONV_STEPS:
+                        res = self.band(x_full, j) if s == "conv_res" else None
+                        o = self._conv(pj, xb, self.maps[k], conv_i, residual=res)
                     else:
                         tok = self._tok(xb)
                         st = self._tok(self.maps[k])
                         o = dp_attention_splice(pj, c.heads, tok, tok, tok, st, st).reshape(xb.shape)
                     dp_stale_update(pj, o, out_full)
-                if s == "conv":
+                if s in CONV_STEPS:
                     conv_i += 1
             outs.append(out_full)
             h_full = out_full

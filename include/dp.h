@@ -20,6 +20,9 @@
  *   dp_stale_update      writes the fresh patch into the resident stale map
  *   dp_linear            y = x W^T + b, the Q/K/V/O projections of an attention
  *                        layer whose K/V cache holds projected keys and values
+ *   dp_conv3x3_halo_residual, dp_linear_residual
+ *                        the conv and the projection with a block's skip
+ *                        connection added before rounding
  *
  * Geometry.  Maps are NHWC, batch-major: element (b, r, c, ch) of a [B][H][W][C]
  * map sits at ((b*H + r)*W + c)*C + ch.  The P patches are equal row bands:
@@ -122,6 +125,9 @@ typedef struct {
  *   ws              >= dp_groupnorm_async_ws bytes
  * Requires C % G == 0, C % 8 == 0 and C <= 8192 (bf16) or C % 4 == 0 and
  * C <= 4096 (f32), eps > 0; other channel counts give DP_ERR_UNSUPPORTED.
+ * The normalising kernel's block holds one thread per group at least, so
+ * G <= 1024; a G whose blocks would exceed 1024 threads or 64 KB of LDS is
+ * rejected with DP_ERR_UNSUPPORTED before anything is enqueued.
  * After the call, fresh_stats_out is what dp_stale_update copies into slot i
  * of the table for the next step (see dp_stale_update).
  * ---------------------------------------------------------------------- */
@@ -192,6 +198,30 @@ dp_status dp_conv3x3_halo_packed(const dp_patch* p, dp_dtype dtype, int32_t Cout
                                  void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * dp_conv3x3_halo_residual -- the same convolution with a residual added:
+ *   y[b,y,x,o] = (conv of dp_conv3x3_halo)[b,y,x,o] + residual[b,y,x,o]
+ * with the sum formed in fp32 before the single rounding of the output.
+ *
+ * Source: the convolution as dp_conv3x3_halo (study.space page, Method).  The
+ * residual is the skip connection of a UNet ResNet block (the denoiser of the
+ * DistriFusion summary's experiments is SDXL, a U-Net; AsyncDiff rebuttal on
+ * paperhub.cn, answer to Q2, speaks of the U-Net's blocks and their hidden
+ * states): the block's second conv adds the block input of the same band.
+ * The residual is fresh data of band i only, so displacement does not touch it.
+ *
+ *   w          [Cout][3][3][Cin] (w_packed == 0) or the packed layout of
+ *              dp_conv3x3_pack_weights (w_packed == 1, bf16 only)
+ *   residual   [B][h][W][Cout] dtype, or NULL (then exactly dp_conv3x3_halo /
+ *              dp_conv3x3_halo_packed); must not overlap y_patch or ws
+ * Other arguments, requirements and errors as dp_conv3x3_halo; w_packed other
+ * than 0 or 1 gives DP_ERR_ARG.
+ * ---------------------------------------------------------------------- */
+dp_status dp_conv3x3_halo_residual(const dp_patch* p, dp_dtype dtype, int32_t Cout, const void* x_patch,
+                                   const void* x_stale, const void* w, int32_t w_packed, const float* bias,
+                                   const void* residual, void* y_patch, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * dp_attention_splice -- self-attention of patch i over spliced K/V.
  *
  * Source: PipeFusion explainer (gist.science), Problem Statement and Memory
@@ -259,6 +289,24 @@ dp_status dp_stale_update(const dp_patch* p, dp_dtype dtype, const void* x_patch
  * ---------------------------------------------------------------------- */
 dp_status dp_linear(dp_dtype dtype, int32_t M, int32_t N, int32_t K, const void* x, int64_t ldx, const void* w,
                     const float* bias, void* y, int64_t ldy, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * dp_linear_residual -- y = x W^T + bias + r: dp_linear with a residual added
+ * in fp32 before the single rounding of the output.
+ *
+ * Source: as dp_linear (PipeFusion explainer on gist.science, Problem
+ * Statement); the residual is the skip connection of a transformer block of
+ * the U-Net denoiser (AsyncDiff rebuttal on paperhub.cn, answer to Q2): the
+ * output projection of the attention adds the block input of the same tokens.
+ *
+ *   r     [M][N] dtype, row r at r + m*ldr (elements), or NULL (then exactly
+ *         dp_linear); must not overlap y
+ * Other arguments, requirements and errors as dp_linear; bf16 also needs ldr
+ * a multiple of 8, and ldr >= N when r is given.
+ * ---------------------------------------------------------------------- */
+dp_status dp_linear_residual(dp_dtype dtype, int32_t M, int32_t N, int32_t K, const void* x, int64_t ldx,
+                             const void* w, const float* bias, const void* r, int64_t ldr, void* y, int64_t ldy,
+                             hipStream_t stream);
 
 /* Description of the last error on the calling thread (empty if none). The
  * string stays valid until the thread's next dp_* call. */

@@ -51,3 +51,14 @@ def announce(*parts):
     """Print (and flush) what case is about to run on the GPU."""
     print("[gpu case]", *parts, flush=True)
     sys.stdout.flush()
+
+
+def assert_table(got, ref, dtype, k, what=""):
+    """A GroupNorm statistics table against the oracle's.  The first GroupNorm step (k == 0)
+    reads the layer input itself, identical bits on both sides, so its fp32 moments are held to
+    1e-4; a later GroupNorm step normalises an intermediate the GPU stores in the layer's dtype
+    (rounded) while the oracle keeps it in float64, so its moments get that dtype's tolerance."""
+    if k == 0 or dtype == "f32":
+        np.testing.assert_allclose(got, ref, rtol=1e-4, atol=1e-4, err_msg=what)
+    else:
+        assert_parity(got, ref, dtype, what)

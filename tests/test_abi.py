@@ -15,7 +15,11 @@ import displaced_patch_parallelism_amd as dp
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dp.h")
 
-pytestmark = pytest.mark.skipif(not os.path.exists(dp.LIB_PATH), reason="libdp.so not built")
+
+
+def test_library_is_built():
+    """The boundary suite needs the built library; a missing one is a failure, not a skip."""
+    assert os.path.exists(dp.LIB_PATH), f"{dp.LIB_PATH} is not built (run __graft_entry__.build())"
 
 
 def declared_functions():
@@ -137,6 +141,22 @@ def test_unsupported_shapes():
     assert ws_query("attn", dp.Patch(1, 8, 8, 24, 2, 0), dp.DP_F32, 1, 24)[0] == dp.DP_ERR_UNSUPPORTED
 
 
+def test_groupnorm_group_count_bound():
+    """The normalising block holds a thread per group: G beyond what 1024 threads (and 64 KB
+    of LDS) hold is rejected on the host, with nothing enqueued."""
+    # C = G = 2048 bf16: 256 channel vectors, 2048 groups -> a block of 2048 threads
+    assert ws_query("gn", dp.Patch(1, 8, 8, 2048, 2, 0), dp.DP_BF16, 2048)[0] == dp.DP_ERR_UNSUPPORTED
+    assert "1024" in dp.lib().dp_last_error().decode()
+    assert ws_query("gn", dp.Patch(1, 8, 8, 8192, 2, 0), dp.DP_BF16, 8192)[0] == dp.DP_ERR_UNSUPPORTED
+    L = dp.lib()
+    p = dp._cpatch(dp.Patch(1, 8, 8, 2048, 2, 0))
+    assert L.dp_groupnorm_async(p, dp.DP_BF16, 2048, 1e-5, 1, 0, FAKE, None, None, None, FAKE2, FAKE2 * 2,
+                                FAKE2 * 4, 1 << 24, None) == dp.DP_ERR_UNSUPPORTED
+    # the largest group counts that fit are accepted
+    assert ws_query("gn", dp.Patch(1, 8, 8, 1024, 2, 0), dp.DP_BF16, 1024)[0] == dp.DP_OK
+    assert ws_query("gn", dp.Patch(1, 8, 8, 2048, 2, 0), dp.DP_BF16, 1024)[0] == dp.DP_OK
+
+
 def test_groupnorm_argument_errors():
     L = dp.lib()
     p = dp._cpatch(dp.Patch(1, 8, 8, 64, 2, 0))
@@ -235,3 +255,27 @@ def call_linear(dtype=dp.DP_BF16, M=16, N=64, K=64, x=FAKE, ldx=64, w=FAKE2, bia
 def test_linear_rejects(kw, code, msg):
     assert call_linear(**kw) == code
     assert msg in dp.lib().dp_last_error().decode()
+
+
+def test_residual_entry_points_validate():
+    L = dp.lib()
+    p = dp._cpatch(dp.Patch(1, 8, 8, 64, 2, 0))
+    # residual overlapping the output; misaligned residual; bad layout flag
+    assert L.dp_conv3x3_halo_residual(p, dp.DP_BF16, 64, FAKE, FAKE2, FAKE2 * 2, 0, None, FAKE2 * 3 + 64,
+                                      FAKE2 * 3, FAKE2 * 4, 1 << 24, None) == dp.DP_ERR_ARG
+    assert "overlap" in L.dp_last_error().decode()
+    assert L.dp_conv3x3_halo_residual(p, dp.DP_BF16, 64, FAKE, FAKE2, FAKE2 * 2, 0, None, FAKE2 * 3 + 8,
+                                      0x7000000, FAKE2 * 4, 1 << 24, None) == dp.DP_ERR_ARG
+    assert "aligned" in L.dp_last_error().decode()
+    assert L.dp_conv3x3_halo_residual(p, dp.DP_BF16, 64, FAKE, FAKE2, FAKE2 * 2, 2, None, None,
+                                      FAKE2 * 3, FAKE2 * 4, 1 << 24, None) == dp.DP_ERR_ARG
+    assert L.dp_conv3x3_halo_residual(p, dp.DP_F32, 64, FAKE, FAKE2, FAKE2 * 2, 1, None, None,
+                                      FAKE2 * 3, FAKE2 * 4, 1 << 24, None) == dp.DP_ERR_UNSUPPORTED
+    lin = L.dp_linear_residual
+    # residual stride shorter than a row; residual overlapping y; bf16 residual stride not a multiple of 8
+    assert lin(dp.DP_BF16, 16, 64, 64, FAKE, 64, FAKE2, None, 0x40000000, 32, 0x30000000, 64, None) == dp.DP_ERR_ARG
+    assert lin(dp.DP_BF16, 16, 64, 64, FAKE, 64, FAKE2, None, 0x30000000 + 256, 64, 0x30000000, 64,
+               None) == dp.DP_ERR_ARG
+    assert "overlap" in L.dp_last_error().decode()
+    assert lin(dp.DP_BF16, 16, 64, 64, FAKE, 64, FAKE2, None, 0x40000000, 68, 0x30000000, 64,
+               None) == dp.DP_ERR_UNSUPPORTED

@@ -22,7 +22,7 @@ def bits(t):
     return t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)
 
 
-@pytest.mark.parametrize("name", ["c0", "c1", "c3", "c2p"])
+@pytest.mark.parametrize("name", ["c0", "c1", "c3", "c2p", "c1r", "c2t"])
 def test_graph_replays_match_eager(name):
     announce("graph replay", name)
     c = CONFIGS[name]
@@ -37,7 +37,7 @@ def test_graph_replays_match_eager(name):
     layer.step(xb, i)
     torch.cuda.synchronize()
     eager = [bits(o).clone() for o in outs]
-    eager_table = layer.table.clone()
+    eager_tables = {k: t.clone() for k, t in layer.tables.items()}
 
     graph = layer.capture(xb, i)
     for r in range(3):
@@ -45,9 +45,11 @@ def test_graph_replays_match_eager(name):
         _ = (junk * junk).sum().item()               # eager work and a synchronisation
         for o in outs:
             o.fill_(float(r + 7))
-        layer.table[i].fill_(-1.0)
+        for t in layer.tables.values():
+            t[i].fill_(-1.0)
         graph.replay()
         torch.cuda.synchronize()
         for k, (o, e) in enumerate(zip(outs, eager)):
             assert torch.equal(bits(o), e), f"{name} replay {r} output {k}"
-        assert torch.equal(layer.table, eager_table), f"{name} replay {r} statistics table"
+        for k, t in layer.tables.items():
+            assert torch.equal(t, eager_tables[k]), f"{name} replay {r} statistics table {k}"

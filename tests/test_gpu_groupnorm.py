@@ -31,13 +31,18 @@ def run_case(B, H, W, C, G, P, i, dtype, mode="corrected", act=None, affine=Fals
     return y, st
 
 
-@pytest.mark.parametrize("name", list(CONFIGS))
-def test_config_shapes(name):
-    c = CONFIGS[name]
-    act = "silu" if "gn_silu" in c.graph else None
-    for i in ([0, c.patch, c.P - 1] if c.P > 2 else range(c.P)):
-        announce("groupnorm", name, "patch", i)
-        run_case(c.B, c.H, c.W, c.C, c.G, c.P, i, c.dtype, act=act, seed=i)
+GN_SHAPES = sorted({(c.B, c.H, c.W, c.C, c.G, c.P, c.patch, c.dtype, "gn_silu" in c.graph)
+                    for c in CONFIGS.values()})
+
+
+@pytest.mark.parametrize("shape", GN_SHAPES, ids=lambda s: "x".join(map(str, s[:6])) + s[7] + ("silu" if s[8] else ""))
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_config_shapes(shape, seed):
+    B, H, W, C, G, P, ip, dtype, silu = shape
+    act = "silu" if silu else None
+    for i in ([0, ip, P - 1] if P > 2 else range(P)):
+        announce("groupnorm", shape, "patch", i, "seed", seed)
+        run_case(B, H, W, C, G, P, i, dtype, act=act, seed=10 * seed + i)
 
 
 @pytest.mark.parametrize("mode", ["corrected", "local", "stale"])
@@ -51,6 +56,21 @@ def test_nonzero_mean_and_ragged_tokens():
     announce("groupnorm mean 3, 7x13 map")
     run_case(1, 14, 13, 64, 8, 2, 1, "bf16", mean=3.0, seed=4)
     run_case(1, 14, 13, 64, 8, 2, 0, "f32", mean=3.0, seed=4)
+
+
+@pytest.mark.parametrize("mean", [10.0, 30.0])
+@pytest.mark.parametrize("shape", [
+    (1, 128, 128, 320, 32, 4, 1),     # c1 band: 40960 elements per group
+    (1, 480, 480, 320, 32, 8, 1),     # c4a band: 288000 elements per group
+])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_large_mean_over_std(mean, shape, dtype):
+    """Inputs with mean/std of 10 and 30: the variance E[x^2] - E[x]^2 is a small difference of
+    large moments, the case where fp32 moments lose digits to cancellation."""
+    B, H, W, C, G, P, i = shape
+    announce("groupnorm mean", mean, shape, dtype)
+    for mode in ("corrected", "local"):
+        run_case(B, H, W, C, G, P, i, dtype, mode=mode, act="silu", seed=11, mean=mean)
 
 
 def test_stats_only_and_in_place_and_determinism():

@@ -68,3 +68,36 @@ def test_deterministic():
     y2 = dp.dp_linear(xs, ws, bs)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("M,N,K,dtype", [
+    (1024, 640, 640, "bf16"),    # c2t output projection (64x64 tiles)
+    (7200, 640, 640, "bf16"),    # 128x128 tiles
+    (100, 136, 128, "bf16"),     # ragged rows and columns
+    (33, 40, 16, "f32"),
+])
+def test_residual(M, N, K, dtype):
+    """The skip connection is added before rounding: y = x W^T + b + r."""
+    announce("linear residual", M, N, K, dtype)
+    x, w, b = case(M, N, K, dtype, M + 3)
+    r = synth.to_storage(np.random.default_rng(M).standard_normal((M, N), dtype=np.float32), dtype)
+    y = dp.dp_linear_residual(gpu(x, dtype), gpu(w, dtype), gpu(b, "f32"), gpu(r, dtype))
+    torch.cuda.synchronize()
+    assert_parity(host(y), oracle.linear(x, w, b) + r, dtype, f"linear residual {M}x{N}x{K}")
+    # no residual: exactly dp_linear
+    y0 = dp.dp_linear_residual(gpu(x, dtype), gpu(w, dtype), gpu(b, "f32"), None)
+    y1 = dp.dp_linear(gpu(x, dtype), gpu(w, dtype), gpu(b, "f32"))
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+
+
+def test_residual_strided_rows():
+    """Residual rows strided inside a wider buffer (a band of a token map)."""
+    M, N, K = 96, 64, 128
+    x, w, b = case(M, N, K, "bf16", 6)
+    r = synth.to_storage(np.random.default_rng(8).standard_normal((M, N), dtype=np.float32), "bf16")
+    big = torch.zeros((M, N + 64), dtype=torch.bfloat16, device="cuda")
+    big[:, 16:16 + N] = gpu(r, "bf16")
+    y = dp.dp_linear_residual(gpu(x, "bf16"), gpu(w, "bf16"), gpu(b, "f32"), big[:, 16:16 + N])
+    torch.cuda.synchronize()
+    assert_parity(host(y), oracle.linear(x, w, b) + r, "bf16", "linear residual strided")

@@ -14,7 +14,7 @@ import oracle
 from displaced_patch_parallelism_amd import synth, trajectory
 from displaced_patch_parallelism_amd.configs import CONFIGS, LayerConfig
 from displaced_patch_parallelism_amd.layers import DisplacedLayer
-from tests.gpu_util import announce, assert_parity, gpu, host
+from tests.gpu_util import announce, assert_parity, assert_table, gpu, host
 
 pytestmark = pytest.mark.gpu
 
@@ -25,6 +25,11 @@ CASES = {
                            heads=2, head_dim=64),
     "c2p-like": LayerConfig("c2ps", "bf16", B=1, H=16, W=16, C=128, G=32, P=4,
                             graph=("gn", "attn_proj", "conv"), heads=2, head_dim=64),
+    # an SDXL-like ResNet block followed by a transformer block: three GroupNorm sites, each
+    # with its own statistics table, and two skip connections
+    "block-like": LayerConfig("blk", "bf16", B=1, H=16, W=16, C=128, G=32, P=4,
+                              graph=("gn_silu", "conv", "gn_silu", "conv_res", "gn", "attn_proj_res"),
+                              heads=2, head_dim=64),
 }
 
 
@@ -44,7 +49,9 @@ def test_step_all_matches_oracle(name, mode):
         ref, state = oracle.displaced_step_all(c.graph, params, tr.xs[t], state, c.P, gn_mode)
         for k, (g, r) in enumerate(zip(outs, ref)):
             assert_parity(host(g), r, c.dtype, f"{name} {mode} t{t} step {k} ({c.graph[k]})")
-        assert_parity(host(layer.table), state["stats"], "f32", f"{name} {mode} t{t} statistics table")
+        assert set(layer.tables) == set(state["stats"])
+        for k, tab in layer.tables.items():
+            assert_table(host(tab), state["stats"][k], c.dtype, k, f"{name} {mode} t{t} statistics table {k}")
         for key, m in layer.maps.items():
             assert_parity(host(m), state["maps"][key], c.dtype, f"{name} {mode} t{t} state map {key}")
 
