@@ -68,6 +68,7 @@ def lib():
         sigs = {
             "dp_groupnorm_async_ws": [pp, i32, i32, psz],
             "dp_groupnorm_async": [pp, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+            "dp_groupnorm_async_noalloc": [pp, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp, vp, vp],
             "dp_conv3x3_halo_ws": [pp, i32, i32, psz],
             "dp_conv3x3_halo": [pp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp],
             "dp_conv3x3_pack_weights": [i32, i32, i32, vp, vp, vp],
@@ -221,6 +222,33 @@ def dp_groupnorm_async(patch: Patch, x_patch, G, stale_stats=None, eps=1e-5, mod
     _check(lib().dp_groupnorm_async(
         _cpatch(p), dt, G, float(eps), GN_MODES[mode], ACTS[act], x_patch.data_ptr(), gp(stale_stats),
         gp(gamma), gp(beta), fresh_stats_out.data_ptr(), gp(y_patch), wptr, wbytes, _stream(dev)))
+    return y_patch, fresh_stats_out
+
+
+def dp_groupnorm_async_noalloc(patch: Patch, x_patch, G, stale_stats=None, eps=1e-5, mode="corrected",
+                               act=None, gamma=None, beta=None, fresh_stats_out=None, y_patch=None,
+                               stats_only=False):
+    """dp_groupnorm_async without a workspace: the library's static scratch holds the partials (one
+    array per GPU, shared by every call on it; calls that overlap on one GPU race).  The outputs
+    must already exist when this is called from code that cannot allocate."""
+    torch = _torch()
+    p = Patch(*patch)
+    dt = _dtype_code(x_patch)
+    dev = x_patch.device
+    _ptr(x_patch, "x_patch", (p.B, p.h, p.W, p.C))
+    if fresh_stats_out is None:
+        fresh_stats_out = torch.empty((p.B, G, 2), dtype=torch.float32, device=dev)
+    if y_patch is None and not stats_only:
+        y_patch = torch.empty_like(x_patch)
+    _ptr(fresh_stats_out, "fresh_stats_out", (p.B, G, 2), torch.float32, dev)
+    _ptr(y_patch, "y_patch", (p.B, p.h, p.W, p.C), x_patch.dtype, dev)
+    _ptr(stale_stats, "stale_stats", (p.P, p.B, G, 2), torch.float32, dev)
+    _ptr(gamma, "gamma", (p.C,), torch.float32, dev)
+    _ptr(beta, "beta", (p.C,), torch.float32, dev)
+    gp = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    _check(lib().dp_groupnorm_async_noalloc(
+        _cpatch(p), dt, G, float(eps), GN_MODES[mode], ACTS[act], x_patch.data_ptr(), gp(stale_stats),
+        gp(gamma), gp(beta), fresh_stats_out.data_ptr(), gp(y_patch), _stream(dev)))
     return y_patch, fresh_stats_out
 
 

@@ -172,10 +172,16 @@ dp_status dp_groupnorm_async_ws(const dp_patch* p, dp_dtype dtype, int32_t G, si
     return ok();
 }
 
-dp_status dp_groupnorm_async(const dp_patch* p, dp_dtype dtype, int32_t G, float eps, dp_gn_mode mode,
-                             dp_act act, const void* x_patch, const float* stale_stats,
-                             const float* gamma, const float* beta, float* fresh_stats_out,
-                             void* y_patch, void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and launch shared by dp_groupnorm_async and dp_groupnorm_async_noalloc; `noalloc`
+// takes the statistics partials' scratch from the library's static array instead of ws.
+dp_status groupnorm_call(const dp_patch* p, dp_dtype dtype, int32_t G, float eps, dp_gn_mode mode, dp_act act,
+                         const void* x_patch, const float* stale_stats, const float* gamma, const float* beta,
+                         float* fresh_stats_out, void* y_patch, void* ws, size_t ws_bytes, bool noalloc,
+                         hipStream_t stream) {
     dp::Geom g;
     DP_TRY(check_gn(p, dtype, G, &g));
     if (!(eps > 0.0f) || !std::isfinite(eps)) return fail(DP_ERR_ARG, "eps must be a positive finite number");
@@ -193,9 +199,18 @@ dp_status dp_groupnorm_async(const dp_patch* p, dp_dtype dtype, int32_t G, float
         return fail(DP_ERR_ARG, "stale_stats is NULL (needed by this GroupNorm mode)");
     DP_OPT(stale_stats, "stale_stats");
     const dp::GnPlan plan = dp::plan_groupnorm(g, G, dtype == DP_BF16);
-    if (ws_bytes < plan.ws_bytes)
-        return fail(DP_ERR_ARG, "workspace too small: %zu < %zu bytes", ws_bytes, plan.ws_bytes);
-    DP_NEED(ws, "ws");
+    if (noalloc) {
+        if (plan.ws_bytes > dp::kNoallocScratchBytes)
+            return fail(DP_ERR_UNSUPPORTED, "dp_groupnorm_async_noalloc: this call needs %zu bytes of scratch, "
+                        "more than the %zu its static array holds (use dp_groupnorm_async with a workspace)",
+                        plan.ws_bytes, dp::kNoallocScratchBytes);
+        ws = nullptr;
+        ws_bytes = 0;
+    } else {
+        if (ws_bytes < plan.ws_bytes)
+            return fail(DP_ERR_ARG, "workspace too small: %zu < %zu bytes", ws_bytes, plan.ws_bytes);
+        DP_NEED(ws, "ws");
+    }
     const size_t es = elem_size(dtype);
     const size_t band_bytes = (size_t)g.B * g.band_tokens() * g.C * es;
     const size_t stats_bytes = (size_t)g.B * G * 2 * sizeof(float);
@@ -215,9 +230,33 @@ dp_status dp_groupnorm_async(const dp_patch* p, dp_dtype dtype, int32_t G, float
         return fail(DP_ERR_ARG, "fresh_stats_out overlaps an input, y_patch or the workspace");
     if (overlaps(ws, plan.ws_bytes, x_patch, band_bytes) || overlaps(ws, plan.ws_bytes, stale_stats, table_bytes))
         return fail(DP_ERR_ARG, "workspace overlaps an input");
+    if (noalloc) {
+        const hipError_t e = dp::groupnorm_scratch(stream, &ws);
+        if (e != hipSuccess) return hip_status(e, "dp_groupnorm_async_noalloc scratch address");
+    }
     return hip_status(dp::launch_groupnorm(g, plan, dtype == DP_BF16, G, eps, (int)mode, (int)act, x_patch,
                                            stale_stats, gamma, beta, fresh_stats_out, y_patch, ws, stream),
-                      "dp_groupnorm_async launch");
+                      noalloc ? "dp_groupnorm_async_noalloc launch" : "dp_groupnorm_async launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+dp_status dp_groupnorm_async(const dp_patch* p, dp_dtype dtype, int32_t G, float eps, dp_gn_mode mode,
+                             dp_act act, const void* x_patch, const float* stale_stats,
+                             const float* gamma, const float* beta, float* fresh_stats_out,
+                             void* y_patch, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return groupnorm_call(p, dtype, G, eps, mode, act, x_patch, stale_stats, gamma, beta, fresh_stats_out,
+                          y_patch, ws, ws_bytes, false, stream);
+}
+
+dp_status dp_groupnorm_async_noalloc(const dp_patch* p, dp_dtype dtype, int32_t G, float eps, dp_gn_mode mode,
+                                     dp_act act, const void* x_patch, const float* stale_stats,
+                                     const float* gamma, const float* beta, float* fresh_stats_out,
+                                     void* y_patch, hipStream_t stream) {
+    return groupnorm_call(p, dtype, G, eps, mode, act, x_patch, stale_stats, gamma, beta, fresh_stats_out,
+                          y_patch, nullptr, 0, true, stream);
 }
 
 dp_status dp_conv3x3_halo_ws(const dp_patch* p, dp_dtype dtype, int32_t Cout, size_t* ws_bytes) {

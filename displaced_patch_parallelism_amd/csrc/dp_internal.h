@@ -48,6 +48,10 @@ GnPlan plan_groupnorm(const Geom& g, int G, bool bf16);
 constexpr size_t kMaxGnLds = 64 * 1024;
 size_t gn_stats_lds_bytes(const Geom& g, const GnPlan& plan);
 size_t gn_apply_lds_bytes(const Geom& g, const GnPlan& plan, int G);
+// Allocation-free GroupNorm: the statistics partials live in a static device array of this many
+// bytes (one per GPU); groupnorm_scratch returns its address on the stream's device.
+constexpr size_t kNoallocScratchBytes = (size_t)1 << 20;
+hipError_t groupnorm_scratch(hipStream_t stream, void** out);
 hipError_t launch_groupnorm(const Geom& g, const GnPlan& plan, bool bf16, int G, float eps, int mode,
                             int act, const void* x, const float* stale_stats, const float* gamma,
                             const float* beta, float* fresh_stats_out, void* y, void* ws,

@@ -34,6 +34,14 @@
 #include "dp_device.h"
 #include "dp_internal.h"
 
+#include <mutex>
+
+// Scratch of the allocation-free GroupNorm entry point: the statistics partials of a call live
+// here instead of in a caller workspace.  Every GPU the library runs on holds its own copy until
+// the process ends; host code never names the array itself (in host code the name is a host-side
+// stand-in, not a device address) but only the per-device address groupnorm_scratch() returns.
+static __device__ __align__(256) unsigned char scratch[dp::kNoallocScratchBytes];
+
 namespace dp {
 namespace {
 
@@ -375,6 +383,40 @@ size_t gn_stats_lds_bytes(const Geom& g, const GnPlan& plan) {
 size_t gn_apply_lds_bytes(const Geom& g, const GnPlan& plan, int G) {
     const size_t pg = (size_t)g.P * G;
     return ((size_t)(plan.threads / G) * G + G + (pg <= (size_t)kStaleLds ? pg : 0)) * sizeof(float2);
+}
+
+// Device address of `scratch` on the device `stream` runs on (the current device for the null
+// stream), looked up once per device with that device current.  No allocation.
+hipError_t groupnorm_scratch(hipStream_t stream, void** out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* ptrs[kMaxDevices] = {};
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    int dev = cur;
+    if (stream) {
+        hipDevice_t d;
+        e = hipStreamGetDevice(stream, &d);
+        if (e != hipSuccess) return e;
+        dev = (int)d;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        ptrs[dev] = p;
+    }
+    *out = ptrs[dev];
+    return hipSuccess;
 }
 
 GnPlan plan_groupnorm(const Geom& g, int G, bool bf16) {

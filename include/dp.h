@@ -140,6 +140,32 @@ dp_status dp_groupnorm_async(const dp_patch* p, dp_dtype dtype, int32_t G, float
                              hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * dp_groupnorm_async_noalloc -- dp_groupnorm_async without a workspace, for
+ * callers that cannot allocate device memory around the call (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Arguments, results and errors as dp_groupnorm_async (same kernels, bitwise
+ * the same outputs), minus ws and ws_bytes: the statistics partials live in a
+ * static device array of DP_NOALLOC_SCRATCH_BYTES bytes that every GPU the
+ * library runs on holds until the process ends.  The call allocates nothing
+ * and calls no allocating routine; its first call on a device looks up that
+ * device's address of the array once.  A call whose partials need more than
+ * DP_NOALLOC_SCRATCH_BYTES (B * nblk * G * 8 bytes, nblk <= 256 statistics
+ * blocks per batch; dp_groupnorm_async_ws reports the size) gives
+ * DP_ERR_UNSUPPORTED before anything is enqueued.  All calls on one GPU share
+ * the array: calls that may run at the same time on one GPU (on different
+ * streams, or from different threads without ordering) race and must not be
+ * issued; calls ordered on one stream are safe.  The array needs no clearing:
+ * each call writes every partial it reads.
+ * ---------------------------------------------------------------------- */
+#define DP_NOALLOC_SCRATCH_BYTES ((size_t)1 << 20)
+
+dp_status dp_groupnorm_async_noalloc(const dp_patch* p, dp_dtype dtype, int32_t G, float eps,
+                                     dp_gn_mode mode, dp_act act, const void* x_patch,
+                                     const float* stale_stats, const float* gamma, const float* beta,
+                                     float* fresh_stats_out, void* y_patch, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * dp_conv3x3_halo -- 3x3 convolution of patch i with stale halo rows.
  *
  * Source: study.space page, Method (previous-step activations give each
