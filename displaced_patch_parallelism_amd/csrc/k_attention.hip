@@ -497,15 +497,18 @@ AttnPlan plan_attention(const Geom& g, int heads, int head_dim, bool bf16) {
     p.qtiles = (int)((Nq + p.qtile - 1) / p.qtile);
     const int kv_tiles = (int)((g.map_tokens() + KT - 1) / KT);
     const int64_t units = (int64_t)p.qtiles * g.B * heads;
-    // Pick the key split that fills whole rounds of 256 workgroups best (>= 2 key tiles per
+    // Pick the key split that fills whole rounds of workgroup slots best (>= 2 key tiles per
     // split), preferring fewer splits: fewer, longer workgroups pay the pipeline fill, the
-    // partial write and the merge less often.
-    const int64_t slots = 256;
+    // partial write and the merge less often.  Two workgroups fit a CU (64 KB of LDS each), so a
+    // grid of at least 512 workgroups runs in rounds of 512; a smaller one is counted in rounds
+    // of 256 (one per CU: a CU's second workgroup would only share its SIMDs).  3840px layer: 290
+    // units x 7 splits = 2030 workgroups, 99 % of four rounds of 512 (6 splits: 85 %).
     int ks = 1;
     double best = 0.0;
     for (int k = 1; k <= kMaxSplit; ++k) {
         if (k > 1 && kv_tiles / k < 2) break;
         const int64_t wgs = units * k;
+        const int64_t slots = wgs >= 512 ? 512 : 256;
         const int64_t rounds = (wgs + slots - 1) / slots;
         const double eff = (double)wgs / (double)(rounds * slots);
         if (eff > best + 0.04) {

@@ -107,11 +107,11 @@ def test_workspace_queries():
     ("conv", dp.Patch(1, 128, 128, 320, 4, 1), (320,), 0),       # 256 tiles: no split
     ("conv", dp.Patch(1, 480, 480, 320, 8, 1), (320,), 0),       # large-map tiles: no split
     # attention: per key split, fp32 O [heads][Nq][64] and (max, sum) per query; 256-query
-    # tiles x heads, split to fill whole rounds of 256 workgroups: c2 40 units -> 6, c3 20 -> 8,
-    # c4b 290 -> 6
+    # tiles x heads, split to fill whole rounds of workgroups (256, or 512 for grids of 512 or
+    # more: two per CU): c2 40 units -> 6, c3 20 -> 8, c4b 290 -> 7
     ("attn", dp.Patch(1, 64, 64, 640, 4, 1), (10, 64), 6 * 10 * 1024 * (64 * 4 + 8)),
     ("attn", dp.Patch(1, 32, 32, 1280, 8, 1), (20, 64), 8 * 20 * 128 * (64 * 4 + 8)),
-    ("attn", dp.Patch(1, 240, 240, 640, 8, 1), (10, 64), 6 * 10 * 7200 * (64 * 4 + 8)),
+    ("attn", dp.Patch(1, 240, 240, 640, 8, 1), (10, 64), 7 * 10 * 7200 * (64 * 4 + 8)),
     # GroupNorm: (sum, sum of squares) per statistics block and group; c1 splits its 4096 tokens
     # into 228 blocks of 18
     ("gn", dp.Patch(1, 128, 128, 320, 4, 1), (32,), 228 * 32 * 2 * 4),
