@@ -38,9 +38,13 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA bf16; fp32 vector
 PEAK_HBM_GBS = 8000.0
 
 # source file of each call's main kernel (for the counter file's staleness check)
-KERNEL_SOURCES = {"conv": "k_conv.hip", "attn": "k_attention.hip", "gn": "k_groupnorm.hip",
-                  "gn_silu": "k_groupnorm.hip", "stale_update": "k_splice.hip", "proj_q": "k_linear.hip",
-                  "proj_k": "k_linear.hip", "proj_v": "k_linear.hip", "proj_o": "k_linear.hip"}
+KERNEL_SOURCES = {"conv": "k_conv.hip", "conv_res": "k_conv.hip", "attn": "k_attention.hip",
+                  "gn": "k_groupnorm.hip", "gn_silu": "k_groupnorm.hip", "stale_update": "k_splice.hip",
+                  "proj_q": "k_linear.hip", "proj_k": "k_linear.hip", "proj_v": "k_linear.hip",
+                  "proj_o": "k_linear.hip"}
+for _g in ("gn", "gn_silu"):
+    for _c in ("conv", "conv_res"):
+        KERNEL_SOURCES[f"{_g}+{_c}"] = "k_conv.hip"     # GroupNorm folded into the conv
 PROJ_CALLS = ("proj_q", "proj_k", "proj_v", "proj_o")
 
 
@@ -51,7 +55,7 @@ def step_flops(cfg):
 
 def call_flops(cfg, name):
     """Algorithmic flops of one call of the step (one conv, one attention, one projection)."""
-    if name in ("conv", "conv_res"):
+    if name.split("+")[-1] in ("conv", "conv_res"):
         return cfg.conv_flops() / max(cfg.n_conv, 1)
     if name == "attn":
         return cfg.attn_flops() / max(cfg.n_attn, 1)
@@ -68,14 +72,15 @@ def kernel_name(op, cfg, cout=None):
         return "attn_bf16_d64_kernel" if cfg.dtype == "bf16" else "attn_f32_kernel"
     if op in PROJ_CALLS:
         return "linear_bf16_kernel" if cfg.dtype == "bf16" else "linear_f32_kernel"
-    if op in ("conv", "conv_res"):
+    if op.split("+")[-1] in ("conv", "conv_res"):
         if cfg.dtype != "bf16":
             return "conv3x3_f32_direct_kernel"
         cout = cout or cfg.C
         big = cfg.B * -(-cfg.h // 4) * -(-cfg.W // 32) * -(-cout // 160)
         big8 = cfg.B * -(-cfg.h // 8) * -(-cfg.W // 32) * -(-cout // 160)
         if big >= 384 and -(-big8 // 256) <= -(-big // 512):
-            return "conv3x3_bf16_halo_tile8_kernel"
+            # with a GroupNorm folded in (its lanes and parameter table fit the kernel's LDS)
+            return "conv3x3_bf16_gn_tile8_kernel" if "+" in op else "conv3x3_bf16_halo_tile8_kernel"
         return "conv3x3_bf16_halo_tile_kernel" if big >= 384 else "conv3x3_bf16_halo_wave8_kernel"
     return op
 

@@ -80,6 +80,9 @@ def lib():
             "dp_conv3x3_halo_residual": [pp, i32, i32, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp],
             "dp_linear_residual": [i32, i32, i32, i32, vp, ctypes.c_int64, vp, vp, vp, ctypes.c_int64, vp,
                                    ctypes.c_int64, vp],
+            "dp_groupnorm_conv3x3_halo_ws": [pp, i32, i32, i32, psz],
+            "dp_groupnorm_conv3x3_halo": [pp, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, i32, vp,
+                                          vp, vp, vp, sz, vp],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
@@ -171,7 +174,7 @@ def workspace_bytes(kind, patch: Patch, dtype_code, *args):
     """Bytes of workspace an entry point needs ("groupnorm", "conv", "attention")."""
     out = ctypes.c_size_t(0)
     fn = {"groupnorm": lib().dp_groupnorm_async_ws, "conv": lib().dp_conv3x3_halo_ws,
-          "attention": lib().dp_attention_splice_ws}[kind]
+          "attention": lib().dp_attention_splice_ws, "groupnorm_conv": lib().dp_groupnorm_conv3x3_halo_ws}[kind]
     _check(fn(_cpatch(patch), dtype_code, *args, ctypes.byref(out)))
     return out.value
 
@@ -342,6 +345,44 @@ def dp_conv3x3_halo_residual(patch: Patch, x_patch, x_stale, w, bias=None, resid
                                           w.data_ptr(), 1 if packed else 0, gp(bias), gp(residual),
                                           y_patch.data_ptr(), wptr, wbytes, _stream(dev)))
     return y_patch
+
+
+def dp_groupnorm_conv3x3_halo(patch: Patch, x_patch, G, u_stale, w, bias=None, stale_stats=None, eps=1e-5,
+                              mode="corrected", act=None, gamma=None, beta=None, fresh_stats_out=None,
+                              residual=None, y_patch=None, packed=None, ws=None):
+    """GroupNorm (+SiLU) of patch i, then the 3x3 conv with stale halo on the normalised band; band i
+    of ``u_stale`` (the conv input's stale map) receives the normalised band.  ``w`` as in
+    dp_conv3x3_halo_residual.  Returns (y_patch, fresh_stats_out)."""
+    torch = _torch()
+    p = Patch(*patch)
+    dt = _dtype_code(x_patch)
+    dev = x_patch.device
+    if packed is None:
+        packed = w.dim() == 5
+    cout = int(w.shape[3]) if packed else int(w.shape[0])
+    wshape = (3, p.C // 32, 3, cout, 32) if packed else (cout, 3, 3, p.C)
+    _ptr(x_patch, "x_patch", (p.B, p.h, p.W, p.C))
+    _ptr(u_stale, "u_stale", (p.B, p.H, p.W, p.C), x_patch.dtype, dev)
+    _ptr(w, "w", wshape, x_patch.dtype, dev)
+    _ptr(bias, "bias", (cout,), torch.float32, dev)
+    _ptr(residual, "residual", (p.B, p.h, p.W, cout), x_patch.dtype, dev)
+    if fresh_stats_out is None:
+        fresh_stats_out = torch.empty((p.B, G, 2), dtype=torch.float32, device=dev)
+    if y_patch is None:
+        y_patch = torch.empty((p.B, p.h, p.W, cout), dtype=x_patch.dtype, device=dev)
+    _ptr(fresh_stats_out, "fresh_stats_out", (p.B, G, 2), torch.float32, dev)
+    _ptr(y_patch, "y_patch", (p.B, p.h, p.W, cout), x_patch.dtype, dev)
+    _ptr(stale_stats, "stale_stats", (p.P, p.B, G, 2), torch.float32, dev)
+    _ptr(gamma, "gamma", (p.C,), torch.float32, dev)
+    _ptr(beta, "beta", (p.C,), torch.float32, dev)
+    need = workspace_bytes("groupnorm_conv", p, dt, G, cout)
+    wptr, wbytes = _workspace(need, dev, ws)
+    gp = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    _check(lib().dp_groupnorm_conv3x3_halo(
+        _cpatch(p), dt, G, float(eps), GN_MODES[mode], ACTS[act], x_patch.data_ptr(), gp(stale_stats), gp(gamma),
+        gp(beta), fresh_stats_out.data_ptr(), u_stale.data_ptr(), cout, w.data_ptr(), 1 if packed else 0, gp(bias),
+        gp(residual), y_patch.data_ptr(), wptr, wbytes, _stream(dev)))
+    return y_patch, fresh_stats_out
 
 
 def dp_attention_splice(patch: Patch, heads, q_patch, k_patch, v_patch, k_stale, v_stale, o_patch=None,

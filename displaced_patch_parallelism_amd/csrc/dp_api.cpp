@@ -350,6 +350,144 @@ dp_status dp_conv3x3_halo_residual(const dp_patch* p, dp_dtype dtype, int32_t Co
                      stream, "dp_conv3x3_halo_residual launch");
 }
 
+}  // extern "C"
+
+namespace {
+
+// Workspace of the GroupNorm + conv call.  Fused: the statistics partials.  Otherwise the
+// GroupNorm output band (B > 1 only: a band of a batched map is not one contiguous block, so it
+// is normalised into the workspace and then spliced; for B == 1 it is normalised straight into
+// band i of the conv's stale map) followed by one region the statistics partials and then the
+// conv's split-K partials use in turn.
+struct GnConvLayout {
+    bool fused;
+    size_t band_off, band_bytes, part_off, part_bytes, total;
+};
+
+GnConvLayout gn_conv_layout(const dp::Geom& g, int G, int Cout, bool bf16, dp::GnPlan* gp, dp::ConvPlan* cp) {
+    *gp = dp::plan_groupnorm(g, G, bf16);
+    *cp = dp::plan_conv(g, Cout, bf16);
+    GnConvLayout l{};
+    l.fused = dp::conv_gn_fusable(g, *cp, *gp, G, bf16);
+    if (l.fused) {
+        l.part_bytes = gp->ws_bytes;
+    } else {
+        l.band_bytes = g.B > 1 ? (size_t)g.B * g.band_tokens() * g.C * (bf16 ? 2 : 4) : 0;
+        l.part_off = (l.band_bytes + 255) & ~(size_t)255;
+        l.part_bytes = gp->ws_bytes > cp->ws_bytes ? gp->ws_bytes : cp->ws_bytes;
+    }
+    l.total = l.part_off + l.part_bytes;
+    return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+dp_status dp_groupnorm_conv3x3_halo_ws(const dp_patch* p, dp_dtype dtype, int32_t G, int32_t Cout,
+                                       size_t* ws_bytes) {
+    dp::Geom g;
+    DP_TRY(check_gn(p, dtype, G, &g));
+    DP_TRY(check_conv(p, dtype, Cout, &g));
+    if (!ws_bytes) return fail(DP_ERR_ARG, "ws_bytes is NULL");
+    dp::GnPlan gp;
+    dp::ConvPlan cp;
+    *ws_bytes = gn_conv_layout(g, G, Cout, dtype == DP_BF16, &gp, &cp).total;
+    return ok();
+}
+
+dp_status dp_groupnorm_conv3x3_halo(const dp_patch* p, dp_dtype dtype, int32_t G, float eps, dp_gn_mode mode,
+                                    dp_act act, const void* x_patch, const float* stale_stats, const float* gamma,
+                                    const float* beta, float* fresh_stats_out, void* u_stale, int32_t Cout,
+                                    const void* w, int32_t w_packed, const float* bias, const void* residual,
+                                    void* y_patch, void* ws, size_t ws_bytes, hipStream_t stream) {
+    dp::Geom g;
+    DP_TRY(check_gn(p, dtype, G, &g));
+    DP_TRY(check_conv(p, dtype, Cout, &g));
+    if (!(eps > 0.0f) || !std::isfinite(eps)) return fail(DP_ERR_ARG, "eps must be a positive finite number");
+    if (mode != DP_GN_CORRECTED && mode != DP_GN_LOCAL && mode != DP_GN_STALE)
+        return fail(DP_ERR_ARG, "unknown GroupNorm mode %d", (int)mode);
+    if (act != DP_ACT_NONE && act != DP_ACT_SILU) return fail(DP_ERR_ARG, "unknown activation %d", (int)act);
+    if (w_packed != 0 && w_packed != 1) return fail(DP_ERR_ARG, "w_packed must be 0 or 1 (got %d)", w_packed);
+    if (w_packed && dtype != DP_BF16) return fail(DP_ERR_UNSUPPORTED, "packed weights are bf16 only");
+    DP_NEED(x_patch, "x_patch");
+    DP_NEED(u_stale, "u_stale");
+    DP_NEED(w, w_packed ? "w_packed" : "w");
+    DP_NEED(y_patch, "y_patch");
+    DP_OPT(gamma, "gamma");
+    DP_OPT(beta, "beta");
+    DP_OPT(fresh_stats_out, "fresh_stats_out");
+    DP_OPT(bias, "bias");
+    DP_OPT(residual, "residual");
+    if (mode != DP_GN_LOCAL && !stale_stats)
+        return fail(DP_ERR_ARG, "stale_stats is NULL (needed by this GroupNorm mode)");
+    DP_OPT(stale_stats, "stale_stats");
+    dp::GnPlan gp;
+    dp::ConvPlan cp;
+    const GnConvLayout l = gn_conv_layout(g, G, Cout, dtype == DP_BF16, &gp, &cp);
+    if (ws_bytes < l.total) return fail(DP_ERR_ARG, "workspace too small: %zu < %zu bytes", ws_bytes, l.total);
+    if (l.total) DP_NEED(ws, "ws");
+    const size_t es = elem_size(dtype);
+    const size_t band = (size_t)g.B * g.band_tokens() * g.C * es;
+    const size_t map = (size_t)g.B * g.map_tokens() * g.C * es;
+    const size_t out_band = (size_t)g.B * g.band_tokens() * Cout * es;
+    const size_t w_bytes = (size_t)Cout * 9 * g.C * es;
+    const size_t stats_bytes = (size_t)g.B * G * 2 * sizeof(float);
+    const size_t table_bytes = (size_t)g.P * stats_bytes;
+    const size_t ch_bytes = (size_t)g.C * sizeof(float);
+    const size_t wsb = l.total;
+    // written: u_stale (band i), y_patch, fresh_stats_out, ws; everything else is only read
+    if (overlaps(u_stale, map, x_patch, band) || overlaps(u_stale, map, stale_stats, table_bytes) ||
+        overlaps(u_stale, map, gamma, ch_bytes) || overlaps(u_stale, map, beta, ch_bytes) ||
+        overlaps(u_stale, map, w, w_bytes) || overlaps(u_stale, map, bias, Cout * sizeof(float)) ||
+        overlaps(u_stale, map, residual, out_band) || overlaps(u_stale, map, ws, wsb))
+        return fail(DP_ERR_ARG, "u_stale overlaps an input or the workspace");
+    if (overlaps(y_patch, out_band, x_patch, band) || overlaps(y_patch, out_band, u_stale, map) ||
+        overlaps(y_patch, out_band, stale_stats, table_bytes) || overlaps(y_patch, out_band, gamma, ch_bytes) ||
+        overlaps(y_patch, out_band, beta, ch_bytes) || overlaps(y_patch, out_band, w, w_bytes) ||
+        overlaps(y_patch, out_band, bias, Cout * sizeof(float)) || overlaps(y_patch, out_band, residual, out_band) ||
+        overlaps(y_patch, out_band, ws, wsb))
+        return fail(DP_ERR_ARG, "y_patch overlaps an input, u_stale or the workspace");
+    const bool stats_in_slot_i = stale_stats && mode == DP_GN_CORRECTED &&
+                                 fresh_stats_out == stale_stats + (size_t)g.i * g.B * G * 2;
+    if (fresh_stats_out && (overlaps(fresh_stats_out, stats_bytes, x_patch, band) ||
+                            (!stats_in_slot_i && overlaps(fresh_stats_out, stats_bytes, stale_stats, table_bytes)) ||
+                            overlaps(fresh_stats_out, stats_bytes, u_stale, map) ||
+                            overlaps(fresh_stats_out, stats_bytes, y_patch, out_band) ||
+                            overlaps(fresh_stats_out, stats_bytes, gamma, ch_bytes) ||
+                            overlaps(fresh_stats_out, stats_bytes, beta, ch_bytes) ||
+                            overlaps(fresh_stats_out, stats_bytes, w, w_bytes) ||
+                            overlaps(fresh_stats_out, stats_bytes, bias, Cout * sizeof(float)) ||
+                            overlaps(fresh_stats_out, stats_bytes, residual, out_band) ||
+                            overlaps(fresh_stats_out, stats_bytes, ws, wsb)))
+        return fail(DP_ERR_ARG, "fresh_stats_out overlaps an input, an output or the workspace");
+    if (overlaps(ws, wsb, x_patch, band) || overlaps(ws, wsb, stale_stats, table_bytes) ||
+        overlaps(ws, wsb, gamma, ch_bytes) || overlaps(ws, wsb, beta, ch_bytes) || overlaps(ws, wsb, w, w_bytes) ||
+        overlaps(ws, wsb, bias, Cout * sizeof(float)) || overlaps(ws, wsb, residual, out_band))
+        return fail(DP_ERR_ARG, "workspace overlaps an input");
+    const bool bf16 = dtype == DP_BF16;
+    char* wsc = (char*)ws;
+    if (l.fused) {
+        hipError_t e = dp::launch_gn_stats(g, gp, bf16, G, x_patch, wsc, stream);
+        if (e == hipSuccess)
+            e = dp::launch_conv_gn(g, cp, gp, G, eps, (int)mode, (int)act, x_patch, stale_stats, gamma, beta,
+                                   fresh_stats_out, u_stale, Cout, w, w_packed == 1, bias, residual, y_patch, wsc,
+                                   stream);
+        return hip_status(e, "dp_groupnorm_conv3x3_halo launch");
+    }
+    // the three calls it stands for: GroupNorm into the conv's input band, the splice of that
+    // band into u_stale (in place for B == 1), the conv
+    void* u_band = g.B == 1 ? (void*)((char*)u_stale + (size_t)g.r0 * g.W * g.C * es) : (void*)(wsc + l.band_off);
+    void* part = l.part_bytes ? (void*)(wsc + l.part_off) : nullptr;
+    hipError_t e = dp::launch_groupnorm(g, gp, bf16, G, eps, (int)mode, (int)act, x_patch, stale_stats, gamma, beta,
+                                        fresh_stats_out, u_band, part, stream);
+    if (e == hipSuccess && g.B > 1) e = dp::launch_band_copy(u_band, u_stale, g, es, stream);
+    if (e == hipSuccess)
+        e = dp::launch_conv(g, cp, bf16, Cout, u_band, u_stale, w, w_packed == 1, bias, residual, y_patch, part,
+                            stream);
+    return hip_status(e, "dp_groupnorm_conv3x3_halo launch");
+}
+
 dp_status dp_attention_splice_ws(const dp_patch* p, dp_dtype dtype, int32_t heads, int32_t head_dim,
                                  size_t* ws_bytes) {
     dp::Geom g;

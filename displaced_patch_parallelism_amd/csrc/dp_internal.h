@@ -52,6 +52,11 @@ size_t gn_apply_lds_bytes(const Geom& g, const GnPlan& plan, int G);
 // bytes (one per GPU); groupnorm_scratch returns its address on the stream's device.
 constexpr size_t kNoallocScratchBytes = (size_t)1 << 20;
 hipError_t groupnorm_scratch(hipStream_t stream, void** out);
+// The statistics pass alone: partials [nblk][B][G] (sum, sum of squares) into ws.
+hipError_t launch_gn_stats(const Geom& g, const GnPlan& plan, bool bf16, int G, const void* x, void* ws,
+                           hipStream_t stream);
+// 1 / (elements of one group in the band), as both normalising paths scale the sums.
+float gn_inv_count(const Geom& g, int G);
 hipError_t launch_groupnorm(const Geom& g, const GnPlan& plan, bool bf16, int G, float eps, int mode,
                             int act, const void* x, const float* stale_stats, const float* gamma,
                             const float* beta, float* fresh_stats_out, void* y, void* ws,
@@ -72,6 +77,16 @@ ConvPlan plan_conv(const Geom& g, int Cout, bool bf16);
 hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout, const void* x_patch,
                        const void* x_stale, const void* w, bool w_packed, const float* bias, const void* res,
                        void* y, void* ws, hipStream_t stream);
+// GroupNorm (+SiLU) folded into the 256x160-tile conv (plan kind 3): the conv's A operand is
+// the raw GroupNorm input band x_patch, normalised on the fly with the band's statistics
+// partials (launch_gn_stats, in ws) and the stale moments; the normalised band also goes to band
+// i of u_stale, the conv's stale map.  conv_gn_fusable says whether a geometry takes this path.
+bool conv_gn_fusable(const Geom& g, const ConvPlan& cp, const GnPlan& gp, int G, bool bf16);
+hipError_t launch_conv_gn(const Geom& g, const ConvPlan& cp, const GnPlan& gp, int G, float eps, int mode, int act,
+                          const void* x_patch, const float* stale_stats, const float* gamma, const float* beta,
+                          float* fresh_stats_out, void* u_stale, int Cout, const void* w, bool w_packed,
+                          const float* bias, const void* res, void* y, const void* gn_partials,
+                          hipStream_t stream);
 // bf16 weights [Cout][3][3][Cin] -> packed [3][Cin/32][3][Cout][32] (Cin % 32 == 0)
 hipError_t launch_conv_pack(int Cin, int Cout, const void* w, void* w_packed, hipStream_t stream);
 

@@ -45,6 +45,7 @@
 // f32 path: one thread per output element (correctness path for small maps).
 
 #include "dp_device.h"
+#include "dp_gn_device.h"
 #include "dp_internal.h"
 
 
@@ -69,7 +70,23 @@ struct ConvArgs {
     int kstages;         // K stages (cc, ky): 32 input channels of one kernel row; 3 * Cin / 32
     int ksplit;          // K partitions across workgroups
     int wpacked;         // weights in the packed layout [ky][Cin/32][kx][Cout][32] (else [Cout][3][3][Cin])
+    // GroupNorm (+SiLU) applied to the A operand's fresh pixels (the fused kernel only): xp is
+    // then the raw GroupNorm input band and xs the conv's stale map, whose band i receives the
+    // normalised band (the state the next step reads)
+    const float2* gn_part;   // [gn_nblk][B][G] (sum, sum of squares) partials of the band
+    const float* gn_stale;   // [P][B][G][2] previous step's moments (null in LOCAL mode)
+    const float* gn_gamma;   // [Cin] or null (1)
+    const float* gn_beta;    // [Cin] or null (0)
+    float* gn_fresh_out;     // [B][G][2] or null
+    uint16_t* ystate;        // = xs, writable
+    int gn_nblk, gn_G, gn_lanes, gn_mode, gn_silu, gn_P, gn_i;
+    float gn_inv_count, gn_eps;
 };
+
+// LDS the fused kernel adds after its ring: [lanes][G] lane sums + [G] (mean, rstd), padded to 16
+// bytes, then per-channel scale and shift; the host admits the fused kernel only when that fits.
+constexpr int kGnFuseLds = 16 * 1024;
+__host__ __device__ constexpr int gn_fuse_table_offset(int lanes, int G) { return ((lanes * G + G) * 8 + 15) & ~15; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -79,6 +96,37 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier of the K loops.  Each wave has already waited (explicit vmcnt) for its own
+// direct-to-LDS loads of the stage about to be read; the barrier then waits only for the wave's
+// own LDS reads and writes.  __syncthreads() would also wait for the loads still in flight into
+// the other ring buffers (its fence counts them), leaving the ring a single stage of lookahead.
+// The wait sits in the same asm block as the barrier, whose memory clobber keeps the compiler
+// from moving memory accesses across the pair.
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// LDS accesses of the fused normalisation, written as asm: the compiler's wait insertion takes any
+// LDS access for one that may touch the ring buffers the direct-to-LDS loads are still filling, and
+// waits for every load in flight before it.  Each thread only touches slots its own loads filled
+// (waited for explicitly) and the parameter table; the reads wait for their data in the same block.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const lds_void*)p; }
+__device__ __forceinline__ u32x4 lds_read16(uint32_t a) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a) : "memory");
+    return v;
+}
+__device__ __forceinline__ void lds_read32x2(uint32_t a, uint32_t b, u32x4& a0, u32x4& a1, u32x4& b0, u32x4& b1) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:16\n\t"
+        "ds_read_b128 %2, %5\n\tds_read_b128 %3, %5 offset:16\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(a0), "=&v"(a1), "=&v"(b0), "=&v"(b1)
+        : "v"(a), "v"(b)
+        : "memory");
+}
+__device__ __forceinline__ void lds_write16(uint32_t a, u32x4 v) {
+    asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(v) : "memory");
 }
 
 __device__ __forceinline__ int slot_swz(int p) { return (p >> 1) & 3; }
@@ -215,7 +263,30 @@ __device__ __forceinline__ void tile_origin(const ConvArgs& a, int mt, int& bb, 
 //           256 pixels instead of 128 (fewer bytes per MFMA from L2), and two stages load while
 //           one is multiplied.
 // ---------------------------------------------------------------------------
-template <int TR, int STAGES>
+// Fused GroupNorm: which kernel rows ky = 0..2 read slot s of a stage from the fresh band (bit ky
+// of the mask), and, for a fresh pixel of the tile's own columns in its own rows (kernel row 1)
+// of channel tile 0, where its normalised value goes in the conv's stale map (else null).
+template <int TR>
+__device__ __forceinline__ void fuse_slot(const ConvArgs& a, int bb, int ty0, int tx0, int s, bool own_tile,
+                                          uint32_t& fmask, uint16_t*& ysp) {
+    constexpr int HWC = kTileTC + 2;
+    const int p = s >> 2;
+    const int t = p / HWC, u = p - t * HWC;
+    const int c = (s & 3) ^ slot_swz(p);
+    const int x = tx0 + u - 1;
+    const bool xok = s < TR * HWC * 4 && x >= 0 && x < a.W;
+    fmask = 0;
+#pragma unroll
+    for (int ky = 0; ky < 3; ++ky) {
+        const int r = a.r0 + ty0 + t + ky - 1;
+        if (xok && r >= a.r0 && r < a.r0 + a.h) fmask |= 1u << ky;
+    }
+    ysp = nullptr;
+    if (own_tile && (fmask & 2u) && u >= 1 && u <= kTileTC)
+        ysp = a.ystate + (((int64_t)bb * a.H + a.r0 + ty0 + t) * a.W + x) * a.Cin + c * 8;
+}
+
+template <int TR, int STAGES, bool FUSE>
 __device__ __forceinline__ void conv_tile_body(const ConvArgs& a, char* smem) {
     constexpr int BN = 160;
     constexpr int NW = TR;                        // waves: TR / 2 row pairs x 2 channel halves
@@ -249,6 +320,21 @@ __device__ __forceinline__ void conv_tile_body(const ConvArgs& a, char* smem) {
     for (int q = 0; q < BQ; ++q) bo[q] = b_slot_offset<BN>(a, n0, wave + NW * q, lane);
     // this wave's loads per stage (the deal is uneven when NW does not divide the load counts)
     const int nloads = (S::A_LOADS - wave + NW - 1) / NW + (S::B_LOADS - wave + NW - 1) / NW;
+    // fused GroupNorm: each thread normalises the fresh pixels its own A loads brought in (all of
+    // a thread's slots hold the same 8-channel chunk cthr of their pixel)
+    uint32_t fmask[AQ];
+    uint16_t* ysp[AQ];
+    const int cthr = (lane & 3) ^ ((lane >> 3) & 3);
+    if constexpr (FUSE) {
+        static_assert(AQ <= 3, "one A load per tap: the normalisation is interleaved tap by tap");
+#pragma unroll
+        for (int q = 0; q < AQ; ++q) {
+            const int j = wave + NW * q;
+            fmask[q] = 0;
+            ysp[q] = nullptr;
+            if (j < S::A_LOADS) fuse_slot<TR>(a, bb, ty0, tx0, j * 64 + lane, nt == 0, fmask[q], ysp[q]);
+        }
+    }
 
     // Issue the loads of stage (cc, KY) into ring buffer BUF; KY is a literal so each kernel row
     // reads its own source array (a runtime select between them becomes a scratch-indexed load).
@@ -294,7 +380,148 @@ __device__ __forceinline__ void conv_tile_body(const ConvArgs& a, char* smem) {
 #pragma unroll
     for (int k = 0; k < STAGES - 1; ++k)
         if (k < nk) DPH_ISSUE(k, k);
-    for (int it = 0; it < nk; ++it) {
+
+    if constexpr (FUSE) {
+        static_assert(STAGES == 3, "the fused kernel normalises stage it+1 while it multiplies stage it");
+        // ---- the band's GroupNorm parameters, while the first stages load: the same partial
+        // sums, in the same order, as the normalising kernel's (so the normalised values are
+        // bitwise those of the two-kernel path) ----
+        const int G = a.gn_G, L = a.gn_lanes;
+        float2* gred = (float2*)(smem + STAGES * S::BYTES);    // [L][G]
+        float2* gmr = gred + L * G;                             // [G] (mean, rstd)
+        float* tsc = (float*)(smem + STAGES * S::BYTES + gn_fuse_table_offset(L, G));   // [Cin] scale
+        float* tsf = tsc + a.Cin;                               // [Cin] shift
+        if (tid < L * G) {
+            const int g = tid % G, j0 = tid / G;
+            float sa = 0.f, sq = 0.f;
+            for (int jb = j0; jb < a.gn_nblk; jb += 8 * L) {
+                float2 pv[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int j = jb + u * L;
+                    pv[u] = j < a.gn_nblk ? a.gn_part[((int64_t)j * a.B + bb) * G + g] : make_float2(0.f, 0.f);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    sa += pv[u].x;
+                    sq += pv[u].y;
+                }
+            }
+            gred[j0 * G + g] = make_float2(sa, sq);
+        }
+        __syncthreads();
+        if (tid < G) {
+            const int g = tid;
+            float sa = 0.f, sq = 0.f;
+            for (int k = 0; k < L; ++k) {
+                sa += gred[k * G + g].x;
+                sq += gred[k * G + g].y;
+            }
+            float st_e = 0.f, st_q = 0.f;
+            if (a.gn_mode != 1) {
+                for (int j = 0; j < a.gn_P; ++j) {
+                    if (a.gn_mode == 0 && j == a.gn_i) continue;
+                    st_e += a.gn_stale[(((int64_t)j * a.B + bb) * G + g) * 2 + 0];
+                    st_q += a.gn_stale[(((int64_t)j * a.B + bb) * G + g) * 2 + 1];
+                }
+            }
+            const float m = sa * a.gn_inv_count, qm = sq * a.gn_inv_count;
+            if (a.gn_fresh_out && nt == 0 && ty0 == 0 && tx0 == 0) {   // one workgroup per batch image
+                a.gn_fresh_out[(bb * G + g) * 2 + 0] = m;
+                a.gn_fresh_out[(bb * G + g) * 2 + 1] = qm;
+            }
+            gmr[g] = gn_group_norm_params(m, qm, st_e, st_q, a.gn_mode, a.gn_P, a.gn_eps);
+        }
+        __syncthreads();
+        const int cg = a.Cin / G;
+        for (int c = tid; c < a.Cin; c += 64 * NW)
+            gn_scale_shift(gmr[c / cg], a.gn_gamma ? a.gn_gamma[c] : 1.f, a.gn_beta ? a.gn_beta[c] : 0.f, tsc[c],
+                           tsf[c]);
+        __syncthreads();
+    }
+    // the fresh pixels of this thread's slot of load Q in stage K (ring buffer BUF), normalised in
+    // place; those of the tile's own rows and columns (kernel row 1) also go to the stale map
+#define DPH_XFORM_TABLE(K)                                                                          \
+    do {                                                                                            \
+        const float* gt_ = (const float*)(smem + STAGES * S::BYTES + gn_fuse_table_offset(a.gn_lanes, a.gn_G)); \
+        const int ch_ = ((K) / 3) * 32 + cthr * 8;                                                  \
+        u32x4 s0_, s1_, f0_, f1_;                                                                   \
+        lds_read32x2(lds_addr(gt_ + ch_), lds_addr(gt_ + a.Cin + ch_), s0_, s1_, f0_, f1_);         \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                             \
+            xsc_[e] = __uint_as_float(s0_[e]);                                                      \
+            xsc_[e + 4] = __uint_as_float(s1_[e]);                                                  \
+            xsf_[e] = __uint_as_float(f0_[e]);                                                      \
+            xsf_[e + 4] = __uint_as_float(f1_[e]);                                                  \
+        }                                                                                           \
+    } while (0)
+#define DPH_XFORM_Q(K, BUF, Q)                                                                      \
+    do {                                                                                            \
+        const int ky_ = (K) % 3;                                                                    \
+        if ((fmask[Q] >> ky_) & 1u) {                                                               \
+            const uint32_t sl_ = lds_addr(smem + (BUF) * S::BYTES + (wave + NW * (Q)) * 1024 + lane * 16); \
+            const u32x4 r_ = lds_read16(sl_);                                                       \
+            float f_[8];                                                                            \
+            unpack8(make_uint4(r_[0], r_[1], r_[2], r_[3]), f_);                                    \
+            _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                         \
+                float z_ = fmaf(f_[e], xsc_[e], xsf_[e]);                                           \
+                if (a.gn_silu) z_ = silu(z_);                                                       \
+                f_[e] = z_;                                                                         \
+            }                                                                                       \
+            const uint4 v_ = pack8(f_);                                                             \
+            lds_write16(sl_, u32x4{v_.x, v_.y, v_.z, v_.w});                                        \
+            if (ky_ == 1 && ysp[Q]) *(uint4*)(ysp[Q] + ((K) / 3) * 32) = v_;                        \
+        }                                                                                           \
+    } while (0)
+    float xsc_[8], xsf_[8];      // scale and shift of this thread's 8 channels of one stage
+    if constexpr (FUSE) {
+        if (nk > 0) {
+            // this wave's loads of stage 0 have landed (stage 1's may still be in flight)
+            if (nk > 1) {
+                if (nloads >= 7) wait_vmcnt<7>();
+                else if (nloads == 6) wait_vmcnt<6>();
+                else if (nloads == 5) wait_vmcnt<5>();
+                else wait_vmcnt<0>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            DPH_XFORM_TABLE(0);
+#pragma unroll
+            for (int q = 0; q < AQ; ++q) DPH_XFORM_Q(0, 0, q);
+        }
+        for (int it = 0; it < nk; ++it) {
+            ring_barrier();      // stage it normalised by every thread; everyone is done with stage it-1
+            if (it + 2 < nk) DPH_ISSUE(it + 2, (it + 2) % 3);
+            const bool nxt = it + 1 < nk;
+            if (nxt) {           // this wave's loads of stage it+1 have landed (stage it+2's may not)
+                if (it + 2 < nk) {
+                    if (nloads >= 7) wait_vmcnt<7>();
+                    else if (nloads == 6) wait_vmcnt<6>();
+                    else if (nloads == 5) wait_vmcnt<5>();
+                    else wait_vmcnt<0>();
+                } else {
+                    wait_vmcnt<0>();
+                }
+                DPH_XFORM_TABLE(it + 1);
+            }
+            // stage it's 60 MFMAs, tap by tap, with stage it+1's normalisation between the taps
+            const char* st = smem + (it % 3) * S::BYTES;
+#pragma unroll
+            for (int kx = 0; kx < 3; ++kx) {
+                bf16x8 af[4], bfr[5];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8*)(st + aoff[i >> 1][kx] + (i & 1) * 1024);
+#pragma unroll
+                for (int n = 0; n < 5; ++n) bfr[n] = *(const bf16x8*)(st + boff + (kx * BN + n * 16) * 64);
+                if (nxt && kx < AQ) DPH_XFORM_Q(it + 1, (it + 1) % 3, kx);
+#pragma unroll
+                for (int n = 0; n < 5; ++n)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[i][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[n], acc[i][n], 0, 0, 0);
+            }
+        }
+    }
+    for (int it = 0; it < (FUSE ? 0 : nk); ++it) {
         // this wave's loads of stage it have landed (those of the stages after it, issued later,
         // may still be in flight; loads complete in order) ...
         if (STAGES == 2 || it + 1 >= nk) {
@@ -307,12 +534,14 @@ __device__ __forceinline__ void conv_tile_body(const ConvArgs& a, char* smem) {
             else if (nloads == 5) wait_vmcnt<5>();
             else wait_vmcnt<0>();
         }
-        __syncthreads();     // ... and everyone's; everyone is also done with stage it-1
+        ring_barrier();      // ... and everyone's; everyone is also done with stage it-1
         if (it + STAGES - 1 < nk) DPH_ISSUE(it + STAGES - 1, (it + STAGES - 1) % STAGES);
         stage_mfma<BN>(smem + (it % STAGES) * S::BYTES, aoff, boff, acc);
     }
 #undef DPH_ISSUE
 #undef DPH_ISSUE_KY
+#undef DPH_XFORM_TABLE
+#undef DPH_XFORM_Q
     __syncthreads();   // ring no longer read: reuse it for the output tile
 
     // acc[i][n][r] = D[pixel 16i + 4(l>>4) + r of the wave][channel 16n + (l&15) of the wave]
@@ -386,12 +615,22 @@ constexpr int tile_smem() {
 
 __global__ __launch_bounds__(256, 2) void conv3x3_bf16_halo_tile_kernel(ConvArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[tile_smem<4, 2>()];
-    conv_tile_body<4, 2>(a, smem);
+    conv_tile_body<4, 2, false>(a, smem);
 }
 
 __global__ __launch_bounds__(512, 1) void conv3x3_bf16_halo_tile8_kernel(ConvArgs a) {
     __shared__ __attribute__((aligned(1024))) char smem[tile_smem<8, 3>()];
-    conv_tile_body<8, 3>(a, smem);
+    conv_tile_body<8, 3, false>(a, smem);
+}
+
+// The 256x160-tile conv whose A operand's fresh pixels are the raw GroupNorm input, normalised
+// (+ SiLU) on the fly: GroupNorm-apply fused into the conv (the statistics pass runs before it).
+// Halo rows come from the conv's stale map, already normalised by the previous step; zero padding
+// stays zero.  Channel tile 0 also writes the normalised band into band i of that map.
+__global__ __launch_bounds__(512, 1) void conv3x3_bf16_gn_tile8_kernel(ConvArgs a) {
+    static_assert(tile_smem<8, 3>() + kGnFuseLds <= 160 * 1024, "LDS of one workgroup");
+    __shared__ __attribute__((aligned(1024))) char smem[tile_smem<8, 3>() + kGnFuseLds];
+    conv_tile_body<8, 3, true>(a, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -736,19 +975,11 @@ hipError_t launch_conv_pack(int Cin, int Cout, const void* w, void* w_packed, hi
     return hipGetLastError();
 }
 
-hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout, const void* x_patch,
-                       const void* x_stale, const void* w, bool w_packed, const float* bias, const void* res,
-                       void* y, void* ws, hipStream_t stream) {
-    if (!bf16) {
-        const int64_t total = (int64_t)g.B * g.h * g.W * Cout;
-        const int64_t blocks = (total + 255) / 256;
-        if (!grid_fits(blocks)) return hipErrorInvalidConfiguration;
-        conv3x3_f32_direct_kernel<<<(unsigned)blocks, 256, 0, stream>>>(
-            (const float*)x_patch, (const float*)x_stale, (const float*)w, bias, (const float*)res, (float*)y, g.B,
-            g.H, g.W, g.C, Cout, g.h, g.r0);
-        return hipGetLastError();
-    }
-    ConvArgs a;
+namespace {
+
+ConvArgs conv_args(const Geom& g, const ConvPlan& plan, int Cout, const void* x_patch, const void* x_stale,
+                   const void* w, bool w_packed, const float* bias, const void* res, void* y, void* ws) {
+    ConvArgs a{};
     a.xp = (const uint16_t*)x_patch;
     a.xs = (const uint16_t*)x_stale;
     a.w = (const uint16_t*)w;
@@ -772,6 +1003,24 @@ hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout,
     a.kstages = plan.ktiles;
     a.ksplit = plan.ksplit;
     a.wpacked = w_packed ? 1 : 0;
+    return a;
+}
+
+}  // namespace
+
+hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout, const void* x_patch,
+                       const void* x_stale, const void* w, bool w_packed, const float* bias, const void* res,
+                       void* y, void* ws, hipStream_t stream) {
+    if (!bf16) {
+        const int64_t total = (int64_t)g.B * g.h * g.W * Cout;
+        const int64_t blocks = (total + 255) / 256;
+        if (!grid_fits(blocks)) return hipErrorInvalidConfiguration;
+        conv3x3_f32_direct_kernel<<<(unsigned)blocks, 256, 0, stream>>>(
+            (const float*)x_patch, (const float*)x_stale, (const float*)w, bias, (const float*)res, (float*)y, g.B,
+            g.H, g.W, g.C, Cout, g.h, g.r0);
+        return hipGetLastError();
+    }
+    ConvArgs a = conv_args(g, plan, Cout, x_patch, x_stale, w, w_packed, bias, res, y, ws);
     const int64_t nwg = (int64_t)plan.mtiles * plan.ntiles * plan.ksplit;
     const int64_t total4 = (int64_t)a.M * Cout / 4;
     if (!grid_fits(nwg) || (plan.ksplit > 1 && !grid_fits((total4 + 255) / 256))) return hipErrorInvalidConfiguration;
@@ -786,6 +1035,40 @@ hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout,
         conv_splitk_reduce_kernel<<<(unsigned)((total4 + 255) / 256), 256, 0, stream>>>(
             (const float*)ws, bias, (const uint16_t*)res, (uint16_t*)y, total4, Cout, plan.ksplit);
     }
+    return hipGetLastError();
+}
+
+bool conv_gn_fusable(const Geom& g, const ConvPlan& cp, const GnPlan& gp, int G, bool bf16) {
+    if (!bf16 || cp.kind != 3 || cp.ksplit != 1 || G < 1 || gp.threads < G) return false;
+    const int lanes = gp.threads / G;            // the normalising kernel's lanes per group
+    return lanes * G <= 512 && G <= 512 && gn_fuse_table_offset(lanes, G) + 8 * g.C <= kGnFuseLds;
+}
+
+hipError_t launch_conv_gn(const Geom& g, const ConvPlan& cp, const GnPlan& gp, int G, float eps, int mode, int act,
+                          const void* x_patch, const float* stale_stats, const float* gamma, const float* beta,
+                          float* fresh_stats_out, void* u_stale, int Cout, const void* w, bool w_packed,
+                          const float* bias, const void* res, void* y, const void* gn_partials,
+                          hipStream_t stream) {
+    if (!conv_gn_fusable(g, cp, gp, G, true)) return hipErrorInvalidValue;
+    ConvArgs a = conv_args(g, cp, Cout, x_patch, u_stale, w, w_packed, bias, res, y, nullptr);
+    a.gn_part = (const float2*)gn_partials;
+    a.gn_stale = mode == 1 ? nullptr : stale_stats;
+    a.gn_gamma = gamma;
+    a.gn_beta = beta;
+    a.gn_fresh_out = fresh_stats_out;
+    a.ystate = (uint16_t*)u_stale;
+    a.gn_nblk = gp.nblk;
+    a.gn_G = G;
+    a.gn_lanes = gp.threads / G;
+    a.gn_mode = mode;
+    a.gn_silu = act == 1 ? 1 : 0;
+    a.gn_P = g.P;
+    a.gn_i = g.i;
+    a.gn_inv_count = gn_inv_count(g, G);
+    a.gn_eps = eps;
+    const int64_t nwg = (int64_t)cp.mtiles * cp.ntiles;
+    if (!grid_fits(nwg)) return hipErrorInvalidConfiguration;
+    conv3x3_bf16_gn_tile8_kernel<<<(unsigned)nwg, 512, 0, stream>>>(a);
     return hipGetLastError();
 }
 

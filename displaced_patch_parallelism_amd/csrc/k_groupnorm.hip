@@ -32,6 +32,7 @@
 
 
 #include "dp_device.h"
+#include "dp_gn_device.h"
 #include "dp_internal.h"
 
 #include <mutex>
@@ -285,16 +286,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(6))) void gn_apply_kernel(GnApplyA
             a.fresh_out[(b * G + g) * 2 + 0] = m;
             a.fresh_out[(b * G + g) * 2 + 1] = qm;
         }
-        float E = m, Q = qm;
-        if (a.mode == 0) {            // corrected: own band fresh, the others stale
-            E = (m + st_e) / (float)a.P;
-            Q = (qm + st_q) / (float)a.P;
-        } else if (a.mode == 2) {     // stale: every band from the table
-            E = st_e / (float)a.P;
-            Q = st_q / (float)a.P;
-        }
-        const float var = fmaxf(Q - E * E, 0.f);
-        mr[g] = make_float2(E, 1.0f / sqrtf(var + a.eps));
+        mr[g] = gn_group_norm_params(m, qm, st_e, st_q, a.mode, a.P, a.eps);
     }
     if (!a.y) return;
     __syncthreads();
@@ -310,11 +302,7 @@ __global__ __attribute__((amdgpu_waves_per_eu(6))) void gn_apply_kernel(GnApplyA
     }
     float sc[VEC], sf[VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-        const float2 mv = mr[(cv * VEC + e) / cg];
-        sc[e] = mv.y * ga[e];
-        sf[e] = be[e] - mv.x * sc[e];
-    }
+    for (int e = 0; e < VEC; ++e) gn_scale_shift(mr[(cv * VEC + e) / cg], ga[e], be[e], sc[e], sf[e]);
     uint4* yv = (uint4*)a.y + base;
     const int64_t t_end = (int64_t)(blockIdx.x + 1) * a.tok_per_blk < a.tokens
                               ? (int64_t)(blockIdx.x + 1) * a.tok_per_blk : a.tokens;
@@ -467,6 +455,23 @@ GnPlan plan_groupnorm(const Geom& g, int G, bool bf16) {
     return p;
 }
 
+hipError_t launch_gn_stats(const Geom& g, const GnPlan& plan, bool bf16, int G, const void* x, void* ws,
+                           hipStream_t stream) {
+    const dim3 grid((unsigned)plan.nblk, (unsigned)g.B);
+    const size_t shmem = gn_stats_lds_bytes(g, plan);
+    if (bf16)
+        gn_stats_kernel<true><<<grid, plan.threads_stats, shmem, stream>>>(x, g.band_tokens(), g.C, G, plan.vpt,
+                                                                          plan.rows_stats, plan.tok_per_blk,
+                                                                          (float2*)ws);
+    else
+        gn_stats_kernel<false><<<grid, plan.threads_stats, shmem, stream>>>(x, g.band_tokens(), g.C, G, plan.vpt,
+                                                                           plan.rows_stats, plan.tok_per_blk,
+                                                                           (float2*)ws);
+    return hipGetLastError();
+}
+
+float gn_inv_count(const Geom& g, int G) { return 1.0f / (float)((double)g.band_tokens() * (g.C / G)); }
+
 hipError_t launch_groupnorm(const Geom& g, const GnPlan& plan, bool bf16, int G, float eps, int mode, int act,
                             const void* x, const float* stale_stats, const float* gamma, const float* beta,
                             float* fresh_stats_out, void* y, void* ws, hipStream_t stream) {
@@ -485,7 +490,7 @@ hipError_t launch_groupnorm(const Geom& g, const GnPlan& plan, bool bf16, int G,
     a.vpt = plan.vpt;
     a.rows = plan.rows;
     a.tok_per_blk = 0;
-    a.inv_count = 1.0f / (float)((double)a.tokens * (g.C / G));
+    a.inv_count = gn_inv_count(g, G);
     a.eps = eps;
     a.stale = stale_stats;
     a.gamma = gamma;

@@ -28,8 +28,8 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import torch
 
 from . import (Patch, _dtype_code, dp_attention_splice, dp_conv3x3_halo, dp_conv3x3_halo_packed,
-               dp_conv3x3_halo_residual, dp_conv3x3_pack_weights, dp_groupnorm_async, dp_linear,
-               dp_linear_residual, dp_stale_update, dp_stats_update, workspace_bytes)
+               dp_conv3x3_halo_residual, dp_conv3x3_pack_weights, dp_groupnorm_async, dp_groupnorm_conv3x3_halo,
+               dp_linear, dp_linear_residual, dp_stale_update, dp_stats_update, workspace_bytes)
 
 GN_STEPS = ("gn", "gn_silu")
 CONV_STEPS = ("conv", "conv_res")
@@ -57,8 +57,11 @@ def _done(end):
 
 class DisplacedLayer:
     def __init__(self, cfg, convs: Sequence[Tuple["np.ndarray", "np.ndarray"]], device="cuda",  # noqa: F821
-                 projs=None):
+                 projs=None, fuse=False):
         self.cfg = cfg
+        # fuse: a GroupNorm step that feeds a conv runs as one dp_groupnorm_conv3x3_halo call when
+        # the state is refreshed in place (else as its two calls)
+        self.fuse = fuse
         self.device = torch.device(device)
         self.dt = torch_dtype(cfg.dtype)
         self.convs = [(torch.as_tensor(w).to(self.device, self.dt).contiguous(),
@@ -94,9 +97,15 @@ class DisplacedLayer:
         need = 0
         for w, _ in self.convs:
             need = max(need, workspace_bytes("conv", self.patch(0), code, int(w.shape[0])))
-        for s in c.graph:
+        conv_j = 0
+        for k, s in enumerate(c.graph):
             if s in GN_STEPS:
                 need = max(need, workspace_bytes("groupnorm", self.patch(0), code, c.G))
+                if k + 1 < len(c.graph) and c.graph[k + 1] in CONV_STEPS:
+                    need = max(need, workspace_bytes("groupnorm_conv", self.patch(0), code, c.G,
+                                                     int(self.convs[conv_j][0].shape[0])))
+            elif s in CONV_STEPS:
+                conv_j += 1
             elif s == "attn" or s in PROJ_STEPS:
                 need = max(need, workspace_bytes("attention", self.patch(0), code, c.heads, c.C // c.heads))
         self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
@@ -130,10 +139,11 @@ class DisplacedLayer:
 
     # ---- one patch, displaced ------------------------------------------------
     def calls(self, x_patch, i, gn_mode="corrected", update_state=True):
-        """Patch i's displaced layer step as a list of (name, launch, output): each launch
-        enqueues one C-ABI call on the current stream; ``output`` is the graph step's patch
-        output on the last call of that step and None on the others.  Running them in order
-        is one step (without the splice of ``step`` when the state is not refreshed in place)."""
+        """Patch i's displaced layer step as a list of (name, launch, outputs): each launch
+        enqueues one C-ABI call on the current stream; ``outputs`` are the graph steps' patch
+        outputs that call completes (none, one, or -- for a GroupNorm fused with its conv --
+        two).  Running them in order is one step (without the splice of ``step`` when the
+        state is not refreshed in place)."""
         c = self.cfg
         p = self.patch(i)
         in_place = update_state and c.B == 1 and gn_mode == "corrected"
@@ -141,12 +151,38 @@ class DisplacedLayer:
         out_list = []
         conv_i = 0
         proj_i = 0
+        fused_next = False
         for k, s in enumerate(c.graph):
             nxt = k + 1
             if in_place and nxt < len(c.graph) and nxt in self.maps:
                 out = self.maps[nxt][:, i * c.h:(i + 1) * c.h]      # contiguous for B == 1
             else:
                 out = self.bufs[k]
+            if fused_next:           # this conv ran inside the GroupNorm call before it
+                fused_next = False
+                conv_i += 1
+                h = out
+                continue
+            if (s in GN_STEPS and in_place and self.fuse and nxt < len(c.graph) and c.graph[nxt] in CONV_STEPS):
+                # GroupNorm (+SiLU) and the conv it feeds in one call: the normalised band goes
+                # straight into band i of the conv's stale map (``out``), the conv's output to
+                # the conv step's own output
+                table = self.tables[k]
+                act = "silu" if s == "gn_silu" else None
+                cout_k = nxt + 1
+                y = self.maps[cout_k][:, i * c.h:(i + 1) * c.h] if cout_k < len(c.graph) and cout_k in self.maps \
+                    else self.bufs[nxt]
+                res = x_patch if c.graph[nxt] == "conv_res" else None
+                w, b = self.convs[conv_i]
+                wp = self.wpacked[conv_i]
+                fn = (lambda h=h, y=y, table=table, act=act, res=res, w=w if wp is None else wp, b=b,
+                      u=self.maps[nxt]: dp_groupnorm_conv3x3_halo(
+                          p, h, c.G, u, w, b, stale_stats=table, eps=c.eps, mode=gn_mode, act=act,
+                          fresh_stats_out=table[i], residual=res, y_patch=y, packed=wp is not None, ws=self.ws))
+                out_list.append((f"{s}+{c.graph[nxt]}", fn, (out, y)))
+                fused_next = True
+                h = out
+                continue
             if s in GN_STEPS:
                 table = self.tables[k]
                 stats = table[i] if in_place else self.fresh[k]
@@ -173,23 +209,23 @@ class DisplacedLayer:
                 else:
                     kb, vb = self._tok(pb["k"]), self._tok(pb["v"])
                 tok, q, a = self._tok(h), self._tok(pb["q"]), self._tok(pb["a"])
-                out_list.append(("proj_q", lambda tok=tok, q=q, w=wq, b=bq: dp_linear(tok, w, b, y=q), None))
-                out_list.append(("proj_k", lambda tok=tok, y=kb, w=wk, b=bk: dp_linear(tok, w, b, y=y), None))
-                out_list.append(("proj_v", lambda tok=tok, y=vb, w=wv, b=bv: dp_linear(tok, w, b, y=y), None))
+                out_list.append(("proj_q", lambda tok=tok, q=q, w=wq, b=bq: dp_linear(tok, w, b, y=q), ()))
+                out_list.append(("proj_k", lambda tok=tok, y=kb, w=wk, b=bk: dp_linear(tok, w, b, y=y), ()))
+                out_list.append(("proj_v", lambda tok=tok, y=vb, w=wv, b=bv: dp_linear(tok, w, b, y=y), ()))
                 out_list.append(("attn", lambda q=q, kb=kb, vb=vb, a=a, ks=self._tok(kcache), vs=self._tok(vcache):
-                                 dp_attention_splice(p, c.heads, q, kb, vb, ks, vs, o_patch=a, ws=self.ws), None))
+                                 dp_attention_splice(p, c.heads, q, kb, vb, ks, vs, o_patch=a, ws=self.ws), ()))
                 if s == "attn_proj_res":
                     fn = (lambda a=a, o=self._tok(out), w=wo, b=bo, r=self._tok(x_patch):
                           dp_linear_residual(a, w, b, r, y=o))
                 else:
                     fn = (lambda a=a, o=self._tok(out), w=wo, b=bo: dp_linear(a, w, b, y=o))
                 s = "proj_o"
-            out_list.append((s, fn, out))
+            out_list.append((s, fn, (out,)))
             h = out
         if in_place and 0 in self.maps:
             # a graph that starts with a conv or attention: its stale map's band i is the layer
             # input itself, which no earlier call wrote in place
-            out_list.append(("stale_update", lambda: dp_stale_update(p, x_patch, self.maps[0]), None))
+            out_list.append(("stale_update", lambda: dp_stale_update(p, x_patch, self.maps[0]), ()))
         return out_list
 
     def step(self, x_patch, i, gn_mode="corrected", update_state=True, events=None) -> List[torch.Tensor]:
@@ -211,12 +247,11 @@ class DisplacedLayer:
         c = self.cfg
         in_place = update_state and c.B == 1 and gn_mode == "corrected"
         outs = []
-        for s, fn, out in self.calls(x_patch, i, gn_mode, update_state):
+        for s, fn, done in self.calls(x_patch, i, gn_mode, update_state):
             ev = _mark(events, s)
             fn()
             _done(ev)
-            if out is not None:
-                outs.append(out)
+            outs.extend(done)
         if update_state and not in_place:
             self.splice_state(i, x_patch, outs, events)
         return outs

@@ -23,6 +23,9 @@
  *   dp_conv3x3_halo_residual, dp_linear_residual
  *                        the conv and the projection with a block's skip
  *                        connection added before rounding
+ *   dp_groupnorm_conv3x3_halo
+ *                        GroupNorm (+SiLU) and the conv that consumes it in
+ *                        one call, the normalisation folded into the conv
  *
  * Geometry.  Maps are NHWC, batch-major: element (b, r, c, ch) of a [B][H][W][C]
  * map sits at ((b*H + r)*W + c)*C + ch.  The P patches are equal row bands:
@@ -246,6 +249,49 @@ dp_status dp_conv3x3_halo_residual(const dp_patch* p, dp_dtype dtype, int32_t Co
                                    const void* x_stale, const void* w, int32_t w_packed, const float* bias,
                                    const void* residual, void* y_patch, void* ws, size_t ws_bytes,
                                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * dp_groupnorm_conv3x3_halo -- GroupNorm (+SiLU) of patch i, then the 3x3
+ * conv with stale halo on the normalised band, which also replaces band i of
+ * the conv's stale map: the three calls
+ *   dp_groupnorm_async(x_patch -> u_patch)
+ *   dp_stale_update(u_patch -> band i of u_stale)
+ *   dp_conv3x3_halo_residual(u_patch, u_stale -> y_patch)
+ * in one, with bitwise the same results (u_stale, y_patch, fresh_stats_out).
+ *
+ * Source: the GroupNorm as dp_groupnorm_async (DistriFusion summary on
+ * atlas.scime.ai, Approach) feeding the convolution of dp_conv3x3_halo
+ * (study.space page, Method): in the denoiser's ResNet blocks a GroupNorm and
+ * its activation precede every 3x3 conv, and the normalised band is what the
+ * next step's halo rows come from.  Where the 256x160-tile conv runs (bf16,
+ * large bands) the normalisation is folded into the conv's operand loads: the
+ * band is read once raw (statistics) and once by the conv, and the normalised
+ * band is never read back from memory.  Other shapes run the three kernels.
+ *
+ *   x_patch         [B][h][W][C] dtype, the GroupNorm input band
+ *   stale_stats, gamma, beta, fresh_stats_out, G, eps, mode, act
+ *                   as dp_groupnorm_async (fresh_stats_out may be slot i of
+ *                   stale_stats in DP_GN_CORRECTED mode)
+ *   u_stale         [B][H][W][C] dtype, the conv input's stale map (the
+ *                   previous step's normalised map); band i is overwritten
+ *                   with this step's normalised band, other rows only read
+ *   Cout, w, w_packed, bias, residual
+ *                   as dp_conv3x3_halo_residual (residual may be NULL)
+ *   y_patch         [B][h][W][Cout] dtype
+ *   ws              >= dp_groupnorm_conv3x3_halo_ws bytes
+ * No written buffer (u_stale, y_patch, fresh_stats_out, ws) may overlap
+ * another buffer of the call, except the slot-i case above.  Requirements
+ * and errors are those of dp_groupnorm_async and dp_conv3x3_halo together
+ * (y_patch is required); nothing is enqueued when a check fails.
+ * ---------------------------------------------------------------------- */
+dp_status dp_groupnorm_conv3x3_halo_ws(const dp_patch* p, dp_dtype dtype, int32_t G, int32_t Cout,
+                                       size_t* ws_bytes);
+
+dp_status dp_groupnorm_conv3x3_halo(const dp_patch* p, dp_dtype dtype, int32_t G, float eps, dp_gn_mode mode,
+                                    dp_act act, const void* x_patch, const float* stale_stats, const float* gamma,
+                                    const float* beta, float* fresh_stats_out, void* u_stale, int32_t Cout,
+                                    const void* w, int32_t w_packed, const float* bias, const void* residual,
+                                    void* y_patch, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * dp_attention_splice -- self-attention of patch i over spliced K/V.

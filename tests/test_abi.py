@@ -279,3 +279,78 @@ def test_residual_entry_points_validate():
     assert "overlap" in L.dp_last_error().decode()
     assert lin(dp.DP_BF16, 16, 64, 64, FAKE, 64, FAKE2, None, 0x40000000, 68, 0x30000000, 64,
                None) == dp.DP_ERR_UNSUPPORTED
+
+
+def gn_conv_ws(p, dtype, G, cout):
+    out = ctypes.c_size_t(123)
+    st = dp.lib().dp_groupnorm_conv3x3_halo_ws(dp._cpatch(p), dtype, G, cout, ctypes.byref(out))
+    return st, out.value
+
+
+@pytest.mark.parametrize("p,G,cout,fused", [
+    # 256x160-tile conv, GroupNorm lanes x groups <= 512 and its parameter table in the LDS
+    (dp.Patch(2, 208, 232, 128, 4, 1), 32, 192, True),
+    (dp.Patch(2, 480, 480, 320, 8, 3), 32, 320, True),
+    # 256x160 tiles, but C = 1664 channels' scale and shift do not fit next to the ring
+    (dp.Patch(2, 128, 768, 1664, 2, 0), 32, 32, False),
+    # small map (64x80 tiles, K split) and the fp32 conv: three kernels
+    (dp.Patch(2, 64, 64, 320, 4, 1), 32, 320, False),
+    (dp.Patch(2, 8, 6, 16, 2, 1), 4, 12, False),
+])
+def test_groupnorm_conv_workspace_layout(p, G, cout, fused):
+    """The fused path needs only the statistics partials; otherwise a batched call normalises
+    into a band in the workspace (256-byte aligned), followed by one region the GroupNorm
+    partials and then the conv's split-K partials use in turn."""
+    dtype = dp.DP_F32 if p.C == 16 else dp.DP_BF16
+    st, n = gn_conv_ws(p, dtype, G, cout)
+    assert st == dp.DP_OK
+    gn = ws_query("gn", p, dtype, G)[1]
+    conv = ws_query("conv", p, dtype, cout)[1]
+    if fused:
+        assert n == gn
+    else:
+        band = p.B * (p.H // p.P) * p.W * p.C * (2 if dtype == dp.DP_BF16 else 4)
+        assert n == (band + 255) // 256 * 256 + max(gn, conv)
+    p1 = dp.Patch(1, *list(p)[1:])
+    st, n1 = gn_conv_ws(p1, dtype, G, cout)
+    assert st == dp.DP_OK and n1 == max(ws_query("gn", p1, dtype, G)[1], ws_query("conv", p1, dtype, cout)[1])
+
+
+def call_gn_conv(p=dp.Patch(1, 16, 32, 64, 2, 1), dtype=dp.DP_BF16, G=8, mode=0, act=1, x=FAKE,
+                 table=0x50000000, fresh=None, u=FAKE2, cout=64, w=0x30000000, packed=0, res=None,
+                 y=0x40000000, ws=0x60000000, ws_bytes=1 << 24):
+    return dp.lib().dp_groupnorm_conv3x3_halo(dp._cpatch(p), dtype, G, 1e-5, mode, act, x, table, None, None,
+                                              fresh, u, cout, w, packed, None, res, y, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    ({"x": FAKE2 + 8 * 32 * 64 * 2}, dp.DP_ERR_ARG, "u_stale overlaps"),     # x_patch = band i of u_stale
+    ({"y": FAKE2 + 64}, dp.DP_ERR_ARG, "y_patch overlaps"),
+    ({"res": 0x40000000 + 32}, dp.DP_ERR_ARG, "y_patch overlaps"),
+    ({"fresh": FAKE2}, dp.DP_ERR_ARG, "fresh_stats_out overlaps"),
+    ({"fresh": 0x50000000, "mode": 2}, dp.DP_ERR_ARG, "fresh_stats_out overlaps"),   # slot 0, STALE mode
+    ({"ws": FAKE2 + 1024}, dp.DP_ERR_ARG, "overlaps"),
+    ({"ws_bytes": 0}, dp.DP_ERR_ARG, "workspace too small"),
+    ({"y": 0}, dp.DP_ERR_ARG, "y_patch is NULL"),
+    ({"u": 0}, dp.DP_ERR_ARG, "u_stale is NULL"),
+    ({"table": 0}, dp.DP_ERR_ARG, "stale_stats is NULL"),
+    ({"packed": 2}, dp.DP_ERR_ARG, "w_packed"),
+    ({"packed": 1, "dtype": dp.DP_F32}, dp.DP_ERR_UNSUPPORTED, "bf16 only"),
+    ({"cout": 48}, dp.DP_ERR_UNSUPPORTED, "Cout % 32"),
+    ({"G": 7}, dp.DP_ERR_ARG, "divisible"),
+    ({"mode": 5}, dp.DP_ERR_ARG, "mode"),
+    ({"act": 3}, dp.DP_ERR_ARG, "activation"),
+])
+def test_groupnorm_conv_rejects(kw, code, msg):
+    """Invalid calls fail on the host, before anything is enqueued."""
+    assert call_gn_conv(**kw) == code
+    assert msg in dp.lib().dp_last_error().decode()
+
+
+def test_groupnorm_conv_accepts_fresh_moments_in_slot_i():
+    """CORRECTED mode never reads slot i of the table, so the fresh moments may go there; the
+    other checks pass too (an invalid workspace size then shows the call got that far)."""
+    p = dp.Patch(1, 16, 32, 64, 2, 1)
+    slot_i = 0x50000000 + 1 * 1 * 8 * 2 * 4
+    assert call_gn_conv(p=p, fresh=slot_i, ws_bytes=0) == dp.DP_ERR_ARG
+    assert "workspace too small" in dp.lib().dp_last_error().decode()

@@ -185,3 +185,68 @@ def test_stale_equal_fresh_gives_warmup_output(name):
         outs = layer.step(gpu(inp.x[:, i * c.h:(i + 1) * c.h], c.dtype), i, update_state=False)
         for k, (g, w) in enumerate(zip(outs, warm)):
             assert_parity(host(g), host(w)[:, i * c.h:(i + 1) * c.h], c.dtype, f"patch {i} step {k}")
+
+
+FUSE_CASES = {
+    "c4a": CONFIGS["c4a"],                 # GroupNorm folded into the 256x160-tile conv
+    "c1r": CONFIGS["c1r"],                 # small-map ResNet block: three kernels inside the call
+    # a ResNet block on 256x160 tiles: both GroupNorm sites folded, the second conv adding the skip
+    "resnet-tile8": LayerConfig("r8", "bf16", B=1, H=192, W=512, C=128, G=32, P=2,
+                                graph=("gn_silu", "conv", "gn_silu", "conv_res")),
+    "block-like": SMALL["block-like"],
+}
+
+
+@pytest.mark.parametrize("name", list(FUSE_CASES))
+def test_fused_groupnorm_conv_step_equals_unfused(name):
+    """A state-refreshing step with each GroupNorm -> conv pair as one dp_groupnorm_conv3x3_halo
+    call gives bit for bit the outputs, stale maps and statistics tables of the step that runs
+    the GroupNorm and the conv as two calls."""
+    c = FUSE_CASES[name]
+    inp = synth.layer_inputs(c, 4)
+    i, h = c.patch, c.h
+    xb = inp.x[:, i * h:(i + 1) * h]
+    got = {}
+    for fuse in (True, False):
+        layer = DisplacedLayer(c, inp.convs, projs=inp.projs, fuse=fuse)
+        announce("layer fused" if fuse else "layer unfused", c.name, "patch", i)
+        layer.warmup(gpu(inp.x_prev, c.dtype))
+        names = [n for n, _, _ in layer.calls(gpu(xb, c.dtype), i)]
+        assert any("+" in n for n in names) == fuse, names
+        outs = layer.step(gpu(xb, c.dtype), i, update_state=True)
+        torch.cuda.synchronize()
+        got[fuse] = ([o.clone() for o in outs], {k: m.clone() for k, m in layer.maps.items()},
+                     {k: t.clone() for k, t in layer.tables.items()})
+        del layer
+    (of, mf, tf), (ou, mu, tu) = got[True], got[False]
+    assert len(of) == len(ou) == len(c.graph)
+    bitsof = lambda t: t.view(torch.int16) if t.element_size() == 2 else t.view(torch.int32)  # noqa: E731
+    for k, (a, b) in enumerate(zip(of, ou)):
+        assert torch.equal(bitsof(a), bitsof(b)), f"{name} step {k} ({c.graph[k]})"
+    for k in mu:
+        assert torch.equal(bitsof(mf[k]), bitsof(mu[k])), f"{name} stale map {k}"
+    for k in tu:
+        assert torch.equal(tf[k], tu[k]), f"{name} statistics table {k}"
+
+
+def test_fused_resnet_block_state_matches_oracle():
+    """The 256x160-tile ResNet block's state-refreshing step (both GroupNorm sites folded into
+    their convs) against the oracle: outputs, refreshed stale maps and statistics tables."""
+    c = FUSE_CASES["resnet-tile8"]
+    inp = synth.layer_inputs(c, 5)
+    params = {"G": c.G, "eps": c.eps, "heads": c.heads, "convs": inp.convs, "projs": inp.projs}
+    layer = DisplacedLayer(c, inp.convs, projs=inp.projs)
+    announce("layer fused resnet vs oracle", c.name)
+    layer.warmup(gpu(inp.x_prev, c.dtype))
+    _, state = oracle.sync_layer(c.graph, params, inp.x_prev, c.P, state_only=True)
+    i, h = 1, c.h
+    xb = inp.x[:, i * h:(i + 1) * h]
+    outs = layer.step(gpu(xb, c.dtype), i, update_state=True)
+    torch.cuda.synchronize()
+    ref, new_state = oracle.displaced_layer(c.graph, params, xb, state, c.P, i)
+    for k, (g, r) in enumerate(zip(outs, ref)):
+        assert_parity(host(g), r, c.dtype, f"{c.name} patch {i} step {k} ({c.graph[k]})")
+    for k, tab in layer.tables.items():
+        assert_table(host(tab), new_state["stats"][k], c.dtype, k, f"statistics table {k}")
+    for k, m in layer.maps.items():
+        assert_parity(host(m), new_state["maps"][k], c.dtype, f"state map {k}")
