@@ -108,25 +108,29 @@ __device__ __forceinline__ void ring_barrier() { asm volatile("s_waitcnt lgkmcnt
 
 // LDS accesses of the fused normalisation, written as asm: the compiler's wait insertion takes any
 // LDS access for one that may touch the ring buffers the direct-to-LDS loads are still filling, and
-// waits for every load in flight before it.  Each thread only touches slots its own loads filled
-// (waited for explicitly) and the parameter table; the reads wait for their data in the same block.
+// waits for every load in flight before it.  Each thread only touches the slots its own loads
+// filled (waited for explicitly) and the parameter table.  One block per stage reads the thread's
+// 8 channels of scale and shift (t, t + 16 bytes; shift at u) and its three A slots (a, a + 8 KB,
+// a + 16 KB) and waits for them; the writes carry no memory clobber, so the compiler may move the
+// MFMAs' own LDS reads around them (they touch another ring buffer).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const lds_void*)p; }
-__device__ __forceinline__ u32x4 lds_read16(uint32_t a) {
-    u32x4 v;
-    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a) : "memory");
-    return v;
-}
-__device__ __forceinline__ void lds_read32x2(uint32_t a, uint32_t b, u32x4& a0, u32x4& a1, u32x4& b0, u32x4& b1) {
+__device__ __forceinline__ void lds_read_xform(uint32_t t, uint32_t u, uint32_t a, u32x4& s0, u32x4& s1, u32x4& f0,
+                                               u32x4& f1, u32x4& r0, u32x4& r1, u32x4& r2) {
     asm volatile(
-        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:16\n\t"
-        "ds_read_b128 %2, %5\n\tds_read_b128 %3, %5 offset:16\n\ts_waitcnt lgkmcnt(0)"
-        : "=&v"(a0), "=&v"(a1), "=&v"(b0), "=&v"(b1)
-        : "v"(a), "v"(b)
-        : "memory");
+        "ds_read_b128 %0, %7\n\tds_read_b128 %1, %7 offset:16\n\t"
+        "ds_read_b128 %2, %8\n\tds_read_b128 %3, %8 offset:16\n\t"
+        "ds_read_b128 %4, %9\n\tds_read_b128 %5, %9 offset:8192\n\tds_read_b128 %6, %9 offset:16384\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(s0), "=&v"(s1), "=&v"(f0), "=&v"(f1), "=&v"(r0), "=&v"(r1), "=&v"(r2)
+        : "v"(t), "v"(u), "v"(a));
 }
-__device__ __forceinline__ void lds_write16(uint32_t a, u32x4 v) {
-    asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(v) : "memory");
+template <int Q>
+__device__ __forceinline__ void lds_write_slot(uint32_t a, u32x4 v) {
+    static_assert(Q >= 0 && Q < 3, "three A slots per thread");
+    if constexpr (Q == 0) asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(v));
+    else if constexpr (Q == 1) asm volatile("ds_write_b128 %0, %1 offset:8192" ::"v"(a), "v"(v));
+    else asm volatile("ds_write_b128 %0, %1 offset:16384" ::"v"(a), "v"(v));
 }
 
 __device__ __forceinline__ int slot_swz(int p) { return (p >> 1) & 3; }
@@ -326,7 +330,7 @@ __device__ __forceinline__ void conv_tile_body(const ConvArgs& a, char* smem) {
     uint16_t* ysp[AQ];
     const int cthr = (lane & 3) ^ ((lane >> 3) & 3);
     if constexpr (FUSE) {
-        static_assert(AQ <= 3, "one A load per tap: the normalisation is interleaved tap by tap");
+        static_assert(AQ == 3 && NW == 8, "three A loads 8 KB apart per thread: one normalised per tap");
 #pragma unroll
         for (int q = 0; q < AQ; ++q) {
             const int j = wave + NW * q;
@@ -439,14 +443,15 @@ __device__ __forceinline__ void conv_tile_body(const ConvArgs& a, char* smem) {
                            tsf[c]);
         __syncthreads();
     }
-    // the fresh pixels of this thread's slot of load Q in stage K (ring buffer BUF), normalised in
-    // place; those of the tile's own rows and columns (kernel row 1) also go to the stale map
-#define DPH_XFORM_TABLE(K)                                                                          \
+    // Stage K's table entries and this thread's three A slots (ring buffer BUF), in registers
+#define DPH_XFORM_LOAD(K, BUF)                                                                      \
     do {                                                                                            \
         const float* gt_ = (const float*)(smem + STAGES * S::BYTES + gn_fuse_table_offset(a.gn_lanes, a.gn_G)); \
         const int ch_ = ((K) / 3) * 32 + cthr * 8;                                                  \
+        xsa_ = lds_addr(smem + (BUF) * S::BYTES + wave * 1024 + lane * 16);                          \
         u32x4 s0_, s1_, f0_, f1_;                                                                   \
-        lds_read32x2(lds_addr(gt_ + ch_), lds_addr(gt_ + a.Cin + ch_), s0_, s1_, f0_, f1_);         \
+        lds_read_xform(lds_addr(gt_ + ch_), lds_addr(gt_ + a.Cin + ch_), xsa_, s0_, s1_, f0_, f1_, xr_[0], xr_[1], \
+                       xr_[2]);                                                                     \
         _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                             \
             xsc_[e] = __uint_as_float(s0_[e]);                                                      \
             xsc_[e + 4] = __uint_as_float(s1_[e]);                                                  \
@@ -454,25 +459,27 @@ __device__ __forceinline__ void conv_tile_body(const ConvArgs& a, char* smem) {
             xsf_[e + 4] = __uint_as_float(f1_[e]);                                                  \
         }                                                                                           \
     } while (0)
-#define DPH_XFORM_Q(K, BUF, Q)                                                                      \
+    // the fresh pixels of this thread's slot of load Q in stage K, normalised in place; those of the
+    // tile's own rows and columns (kernel row 1) also go to the stale map
+#define DPH_XFORM_Q(K, Q)                                                                           \
     do {                                                                                            \
         const int ky_ = (K) % 3;                                                                    \
         if ((fmask[Q] >> ky_) & 1u) {                                                               \
-            const uint32_t sl_ = lds_addr(smem + (BUF) * S::BYTES + (wave + NW * (Q)) * 1024 + lane * 16); \
-            const u32x4 r_ = lds_read16(sl_);                                                       \
             float f_[8];                                                                            \
-            unpack8(make_uint4(r_[0], r_[1], r_[2], r_[3]), f_);                                    \
+            unpack8(make_uint4(xr_[Q][0], xr_[Q][1], xr_[Q][2], xr_[Q][3]), f_);                    \
             _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                         \
                 float z_ = fmaf(f_[e], xsc_[e], xsf_[e]);                                           \
                 if (a.gn_silu) z_ = silu(z_);                                                       \
                 f_[e] = z_;                                                                         \
             }                                                                                       \
             const uint4 v_ = pack8(f_);                                                             \
-            lds_write16(sl_, u32x4{v_.x, v_.y, v_.z, v_.w});                                        \
+            lds_write_slot<Q>(xsa_, u32x4{v_.x, v_.y, v_.z, v_.w});                                 \
             if (ky_ == 1 && ysp[Q]) *(uint4*)(ysp[Q] + ((K) / 3) * 32) = v_;                        \
         }                                                                                           \
     } while (0)
     float xsc_[8], xsf_[8];      // scale and shift of this thread's 8 channels of one stage
+    u32x4 xr_[3];                // this thread's three A slots of that stage
+    uint32_t xsa_ = 0;           // LDS address of its first slot
     if constexpr (FUSE) {
         if (nk > 0) {
             // this wave's loads of stage 0 have landed (stage 1's may still be in flight)
@@ -484,9 +491,10 @@ __device__ __forceinline__ void conv_tile_body(const ConvArgs& a, char* smem) {
             } else {
                 wait_vmcnt<0>();
             }
-            DPH_XFORM_TABLE(0);
-#pragma unroll
-            for (int q = 0; q < AQ; ++q) DPH_XFORM_Q(0, 0, q);
+            DPH_XFORM_LOAD(0, 0);
+            DPH_XFORM_Q(0, 0);
+            DPH_XFORM_Q(0, 1);
+            DPH_XFORM_Q(0, 2);
         }
         for (int it = 0; it < nk; ++it) {
             ring_barrier();      // stage it normalised by every thread; everyone is done with stage it-1
@@ -501,7 +509,7 @@ __device__ __forceinline__ void conv_tile_body(const ConvArgs& a, char* smem) {
                 } else {
                     wait_vmcnt<0>();
                 }
-                DPH_XFORM_TABLE(it + 1);
+                DPH_XFORM_LOAD(it + 1, (it + 1) % 3);
             }
             // stage it's 60 MFMAs, tap by tap, with stage it+1's normalisation between the taps
             const char* st = smem + (it % 3) * S::BYTES;
@@ -512,7 +520,11 @@ __device__ __forceinline__ void conv_tile_body(const ConvArgs& a, char* smem) {
                 for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8*)(st + aoff[i >> 1][kx] + (i & 1) * 1024);
 #pragma unroll
                 for (int n = 0; n < 5; ++n) bfr[n] = *(const bf16x8*)(st + boff + (kx * BN + n * 16) * 64);
-                if (nxt && kx < AQ) DPH_XFORM_Q(it + 1, (it + 1) % 3, kx);
+                if (nxt) {
+                    if (kx == 0) DPH_XFORM_Q(it + 1, 0);
+                    else if (kx == 1) DPH_XFORM_Q(it + 1, 1);
+                    else DPH_XFORM_Q(it + 1, 2);
+                }
 #pragma unroll
                 for (int n = 0; n < 5; ++n)
 #pragma unroll
@@ -540,7 +552,7 @@ __device__ __forceinline__ void conv_tile_body(const ConvArgs& a, char* smem) {
     }
 #undef DPH_ISSUE
 #undef DPH_ISSUE_KY
-#undef DPH_XFORM_TABLE
+#undef DPH_XFORM_LOAD
 #undef DPH_XFORM_Q
     __syncthreads();   // ring no longer read: reuse it for the output tile
 
