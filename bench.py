@@ -40,12 +40,11 @@ PEAK_HBM_GBS = 8000.0
 # source file of each call's main kernel (for the counter file's staleness check)
 KERNEL_SOURCES = {"conv": "k_conv.hip", "conv_res": "k_conv.hip", "attn": "k_attention.hip",
                   "gn": "k_groupnorm.hip", "gn_silu": "k_groupnorm.hip", "stale_update": "k_splice.hip",
-                  "proj_q": "k_linear.hip", "proj_k": "k_linear.hip", "proj_v": "k_linear.hip",
-                  "proj_o": "k_linear.hip"}
+                  "proj_qkv": "k_linear.hip", "proj_o": "k_linear.hip"}
 for _g in ("gn", "gn_silu"):
     for _c in ("conv", "conv_res"):
         KERNEL_SOURCES[f"{_g}+{_c}"] = "k_conv.hip"     # GroupNorm folded into the conv
-PROJ_CALLS = ("proj_q", "proj_k", "proj_v", "proj_o")
+PROJ_CALLS = ("proj_qkv", "proj_o")
 
 
 def step_flops(cfg):
@@ -59,8 +58,8 @@ def call_flops(cfg, name):
         return cfg.conv_flops() / max(cfg.n_conv, 1)
     if name == "attn":
         return cfg.attn_flops() / max(cfg.n_attn, 1)
-    if name in PROJ_CALLS:
-        return cfg.proj_flops() / max(4 * cfg.n_proj, 1)
+    if name in PROJ_CALLS:          # the Q/K/V launch is three of the step's four projections
+        return cfg.proj_flops() / max(4 * cfg.n_proj, 1) * (3 if name == "proj_qkv" else 1)
     return 0
 
 

@@ -80,6 +80,8 @@ def lib():
             "dp_conv3x3_halo_residual": [pp, i32, i32, vp, vp, vp, i32, vp, vp, vp, vp, sz, vp],
             "dp_linear_residual": [i32, i32, i32, i32, vp, ctypes.c_int64, vp, vp, vp, ctypes.c_int64, vp,
                                    ctypes.c_int64, vp],
+            "dp_linear_qkv": [i32, i32, i32, i32, vp, ctypes.c_int64, vp, vp, vp, ctypes.c_int64, vp,
+                              ctypes.c_int64, vp, ctypes.c_int64, vp],
             "dp_groupnorm_conv3x3_halo_ws": [pp, i32, i32, i32, psz],
             "dp_groupnorm_conv3x3_halo": [pp, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, i32, vp,
                                           vp, vp, vp, sz, vp],
@@ -421,6 +423,55 @@ def dp_linear_residual(x, w, bias=None, r=None, y=None):
     return _linear(x, w, bias, r, y)
 
 
+def _rows(t, name, width):
+    """(rows, row stride) of a tensor read as rows of `width` contiguous elements: any leading
+    shape whose rows form one strided sequence (a token-major map [B][tokens][C] included)."""
+    if t.dim() < 1 or t.shape[-1] != width or (t.numel() and t.stride(-1) != 1):
+        raise ValueError(f"{name} must end in a contiguous axis of {width}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    m = 1
+    for d in t.shape[:-1]:
+        m *= int(d)
+    flat = t.reshape(m, width) if m else t
+    if m and flat.data_ptr() != t.data_ptr():
+        raise ValueError(f"{name} rows are not one strided sequence")
+    ld = flat.stride(0) if m > 1 else width
+    return m, ld
+
+
+def dp_linear_qkv(x, w3, bias3=None, yq=None, yk=None, yv=None):
+    """(x W_q^T + b_q, x W_k^T + b_k, x W_v^T + b_v) in one launch: w3 = [W_q; W_k; W_v] [3N][K],
+    bias3 [3N] float32.  x and the outputs are read as rows like dp_linear's (e.g. token-major
+    maps); missing outputs are allocated with x's leading shape."""
+    torch = _torch()
+    dt = _dtype_code(x)
+    dev = x.device
+    if w3.dim() != 2 or w3.shape[0] % 3:
+        raise ValueError("w3 must be [3N][K]")
+    N, K = int(w3.shape[0]) // 3, int(w3.shape[1])
+    if x.shape[-1] != K:
+        raise ValueError(f"x has {x.shape[-1]} columns, w3 expects {K}")
+    _ptr(w3, "w3", (3 * N, K), x.dtype, dev)
+    _ptr(bias3, "bias3", (3 * N,), torch.float32, dev)
+    M, ldx = _rows(x, "x", K)
+    outs, lds = [], []
+    for name, y in (("yq", yq), ("yk", yk), ("yv", yv)):
+        if y is None:
+            y = torch.empty(tuple(x.shape[:-1]) + (N,), dtype=x.dtype, device=dev)
+        if y.dtype != x.dtype or y.device != dev:
+            raise TypeError(f"{name} must have x's dtype and device")
+        My, ld = _rows(y, name, N)
+        if My != M:
+            raise ValueError(f"{name} has {My} rows, x has {M}")
+        outs.append(y)
+        lds.append(ld)
+    bp = None if bias3 is None else bias3.data_ptr()
+    _check(lib().dp_linear_qkv(dt, M, N, K, x.data_ptr(), ldx, w3.data_ptr(), bp, outs[0].data_ptr(), lds[0],
+                               outs[1].data_ptr(), lds[1], outs[2].data_ptr(), lds[2], _stream(dev)))
+    return tuple(outs)
+
+
 def _linear(x, w, bias, r, y):
     torch = _torch()
     dt = _dtype_code(x)
@@ -433,22 +484,8 @@ def _linear(x, w, bias, r, y):
     if y is None:
         y = torch.empty(tuple(x.shape[:-1]) + (N,), dtype=x.dtype, device=dev)
 
-    def rows(t, name, width):
-        if t.dim() < 1 or t.shape[-1] != width or (t.numel() and t.stride(-1) != 1):
-            raise ValueError(f"{name} must end in a contiguous axis of {width}")
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
-        m = 1
-        for d in t.shape[:-1]:
-            m *= int(d)
-        flat = t.reshape(m, width) if m else t
-        if m and flat.data_ptr() != t.data_ptr():
-            raise ValueError(f"{name} rows are not one strided sequence")
-        ld = flat.stride(0) if m > 1 else width
-        return m, ld
-
-    M, ldx = rows(x, "x", K)
-    My, ldy = rows(y, "y", N)
+    M, ldx = _rows(x, "x", K)
+    My, ldy = _rows(y, "y", N)
     if My != M:
         raise ValueError(f"y has {My} rows, x has {M}")
     bp = None if bias is None else bias.data_ptr()
@@ -457,7 +494,7 @@ def _linear(x, w, bias, r, y):
         return y
     if r.dtype != x.dtype or r.device != dev:
         raise TypeError("r must have x's dtype and device")
-    Mr, ldr = rows(r, "r", N)
+    Mr, ldr = _rows(r, "r", N)
     if Mr != M:
         raise ValueError(f"r has {Mr} rows, x has {M}")
     _check(lib().dp_linear_residual(dt, M, N, K, x.data_ptr(), ldx, w.data_ptr(), bp, r.data_ptr(), ldr,

@@ -582,4 +582,47 @@ dp_status dp_linear_residual(dp_dtype dtype, int32_t M, int32_t N, int32_t K, co
     return linear_call(dtype, M, N, K, x, ldx, w, bias, r, ldr, y, ldy, stream, "dp_linear_residual launch");
 }
 
+dp_status dp_linear_qkv(dp_dtype dtype, int32_t M, int32_t N, int32_t K, const void* x, int64_t ldx, const void* w3,
+                        const float* bias3, void* yq, int64_t ldq, void* yk, int64_t ldk, void* yv, int64_t ldv,
+                        hipStream_t stream) {
+    if (dtype != DP_F32 && dtype != DP_BF16) return fail(DP_ERR_ARG, "unknown dtype %d", (int)dtype);
+    if (M < 0 || N < 1 || K < 1) return fail(DP_ERR_ARG, "need M >= 0, N >= 1, K >= 1 (got %d, %d, %d)", M, N, K);
+    if ((int64_t)3 * N > 0x7fffffffLL) return fail(DP_ERR_ARG, "3N exceeds the 32-bit range");
+    void* const y[3] = {yq, yk, yv};
+    const int64_t ld[3] = {ldq, ldk, ldv};
+    const char* nm[3] = {"yq", "yk", "yv"};
+    if (ldx < K) return fail(DP_ERR_ARG, "row stride ldx=%lld does not cover K=%d", (long long)ldx, K);
+    for (int s = 0; s < 3; ++s)
+        if (ld[s] < N) return fail(DP_ERR_ARG, "row stride of %s (%lld) does not cover N=%d", nm[s], (long long)ld[s], N);
+    if ((int64_t)M * ldx > ((int64_t)1 << 40) || (int64_t)M * ldq > ((int64_t)1 << 40) ||
+        (int64_t)M * ldk > ((int64_t)1 << 40) || (int64_t)M * ldv > ((int64_t)1 << 40))
+        return fail(DP_ERR_ARG, "matrix too large");
+    if (dtype == DP_BF16 && (K % 64 != 0 || N % 8 != 0 || ldx % 8 != 0 || ldq % 8 != 0 || ldk % 8 != 0 ||
+                             ldv % 8 != 0))
+        return fail(DP_ERR_UNSUPPORTED, "bf16 linear needs K %% 64 == 0 and N, ldx and the output row strides "
+                    "multiples of 8 (K=%d N=%d)", K, N);
+    if (M == 0) return ok();
+    DP_NEED(x, "x");
+    DP_NEED(w3, "w3");
+    DP_OPT(bias3, "bias3");
+    for (int s = 0; s < 3; ++s) {
+        if (!y[s]) return fail(DP_ERR_ARG, "%s is NULL", nm[s]);
+        if (!aligned16(y[s])) return fail(DP_ERR_ARG, "%s is not 16-byte aligned", nm[s]);
+    }
+    const size_t es = elem_size(dtype);
+    const size_t xb = ((size_t)(M - 1) * ldx + K) * es;
+    const size_t wb = (size_t)3 * N * K * es;
+    const size_t bb = bias3 ? (size_t)3 * N * sizeof(float) : 0;
+    size_t yb[3];
+    for (int s = 0; s < 3; ++s) yb[s] = ((size_t)(M - 1) * ld[s] + N) * es;
+    for (int s = 0; s < 3; ++s) {
+        if (overlaps(y[s], yb[s], x, xb) || overlaps(y[s], yb[s], w3, wb) || overlaps(y[s], yb[s], bias3, bb))
+            return fail(DP_ERR_ARG, "%s overlaps an input", nm[s]);
+        for (int t = s + 1; t < 3; ++t)
+            if (overlaps(y[s], yb[s], y[t], yb[t])) return fail(DP_ERR_ARG, "%s overlaps %s", nm[s], nm[t]);
+    }
+    return hip_status(dp::launch_linear_qkv(dtype == DP_BF16, M, N, K, x, ldx, w3, bias3, y, ld, stream),
+                      "dp_linear_qkv launch");
+}
+
 }  // extern "C"

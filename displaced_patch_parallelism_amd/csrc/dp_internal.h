@@ -109,5 +109,9 @@ hipError_t launch_attention(const Geom& g, const AttnPlan& plan, bool bf16, int 
 hipError_t launch_linear(bool bf16, int M, int N, int K, const void* x, int64_t ldx, const void* w,
                          const float* bias, const void* r, int64_t ldr, void* y, int64_t ldy,
                          hipStream_t stream);
+// Q, K and V projections in one product: w3 [3N][K] (W_q, W_k, W_v stacked), bias3 [3N] or null;
+// output segment s (columns s*N ..) goes to y[s] with row stride ldy[s].
+hipError_t launch_linear_qkv(bool bf16, int M, int N, int K, const void* x, int64_t ldx, const void* w3,
+                             const float* bias3, void* const y[3], const int64_t ldy[3], hipStream_t stream);
 
 }  // namespace dp

@@ -43,6 +43,12 @@ struct LinArgs {
     int64_t ldx, ldy, ldr;
     int M, N, K;
     int mtiles, ntiles;
+    // segmented output (segw > 0): columns [s*segw, (s+1)*segw) of the product go to segment s
+    // (y, y1, y2 with their row strides), column n - s*segw
+    uint16_t* y1;
+    uint16_t* y2;
+    int64_t ldy1, ldy2;
+    int segw;
 };
 
 template <int BM, int BN>
@@ -166,7 +172,21 @@ __global__ __launch_bounds__(256) void linear_bf16_kernel(LinArgs a) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) f[e] += rv[e];
             }
-            *(uint4*)(a.y + (int64_t)m * a.ldy + n) = pack8(f);
+            uint16_t* yp = a.y;
+            int64_t ld = a.ldy;
+            int col = n;
+            if (a.segw) {            // segments are multiples of 8 columns: a chunk lies in one
+                const int sg = n / a.segw;
+                col = n - sg * a.segw;
+                if (sg == 1) {
+                    yp = a.y1;
+                    ld = a.ldy1;
+                } else if (sg == 2) {
+                    yp = a.y2;
+                    ld = a.ldy2;
+                }
+            }
+            *(uint4*)(yp + (int64_t)m * ld + col) = pack8(f);
         }
     }
 }
@@ -189,6 +209,27 @@ __global__ __launch_bounds__(256) void linear_f32_kernel(const float* __restrict
 
 }  // namespace
 
+namespace {
+
+hipError_t launch_linear_bf16(LinArgs a, hipStream_t stream) {
+    // 128x128 tiles when there are enough of them to fill the CUs, else 64x64
+    const int64_t big = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
+    if (big >= 256) {
+        a.mtiles = (a.M + 127) / 128;
+        a.ntiles = (a.N + 127) / 128;
+        if (!grid_fits((int64_t)a.mtiles * a.ntiles)) return hipErrorInvalidConfiguration;
+        linear_bf16_kernel<128, 128><<<(unsigned)(a.mtiles * a.ntiles), 256, 0, stream>>>(a);
+    } else {
+        a.mtiles = (a.M + 63) / 64;
+        a.ntiles = (a.N + 63) / 64;
+        if (!grid_fits((int64_t)a.mtiles * a.ntiles)) return hipErrorInvalidConfiguration;
+        linear_bf16_kernel<64, 64><<<(unsigned)(a.mtiles * a.ntiles), 256, 0, stream>>>(a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_linear(bool bf16, int M, int N, int K, const void* x, int64_t ldx, const void* w,
                          const float* bias, const void* r, int64_t ldr, void* y, int64_t ldy,
                          hipStream_t stream) {
@@ -200,7 +241,7 @@ hipError_t launch_linear(bool bf16, int M, int N, int K, const void* x, int64_t 
             (const float*)x, ldx, (const float*)w, bias, (const float*)r, ldr, (float*)y, ldy, M, N, K);
         return hipGetLastError();
     }
-    LinArgs a;
+    LinArgs a{};
     a.x = (const uint16_t*)x;
     a.w = (const uint16_t*)w;
     a.bias = bias;
@@ -212,20 +253,39 @@ hipError_t launch_linear(bool bf16, int M, int N, int K, const void* x, int64_t 
     a.M = M;
     a.N = N;
     a.K = K;
-    // 128x128 tiles when there are enough of them to fill the CUs, else 64x64
-    const int64_t big = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
-    if (big >= 256) {
-        a.mtiles = (M + 127) / 128;
-        a.ntiles = (N + 127) / 128;
-        if (!grid_fits((int64_t)a.mtiles * a.ntiles)) return hipErrorInvalidConfiguration;
-        linear_bf16_kernel<128, 128><<<(unsigned)(a.mtiles * a.ntiles), 256, 0, stream>>>(a);
-    } else {
-        a.mtiles = (M + 63) / 64;
-        a.ntiles = (N + 63) / 64;
-        if (!grid_fits((int64_t)a.mtiles * a.ntiles)) return hipErrorInvalidConfiguration;
-        linear_bf16_kernel<64, 64><<<(unsigned)(a.mtiles * a.ntiles), 256, 0, stream>>>(a);
+    return launch_linear_bf16(a, stream);
+}
+
+hipError_t launch_linear_qkv(bool bf16, int M, int N, int K, const void* x, int64_t ldx, const void* w3,
+                             const float* bias3, void* const y[3], const int64_t ldy[3], hipStream_t stream) {
+    if (M == 0) return hipSuccess;
+    if (!bf16) {     // the fp32 path: three launches of the same kernel
+        for (int sg = 0; sg < 3; ++sg) {
+            const hipError_t e = launch_linear(false, M, N, K, x, ldx, (const float*)w3 + (size_t)sg * N * K,
+                                               bias3 ? bias3 + (size_t)sg * N : nullptr, nullptr, 0, y[sg],
+                                               ldy[sg], stream);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
     }
-    return hipGetLastError();
+    // one product [M][3N] whose column segments go to the three outputs: each output element is
+    // the same K-ordered MFMA sum as in a separate launch
+    LinArgs a{};
+    a.x = (const uint16_t*)x;
+    a.w = (const uint16_t*)w3;
+    a.bias = bias3;
+    a.y = (uint16_t*)y[0];
+    a.y1 = (uint16_t*)y[1];
+    a.y2 = (uint16_t*)y[2];
+    a.ldx = ldx;
+    a.ldy = ldy[0];
+    a.ldy1 = ldy[1];
+    a.ldy2 = ldy[2];
+    a.M = M;
+    a.N = 3 * N;
+    a.K = K;
+    a.segw = N;
+    return launch_linear_bf16(a, stream);
 }
 
 }  // namespace dp

@@ -29,7 +29,7 @@ import torch
 
 from . import (Patch, _dtype_code, dp_attention_splice, dp_conv3x3_halo, dp_conv3x3_halo_packed,
                dp_conv3x3_halo_residual, dp_conv3x3_pack_weights, dp_groupnorm_async, dp_groupnorm_conv3x3_halo,
-               dp_linear, dp_linear_residual, dp_stale_update, dp_stats_update, workspace_bytes)
+               dp_linear, dp_linear_qkv, dp_linear_residual, dp_stale_update, dp_stats_update, workspace_bytes)
 
 GN_STEPS = ("gn", "gn_silu")
 CONV_STEPS = ("conv", "conv_res")
@@ -71,6 +71,10 @@ class DisplacedLayer:
         # per attn_proj step: (wq, bq, wk, bk, wv, bv, wo, bo), weights in the storage type
         self.projs = [tuple(torch.as_tensor(a).to(self.device, self.dt if j % 2 == 0 else torch.float32).contiguous()
                             for j, a in enumerate(pr)) for pr in (projs or [])]
+        # and W_q, W_k, W_v stacked [3C][C] with their biases [3C]: the three input projections
+        # run as one dp_linear_qkv launch
+        self.qkv = [(torch.cat([pr[0], pr[2], pr[4]]).contiguous(), torch.cat([pr[1], pr[3], pr[5]]).contiguous())
+                    for pr in self.projs]
         c = cfg
         # one statistics table and one fresh-moments buffer per GroupNorm step
         self.tables: Dict = {k: torch.zeros((c.P, c.B, c.G, 2), dtype=torch.float32, device=self.device)
@@ -199,7 +203,7 @@ class DisplacedLayer:
                 fn = (lambda tok=tok, st=st, o=o: dp_attention_splice(
                     p, c.heads, tok, tok, tok, st, st, o_patch=o, ws=self.ws))
             else:   # attn_proj
-                wq, bq, wk, bk, wv, bv, wo, bo = self.projs[proj_i]
+                wo, bo = self.projs[proj_i][6:]
                 proj_i += 1
                 pb = self.pbufs[k]
                 kcache, vcache = self.maps[(k, "k")], self.maps[(k, "v")]
@@ -209,9 +213,9 @@ class DisplacedLayer:
                 else:
                     kb, vb = self._tok(pb["k"]), self._tok(pb["v"])
                 tok, q, a = self._tok(h), self._tok(pb["q"]), self._tok(pb["a"])
-                out_list.append(("proj_q", lambda tok=tok, q=q, w=wq, b=bq: dp_linear(tok, w, b, y=q), ()))
-                out_list.append(("proj_k", lambda tok=tok, y=kb, w=wk, b=bk: dp_linear(tok, w, b, y=y), ()))
-                out_list.append(("proj_v", lambda tok=tok, y=vb, w=wv, b=bv: dp_linear(tok, w, b, y=y), ()))
+                w3, b3 = self.qkv[proj_i - 1]
+                out_list.append(("proj_qkv", lambda tok=tok, q=q, kb=kb, vb=vb, w3=w3, b3=b3:
+                                 dp_linear_qkv(tok, w3, b3, yq=q, yk=kb, yv=vb), ()))
                 out_list.append(("attn", lambda q=q, kb=kb, vb=vb, a=a, ks=self._tok(kcache), vs=self._tok(vcache):
                                  dp_attention_splice(p, c.heads, q, kb, vb, ks, vs, o_patch=a, ws=self.ws), ()))
                 if s == "attn_proj_res":
@@ -346,13 +350,13 @@ class DisplacedLayer:
                                               fresh_stats_out=fresh)
                     dp_stale_update(self.patch(j), y, out_full)
             elif s in PROJ_STEPS:
-                wq, bq, wk, bk, wv, bv, wo, bo = self.projs[proj_i]
+                wo, bo = self.projs[proj_i][6:]
                 proj_i += 1
                 tok = self._tok(h_full)
                 kc, vc = self.maps[(k, "k")], self.maps[(k, "v")]
-                dp_linear(tok, wk, bk, y=self._tok(kc))
-                dp_linear(tok, wv, bv, y=self._tok(vc))
-                q_full = dp_linear(tok, wq, bq).reshape(h_full.shape)
+                w3, b3 = self.qkv[proj_i - 1]
+                q_full = torch.empty_like(h_full)
+                dp_linear_qkv(tok, w3, b3, yq=self._tok(q_full), yk=self._tok(kc), yv=self._tok(vc))
                 a_full = torch.empty_like(h_full)
                 for j in range(c.P):
                     pj = self.patch(j)

@@ -26,6 +26,7 @@
  *   dp_groupnorm_conv3x3_halo
  *                        GroupNorm (+SiLU) and the conv that consumes it in
  *                        one call, the normalisation folded into the conv
+ *   dp_linear_qkv        the Q, K and V projections in one launch
  *
  * Geometry.  Maps are NHWC, batch-major: element (b, r, c, ch) of a [B][H][W][C]
  * map sits at ((b*H + r)*W + c)*C + ch.  The P patches are equal row bands:
@@ -379,6 +380,29 @@ dp_status dp_linear(dp_dtype dtype, int32_t M, int32_t N, int32_t K, const void*
 dp_status dp_linear_residual(dp_dtype dtype, int32_t M, int32_t N, int32_t K, const void* x, int64_t ldx,
                              const void* w, const float* bias, const void* r, int64_t ldr, void* y, int64_t ldy,
                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * dp_linear_qkv -- the three input projections of an attention layer in one
+ * launch:  y_s = x W_s^T + bias_s  for s = Q, K, V, with W_s rows [s*N, (s+1)*N)
+ * of w3 and bias_s entries [s*N, (s+1)*N) of bias3.  Bitwise equal to three
+ * dp_linear calls; one product [M][3N] fills the GPU where three [M][N]
+ * products of a small band would each leave it part idle.
+ *
+ * Source: as dp_linear (PipeFusion explainer on gist.science, Problem
+ * Statement and Memory Efficiency: a patch projects its own tokens to Q, K
+ * and V and writes the fresh K and V into band i of the cached maps).
+ *
+ *   x           [M][K] dtype, row r at x + r*ldx
+ *   w3          [3N][K] dtype, contiguous (W_q, W_k, W_v stacked)
+ *   bias3       [3N] float or NULL (0)
+ *   yq, yk, yv  [M][N] dtype, row r at y + r*ld (ldq, ldk, ldv); none may
+ *               overlap x, w3, bias3 or another output
+ * Requirements and errors as dp_linear (bf16: every row stride a multiple of
+ * 8).  No workspace.
+ * ---------------------------------------------------------------------- */
+dp_status dp_linear_qkv(dp_dtype dtype, int32_t M, int32_t N, int32_t K, const void* x, int64_t ldx, const void* w3,
+                        const float* bias3, void* yq, int64_t ldq, void* yk, int64_t ldk, void* yv, int64_t ldv,
+                        hipStream_t stream);
 
 /* Description of the last error on the calling thread (empty if none). The
  * string stays valid until the thread's next dp_* call. */

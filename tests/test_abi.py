@@ -354,3 +354,29 @@ def test_groupnorm_conv_accepts_fresh_moments_in_slot_i():
     slot_i = 0x50000000 + 1 * 1 * 8 * 2 * 4
     assert call_gn_conv(p=p, fresh=slot_i, ws_bytes=0) == dp.DP_ERR_ARG
     assert "workspace too small" in dp.lib().dp_last_error().decode()
+
+
+def call_qkv(dtype=dp.DP_BF16, M=16, N=64, K=64, x=FAKE, ldx=64, w3=FAKE2, bias3=None, yq=0x30000000, ldq=64,
+             yk=0x31000000, ldk=64, yv=0x32000000, ldv=64):
+    return dp.lib().dp_linear_qkv(dtype, M, N, K, x, ldx, w3, bias3, yq, ldq, yk, ldk, yv, ldv, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    ({"yk": 0x30000000 + 64}, dp.DP_ERR_ARG, "yq overlaps yk"),
+    ({"yv": FAKE2 + 128}, dp.DP_ERR_ARG, "yv overlaps an input"),
+    ({"ldk": 32}, dp.DP_ERR_ARG, "row stride of yk"),
+    ({"ldx": 32}, dp.DP_ERR_ARG, "ldx"),
+    ({"K": 96, "ldx": 96}, dp.DP_ERR_UNSUPPORTED, "K % 64"),
+    ({"ldv": 68}, dp.DP_ERR_UNSUPPORTED, "multiples of 8"),
+    ({"yq": 0}, dp.DP_ERR_ARG, "yq is NULL"),
+    ({"yk": 0x31000000 + 8}, dp.DP_ERR_ARG, "aligned"),
+    ({"N": 0}, dp.DP_ERR_ARG, "N >= 1"),
+    ({"dtype": 9}, dp.DP_ERR_ARG, "dtype"),
+])
+def test_linear_qkv_rejects(kw, code, msg):
+    assert call_qkv(**kw) == code
+    assert msg in dp.lib().dp_last_error().decode()
+
+
+def test_linear_qkv_empty_is_noop():
+    assert call_qkv(M=0, x=0, yq=0, yk=0, yv=0) == dp.DP_OK

@@ -101,3 +101,50 @@ def test_residual_strided_rows():
     y = dp.dp_linear_residual(gpu(x, "bf16"), gpu(w, "bf16"), gpu(b, "f32"), big[:, 16:16 + N])
     torch.cuda.synchronize()
     assert_parity(host(y), oracle.linear(x, w, b) + r, "bf16", "linear residual strided")
+
+
+@pytest.mark.parametrize("M,N,K,dtype", [
+    (1024, 640, 640, "bf16"),    # c2p's Q/K/V: one [1024][1920] product on 64x64 tiles
+    (7200, 640, 640, "bf16"),    # c4bp's: 128x128 tiles
+    (100, 96, 128, "bf16"),      # ragged rows; 64-column tiles straddle the segment edges
+    (1, 8, 64, "bf16"),
+    (33, 40, 16, "f32"),
+])
+def test_qkv_equals_three_linears(M, N, K, dtype):
+    """dp_linear_qkv gives bit for bit the three dp_linear outputs (and the oracle's values)."""
+    announce("linear qkv", M, N, K, dtype)
+    rng = np.random.default_rng(M + 2 * N)
+    x = synth.to_storage(rng.standard_normal((M, K), dtype=np.float32), dtype)
+    ws = [synth.to_storage(rng.standard_normal((N, K), dtype=np.float32) / np.float32(np.sqrt(K)), dtype)
+          for _ in range(3)]
+    bs = [rng.standard_normal((N,), dtype=np.float32) for _ in range(3)]
+    xg = gpu(x, dtype)
+    w3 = gpu(np.concatenate(ws), dtype)
+    b3 = gpu(np.concatenate(bs), "f32")
+    outs = dp.dp_linear_qkv(xg, w3, b3)
+    refs = [dp.dp_linear(xg, gpu(w, dtype), gpu(b, "f32")) for w, b in zip(ws, bs)]
+    torch.cuda.synchronize()
+    for s, (o, r) in enumerate(zip(outs, refs)):
+        bits = (lambda t: t.view(torch.int16)) if dtype == "bf16" else (lambda t: t.view(torch.int32))
+        assert torch.equal(bits(o), bits(r)), f"segment {s}"
+        assert_parity(host(o), oracle.linear(x, ws[s], bs[s]), dtype, f"qkv segment {s}")
+
+
+def test_qkv_into_strided_bands_without_bias():
+    """Q into a scratch buffer, K and V straight into band rows of two token maps (row stride
+    wider than N), no bias; rows outside the bands are untouched."""
+    M, N, K = 96, 64, 128
+    rng = np.random.default_rng(21)
+    x = synth.to_storage(rng.standard_normal((M, K), dtype=np.float32), "bf16")
+    w3 = synth.to_storage(rng.standard_normal((3 * N, K), dtype=np.float32) / np.float32(np.sqrt(K)), "bf16")
+    kmap = torch.full((4 * M, N + 32), 5.0, dtype=torch.bfloat16, device="cuda")
+    vmap = torch.full((4 * M, N + 32), 6.0, dtype=torch.bfloat16, device="cuda")
+    q, k, v = dp.dp_linear_qkv(gpu(x, "bf16"), gpu(w3, "bf16"), None, yk=kmap[2 * M:3 * M, :N],
+                               yv=vmap[M:2 * M, 16:16 + N])
+    torch.cuda.synchronize()
+    for s, got in enumerate((q, k, v)):
+        assert_parity(host(got), oracle.linear(x, w3[s * N:(s + 1) * N]), "bf16", f"qkv strided {s}")
+    km, vm = host(kmap), host(vmap)
+    assert np.all(km[:2 * M] == 5.0) and np.all(km[3 * M:] == 5.0) and np.all(km[2 * M:3 * M, N:] == 5.0)
+    assert np.all(vm[:M] == 6.0) and np.all(vm[2 * M:] == 6.0) and np.all(vm[M:2 * M, :16] == 6.0)
+    assert np.all(vm[M:2 * M, 16 + N:] == 6.0)
