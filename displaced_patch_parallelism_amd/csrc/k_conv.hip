@@ -304,8 +304,10 @@ __device__ __forceinline__ void conv_tile_body(const ConvArgs& a, char* smem) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % (TR / 2), wn = wave / (TR / 2);
     const int lt = xcd_order(blockIdx.x, gridDim.x);
-    const int mt = lt % a.mtiles;
-    const int nt = lt / a.mtiles;
+    // channel tile fastest: the workgroups of one pixel tile run on one XCD, which then fetches
+    // the tile's source pixels once for all of them (its L2 holds every channel tile's weights)
+    const int nt = lt % a.ntiles;
+    const int mt = lt / a.ntiles;
     int bb, ty0, tx0;
     tile_origin<TR>(a, mt, bb, ty0, tx0);
     const int n0 = nt * BN;
