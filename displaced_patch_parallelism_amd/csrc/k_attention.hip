@@ -10,19 +10,22 @@
 //
 // bf16 path (d = 64): flash-style single pass with an online softmax in the
 // base-2 domain (log2(e) folded into the scale).  A workgroup holds 256
-// queries (8 waves x 32); K/V tiles of 64 tokens are staged in LDS, K
-// row-major and V transposed.  Each wave computes S^T = K Q^T with
-// v_mfma_f32_32x32x16_bf16 so that lane l owns query l%32: the running
-// offset and sum stay in the lane.  Q is pre-scaled and the S MFMAs start
-// from C = -offset, so S - offset comes out of the MFMA; the offset follows
-// the running maximum lazily (the cross-half exchange happens only when it
-// moves).
+// queries (8 waves x 32); K/V tiles of 64 tokens are staged in LDS, K and V
+// row-major.  Each wave computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 so
+// that lane l owns query l%32: the running offset and sum stay in the lane.
+// Q stays exact (bf16 as given); the scale is applied with the offset by one
+// fp32 FMA per score.  The offset follows the running maximum lazily: a
+// 32-key half is exponentiated with the current offset and its probability
+// sum checked; only a sum above 2^8 (or the first or a ragged tile) makes the
+// half take the slow path that finds its maximum and moves the offset.
 // P^T (bf16) feeds O^T = V^T P^T directly from registers; within each 16-key
 // MFMA step the key order is permuted identically on both operands so the
-// S^T accumulator layout needs no shuffle.  The token loader picks the fresh
-// or stale buffer per key row, so tiles may straddle the band edges.  When
-// (query tiles x heads) cannot fill the GPU, keys are split and the partial
-// (O, max, sum) are merged by a second kernel in split order.
+// S^T accumulator layout needs no shuffle.  The tile loop is software-
+// pipelined so that each wave's exponentials run between its own MFMAs.  The
+// token loader picks the fresh or stale buffer per key row, so tiles may
+// straddle the band edges.  When (query tiles x heads) cannot fill the GPU,
+// keys are split and the partial (O, max, sum) are merged by a second kernel
+// in split order.
 // f32 path: one thread per (query, head), online softmax, for small maps.
 
 #include "dp_device.h"
@@ -38,6 +41,7 @@ constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;
 constexpr float kLazy = 8.0f;     // offset moves when a score exceeds it by more than this (log2)
+constexpr float kLazyMax = 256.0f;  // 2^kLazy: a larger half-tile probability sum takes the slow path
 
 struct AttnArgs {
     const uint16_t* q;
@@ -91,9 +95,33 @@ __device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-// 4 bf16 of V^T for the PV operand via the transposing LDS read (see the lane map below).
-__device__ __forceinline__ s16x4 tr_read(const char* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+// LDS accesses of the tile loop.  The compiler makes an LDS read that it cannot tell apart from
+// the ring buffers being filled by direct-to-LDS loads wait for every such load in flight; the
+// loop waits for its own loads explicitly (vmcnt, then the barrier), so its reads are written so
+// that no such wait is added: the K fragments as plain loads from a 32-bit LDS address, the V^T
+// fragments as asm that waits for its own reads only.
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const lds_void*)p; }
+__device__ __forceinline__ bf16x8 lds_ld128(uint32_t addr) { return *(lds_bf16x8*)(uintptr_t)addr; }
+
+// Workgroup barrier that waits only for the wave's LDS accesses: __syncthreads() would also wait
+// for the direct-to-LDS loads still in flight into the other ring stages.
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// V^T operand fragments of 16-key group U, by ds_read_b64_tr_b16: within a 16-lane group lane c
+// receives element c%4 of the 8-byte reads of lanes c/4, c/4+4, c/4+8, c/4+12, so lane j reads
+// key (j/4) of a 4-key group at 4 consecutive dims and each lane ends up holding one dim for 4
+// keys.  Four reads (va, va + 1 KB: keys +0/+8 of dims 0..31; vb = va ^ 64: dims 32..63), waited
+// for in the same asm block.
+template <int U>
+__device__ __forceinline__ void lds_read_vt(uint32_t va, uint32_t vb, s16x4& r00, s16x4& r10, s16x4& r01,
+                                            s16x4& r11) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:%6\n\tds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
+        "ds_read_b64_tr_b16 %2, %5 offset:%6\n\tds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r00), "=&v"(r10), "=&v"(r01), "=&v"(r11)
+        : "v"(va), "v"(vb), "i"(U * 2048), "i"(U * 2048 + 1024));
 }
 
 // ---------------------------------------------------------------------------
@@ -101,11 +129,8 @@ __device__ __forceinline__ s16x4 tr_read(const char* p) {
 // global_load_lds_dwordx4 in a STAGES-deep LDS ring (16 KB per stage, rows of
 // 128 bytes, 16-byte chunk c of row r at slot c ^ (r & 7)); the loader picks
 // the fresh patch or the stale map per key row.  S^T = K Q^T per wave (lane
-// = query).  The PV operand V^T is read with ds_read_b64_tr_b16: within a
-// 16-lane group, lane c receives element c%4 of the 8-byte reads of lanes
-// c/4, c/4+4, c/4+8, c/4+12, so lane j reads key (j/4) of a 4-key group at
-// dims 4*(j%4)..+3 and each lane ends up holding one dim for 4 keys -- V
-// stays row-major in LDS.
+// = query); the PV operand V^T is read with transposing LDS reads, so V stays
+// row-major in LDS.
 // ---------------------------------------------------------------------------
 template <int STAGES, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4))) void attn_bf16_d64_kernel(AttnArgs a) {
@@ -165,20 +190,18 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
     // DMA lanes: wave w issues chunks w*LOADS+j (0..7 K rows, 8..15 V rows), 8 rows of 128 B per
     // chunk, so a wave loads only K or only V.  A tile wholly inside the fresh band or wholly in
     // the stale map (all but at most two tiles per split) takes one wave-uniform base address
-    // (scalar arithmetic) plus a fixed 32-bit per-lane byte offset; a tile that straddles a band
-    // edge or runs past the last key picks the buffer per row.
+    // (scalar arithmetic) plus a 32-bit per-lane byte offset; a tile that straddles a band edge or
+    // runs past the last key picks the buffer per row.
     const int sub = lane >> 3;
     const int slot = lane & 7;
     const uint16_t* zero = (const uint16_t*)g_attn_zero;
     const bool is_k = wave * LOADS < 8;
     const uint16_t* fresh_buf = is_k ? a.k : a.v;
     const uint16_t* stale_buf = is_k ? a.ks : a.vs;
-    uint32_t loffb[LOADS];
-#pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
-        const int row = ((wave * LOADS + j) & 7) * 8 + sub;
-        loffb[j] = (uint32_t)(row * a.C + col0 + (slot ^ (row & 7)) * 8) * 2u;
-    }
+    // The wave's chunk j covers rows row0 + 8 j (its chunks are consecutive), so chunk j is chunk
+    // 0 moved by 8 j rows of the wave-uniform base: one 32-bit lane offset (row0 + sub, slot) for
+    // all of them.
+    const uint32_t loff0 = (uint32_t)((((wave * LOADS) & 7) * 8 + sub) * a.C + col0 + (slot ^ sub) * 8) * 2u;
     // token n of the band at fresh_tok + n (n in [band0, band0 + Nq)), of the map at stale_tok + n;
     // both wave-uniform, kept in scalar registers
     const uint64_t fresh_tok = uniform_u64((uint64_t)(fresh_buf + ((int64_t)b * a.Nq - a.band0) * a.C));
@@ -194,7 +217,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
             const char* base_ = (const char*)((in_band_ ? fresh_tok : stale_tok) +                  \
                                               (uint64_t)(uint32_t)n0_ * row_bytes);                 \
             _Pragma("unroll") for (int j = 0; j < LOADS; ++j)                                       \
-                __builtin_amdgcn_global_load_lds((const void*)(base_ + loffb[j]),                  \
+                __builtin_amdgcn_global_load_lds((const void*)(base_ + (uint64_t)j * 8 * row_bytes + loff0), \
                                                  (lds_void*)(st_ + (wave * LOADS + j) * 1024), 16, 0, 0); \
         } else {                                                                                    \
             _Pragma("unroll") for (int j = 0; j < LOADS; ++j) {                                     \
@@ -208,30 +231,25 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
         }                                                                                           \
     } while (0)
 
-    // K operand reads (A of S^T): key row kb*32 + (l & 31), 16-byte chunk 2*ks + hsel
+    // K operand reads (A of S^T): key row kb*32 + (l & 31), 16-byte chunk (2 ks + hsel) ^ (row & 7)
+    // for k-step ks, i.e. byte offset koff0 ^ (32 ks) (the XOR only flips bits 5..6)
     const int krow = lane & 31;
-    int koff[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) koff[ks] = krow * 128 + (((2 * ks + hsel) ^ (krow & 7)) * 16);
-    // V^T operand reads via tr reads: lane l = 16g + j; key 16u + 4*(g>>1) + 8h + (j>>2),
-    // dims 32*db + 16*(g&1) + 4*(j&3) .. +3
-    const int gq = lane >> 4, jl = lane & 15;
-    int voff[2][2];   // [h][db] byte offsets inside the V tile for u = 0
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-            const int row = 4 * (gq >> 1) + 8 * h + (jl >> 2);          // + 16u (u*16 rows keeps row & 7)
-            const int d = 32 * db + 16 * (gq & 1) + 4 * (jl & 3);
-            voff[h][db] = 8192 + row * 128 + (((d >> 3) ^ (row & 7)) * 16) + (d & 7) * 2;
-        }
+    const uint32_t koff0 = (uint32_t)(krow * 128 + ((hsel ^ (krow & 7)) * 16));
+    // V^T operand reads: lane l = 16g + j reads key 16u + 4*(g>>1) + (j>>2) (+8 for the second
+    // read) at dims 16*(g&1) + 4*(j&3) .. +3 (+32: chunk c + 4, i.e. byte offset ^ 64)
+    uint32_t voff00;
+    {
+        const int gq = lane >> 4, jl = lane & 15;
+        const int row = 4 * (gq >> 1) + (jl >> 2);
+        const int d = 16 * (gq & 1) + 4 * (jl & 3);
+        voff00 = (uint32_t)(8192 + row * 128 + (((d >> 3) ^ (row & 7)) * 16) + (d & 7) * 2);
+    }
 
     // Online softmax with a lazily moved offset m_run (base-2 units of scale * score):
     // p = 2^(sc * s - m_run), the scale applied in fp32 by one FMA per score.  m_run is set to
-    // the first tile's maximum and moved up to the running maximum only when some score exceeds
-    // it by more than kLazy (p <= 2^kLazy, harmless in the fp32 sums and the bf16 P; the
-    // cross-half exchange happens only then); since m_run is always a score that occurred, the
-    // largest p of a row is >= 1.
+    // the first half tile's maximum and moved up to the running maximum only when some score
+    // exceeds it by more than kLazy (p <= 2^kLazy, harmless in the fp32 sums and the bf16 P);
+    // since m_run is always a score that occurred, the largest p of a row is >= 1.
     f32x16 o0, o1;
     const f32x16 zacc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     o0 = zacc;
@@ -241,116 +259,178 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
     bool first = true;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    if (nt > 0) {
-        for (int s = 0; s < STAGES - 1; ++s)
-            if (s < nt) DPA_ISSUE(t0 + s, s);
+    // Scores of the 32-key half KO / 4096 of the tile whose K starts at LDS address SA (+ koff0).
+#define DPA_S(S, SA, KO)                                                                            \
+    do {                                                                                            \
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_ld128((SA) + (KO)), q0, zacc, 0, 0, 0);     \
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_ld128(((SA) ^ 32) + (KO)), q1, S, 0, 0, 0); \
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_ld128(((SA) ^ 64) + (KO)), q2, S, 0, 0, 0); \
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_ld128(((SA) ^ 96) + (KO)), q3, S, 0, 0, 0); \
+    } while (0)
+    // Probabilities of a half (P^T operands PA: keys 16u + 4*hsel + {0..3, 8..11} of its first 16,
+    // PB: of its second 16) and their sum; the row sum adds the same bf16 values P.V uses.
+#define DPA_EXP(S, PA, PB, L)                                                                       \
+    do {                                                                                            \
+        const float nm_ = -m_run;                                                                   \
+        _Pragma("unroll") for (int i = 0; i < 16; ++i) S[i] = __builtin_amdgcn_exp2f(fmaf(S[i], sc, nm_)); \
+        PA = pack_probs<0>(S);                                                                      \
+        PB = pack_probs<2>(S);                                                                      \
+        float la_ = 0.f, lb_ = 0.f;                                                                 \
+        const uint4 wa_ = __builtin_bit_cast(uint4, PA), wb_ = __builtin_bit_cast(uint4, PB);       \
+        la_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wa_.x), ones, la_, false); \
+        la_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wa_.y), ones, la_, false); \
+        la_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wa_.z), ones, la_, false); \
+        la_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wa_.w), ones, la_, false); \
+        lb_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wb_.x), ones, lb_, false); \
+        lb_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wb_.y), ones, lb_, false); \
+        lb_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wb_.z), ones, lb_, false); \
+        lb_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wb_.w), ones, lb_, false); \
+        L = la_ + lb_;                                                                              \
+    } while (0)
+    // Slow path of a half of tile T (K at SA): its raw scores again, keys >= N masked (-inf, so
+    // p = 0), its maximum (both lane halves of a query), the offset moved if it is exceeded by
+    // more than kLazy (everything accumulated so far rescaled), and the half exponentiated again.
+#define DPA_FIX(S, SA, KO, T, PA, PB, L)                                                            \
+    do {                                                                                            \
+        DPA_S(S, SA, KO);                                                                           \
+        if (((T) + 1) * KT > a.N) {                                                                 \
+            const int kvalid_ = a.N - ((T) * KT + 4 * hsel) - (KO) / 128;                           \
+            _Pragma("unroll") for (int i = 0; i < 16; ++i)                                          \
+                if (8 * (i >> 2) + (i & 3) >= kvalid_) S[i] = -INFINITY;                            \
+        }                                                                                           \
+        float m0_ = fmaxf(S[0], S[1]), m1_ = fmaxf(S[2], S[3]);                                     \
+        _Pragma("unroll") for (int i = 4; i < 16; i += 4) {                                         \
+            m0_ = fmaxf(fmaxf(m0_, S[i]), S[i + 1]);                                                \
+            m1_ = fmaxf(fmaxf(m1_, S[i + 2]), S[i + 3]);                                            \
+        }                                                                                           \
+        float mx_ = fmaxf(m0_, m1_) * sc;                                                           \
+        mx_ = fmaxf(mx_, __shfl_xor(mx_, 32));                                                      \
+        if (first || mx_ > m_run + kLazy) {                                                         \
+            const float mnew_ = first ? mx_ : fmaxf(m_run, mx_);                                    \
+            const float alpha_ = first ? 1.f : __builtin_amdgcn_exp2f(m_run - mnew_);               \
+            l_run *= alpha_;                                                                        \
+            o0 *= alpha_;                                                                           \
+            o1 *= alpha_;                                                                           \
+            m_run = mnew_;                                                                          \
+        }                                                                                           \
+        first = false;                                                                              \
+        DPA_EXP(S, PA, PB, L);                                                                      \
+    } while (0)
+    // One slice of a half's softmax, placed after one MFMA: the exponentials of score pair J, the
+    // bf16 pack of pair J-1 and the row-sum step of pair J-2 (the same operations, in the same
+    // order per value, as DPA_EXP); the fence keeps the compiler from regrouping the slices.
+#define DPA_SLICE(S, J)                                                                             \
+    do {                                                                                            \
+        S[2 * (J)] = __builtin_amdgcn_exp2f(fmaf(S[2 * (J)], sc, nm));                              \
+        S[2 * (J) + 1] = __builtin_amdgcn_exp2f(fmaf(S[2 * (J) + 1], sc, nm));                      \
+        if ((J) >= 1) w[(J) - 1] = pack_bf16x2(S[2 * (J) - 2], S[2 * (J) - 1]);                     \
+        if ((J) >= 2) {                                                                             \
+            if ((J) - 2 < 4) la_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[(J) - 2]), ones, la_, false); \
+            else lb_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[(J) - 2]), ones, lb_, false); \
+        }                                                                                           \
+        __builtin_amdgcn_sched_barrier(0);                                                          \
+    } while (0)
+#define DPA_VT(A, B) __builtin_bit_cast(bf16x8, __builtin_shufflevector(A, B, 0, 1, 2, 3, 4, 5, 6, 7))
+    // One pipelined block: the scores N of half KO/4096 of the next tile (K at kn) and P.V of the
+    // current tile's 16-key groups U0, U1 (operands PIA, PIB), alternating MFMA by MFMA with the
+    // softmax of the raw scores S (into POA, POB and the sum L).
+#define DPA_BLOCK(N, KO, U0, U1, PIA, PIB, S, POA, POB, L)                                          \
+    do {                                                                                            \
+        const float nm = -m_run;                                                                    \
+        uint32_t w[8];                                                                              \
+        float la_ = 0.f, lb_ = 0.f;                                                                 \
+        bf16x8 kf = lds_ld128(kn + (KO));                                                           \
+        s16x4 a0, b0, a1, b1;                                                                       \
+        lds_read_vt<U0>(va, vb, a0, b0, a1, b1);                                                    \
+        __builtin_amdgcn_sched_barrier(0);                                                          \
+        N = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, q0, zacc, 0, 0, 0);                         \
+        kf = lds_ld128((kn ^ 32) + (KO));                                                           \
+        DPA_SLICE(S, 0);                                                                            \
+        o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(DPA_VT(a0, b0), PIA, o0, 0, 0, 0);              \
+        DPA_SLICE(S, 1);                                                                            \
+        N = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, q1, N, 0, 0, 0);                            \
+        kf = lds_ld128((kn ^ 64) + (KO));                                                           \
+        DPA_SLICE(S, 2);                                                                            \
+        o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(DPA_VT(a1, b1), PIA, o1, 0, 0, 0);              \
+        lds_read_vt<U1>(va, vb, a0, b0, a1, b1);                                                    \
+        DPA_SLICE(S, 3);                                                                            \
+        N = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, q2, N, 0, 0, 0);                            \
+        kf = lds_ld128((kn ^ 96) + (KO));                                                           \
+        DPA_SLICE(S, 4);                                                                            \
+        o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(DPA_VT(a0, b0), PIB, o0, 0, 0, 0);              \
+        DPA_SLICE(S, 5);                                                                            \
+        N = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, q3, N, 0, 0, 0);                            \
+        DPA_SLICE(S, 6);                                                                            \
+        o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(DPA_VT(a1, b1), PIB, o1, 0, 0, 0);              \
+        DPA_SLICE(S, 7);                                                                            \
+        w[7] = pack_bf16x2(S[14], S[15]);                                                           \
+        lb_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[6]), ones, lb_, false);  \
+        lb_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[7]), ones, lb_, false);  \
+        POA = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));                       \
+        POB = __builtin_bit_cast(bf16x8, make_uint4(w[4], w[5], w[6], w[7]));                       \
+        L = la_ + lb_;                                                                              \
+    } while (0)
+
+    // Software pipeline over the key tiles, so that a wave's exponentials run between its own
+    // MFMAs (a SIMD does not overlap one wave's MFMAs with another wave's VALU work).  With
+    // Sh(t) the scores of keys 32h.. of tile t and PVh(t) their P.V, iteration t runs
+    //   block 1: S0(t+1) and PV0(t), with the softmax of S1(t); then the check of S1(t);
+    //   block 2: S1(t+1) and PV1(t), with the softmax of S0(t+1); then the check of S0(t+1).
+    // The ring then holds tile t (its V is still read), t+1 (its K is read), t+2 in flight, and
+    // t+3 is requested into the stage t-1 left.  The last iteration computes S(t+1) from a stale
+    // stage and discards it.
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nt) DPA_ISSUE(t0 + s, s);
+    // Q is in registers before the loop (its loads were issued ahead of the first tiles')
+    asm volatile("" ::"v"(q0), "v"(q1), "v"(q2), "v"(q3));
+    if (nt >= 3) wait_vmcnt<2 * LOADS>();
+    else if (nt == 2) wait_vmcnt<LOADS>();
+    else wait_vmcnt<0>();
+    ring_barrier();
+    f32x16 s1;          // raw S1 of the current tile
+    bf16x8 p0, p1;      // P of the current tile's first half (its sum already in l_run)
+    {
+        const uint32_t ka = lds_addr(smem) + koff0;
+        f32x16 s0;
+        DPA_S(s1, ka, 4096);
+        float la;
+        DPA_FIX(s0, ka, 0, t0, p0, p1, la);     // first tile: sets the offset
+        l_run = la;
     }
     for (int it = 0; it < nt; ++it) {
         const int t = t0 + it;
-        const int ahead = nt - 1 - it;
-        if (STAGES >= 4 && ahead >= 2) wait_vmcnt<2 * LOADS>();
-        else if (STAGES >= 3 && ahead >= 1) wait_vmcnt<LOADS>();
+        // this wave's loads of tile t+1 have landed (t+2's may not), then everyone's
+        if (it + 2 < nt) wait_vmcnt<LOADS>();
         else wait_vmcnt<0>();
-        __syncthreads();
-        const char* st = smem + (it % STAGES) * STAGE;
+        ring_barrier();
+        // every wave is done with tile t-1: tile t+3 goes into its stage
+        if (it + 3 < nt) DPA_ISSUE(t + 3, (it + 3) % STAGES);
+        const uint32_t stc = lds_addr(smem) + (uint32_t)((it % STAGES) * STAGE);
+        const uint32_t kn = lds_addr(smem) + (uint32_t)(((it + 1) % STAGES) * STAGE) + koff0;
+        const uint32_t va = stc + voff00, vb = va ^ 64u;
 
-        // S^T[key][query] = K Q^T (unscaled; the MFMAs start from 0), keys kb*32 + 8q + 4*hsel + r
-        // in s_kb[4q + r]
-        f32x16 s0, s1;
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + koff[0]), q0, zacc, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + 4096 + koff[0]), q0, zacc, 0, 0, 0);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + koff[1]), q1, s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + 4096 + koff[1]), q1, s1, 0, 0, 0);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + koff[2]), q2, s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + 4096 + koff[2]), q2, s1, 0, 0, 0);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + koff[3]), q3, s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(st + 4096 + koff[3]), q3, s1, 0, 0, 0);
+        f32x16 n0;          // raw S0 of tile t+1
+        bf16x8 p2, p3;
+        float lb;
+        DPA_BLOCK(n0, 0, 0, 1, p0, p1, s1, p2, p3, lb);
+        if (__builtin_amdgcn_ballot_w64((t + 1) * KT > a.N || !(lb <= kLazyMax)))
+            DPA_FIX(s1, stc + koff0, 4096, t, p2, p3, lb);
+        l_run += lb;
 
-        // keys >= N occur only in a ragged last tile: excluded from the max, p = 0
-        if ((t + 1) * KT > a.N) {
-            const int kvalid = a.N - (t * KT + 4 * hsel);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int off = 8 * (i >> 2) + (i & 3);
-                if (off >= kvalid) s0[i] = -INFINITY;
-                if (off + 32 >= kvalid) s1[i] = -INFINITY;
-            }
+        float la;
+        DPA_BLOCK(s1, 4096, 2, 3, p2, p3, n0, p0, p1, la);
+        if (it + 1 < nt) {
+            if (__builtin_amdgcn_ballot_w64((t + 2) * KT > a.N || !(la <= kLazyMax)))
+                DPA_FIX(n0, kn, 0, t + 1, p0, p1, la);
+            l_run += la;
         }
-        // the tile maximum (two independent chains of 3-input maxima, v_max3_f32, over this
-        // lane's half of the keys) only decides whether the offset must move, which is rare after
-        // the first tile
-        float mx0 = fmaxf(s0[0], s0[1]), mx1 = fmaxf(s1[0], s1[1]);
-#pragma unroll
-        for (int i = 2; i < 16; i += 2) {
-            mx0 = fmaxf(fmaxf(mx0, s0[i]), s0[i + 1]);
-            mx1 = fmaxf(fmaxf(mx1, s1[i]), s1[i + 1]);
-        }
-        float mx = fmaxf(mx0, mx1) * sc;
-        if (__builtin_amdgcn_ballot_w64(first || mx > m_run + kLazy)) {
-            mx = fmaxf(mx, __shfl_xor(mx, 32));     // max of sc * s over the tile's keys
-            const float mnew = first ? mx : fmaxf(m_run, mx);
-            const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(m_run - mnew);
-            l_run *= alpha;
-            o0 *= alpha;
-            o1 *= alpha;
-            m_run = mnew;
-            first = false;
-        }
-        {
-            const float nm = -m_run;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                s0[i] = __builtin_amdgcn_exp2f(fmaf(s0[i], sc, nm));
-                s1[i] = __builtin_amdgcn_exp2f(fmaf(s1[i], sc, nm));
-            }
-        }
-        // P^T operands (keys 16u + 4*hsel + {0..3, 8..11}); the row sum adds the same bf16 values
-        const bf16x8 p0 = pack_probs<0>(s0);
-        const bf16x8 p1 = pack_probs<2>(s0);
-        const bf16x8 p2 = pack_probs<0>(s1);
-        const bf16x8 p3 = pack_probs<2>(s1);
-        float l_t;
-        {
-            float la = 0.f, lb = 0.f;
-#define DPA_SUM(PV, L)                                                                              \
-    do {                                                                                            \
-        const uint4 w_ = __builtin_bit_cast(uint4, PV);                                             \
-        L = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w_.x), ones, L, false);      \
-        L = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w_.y), ones, L, false);      \
-        L = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w_.z), ones, L, false);      \
-        L = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w_.w), ones, L, false);      \
-    } while (0)
-            DPA_SUM(p0, la);
-            DPA_SUM(p1, lb);
-            DPA_SUM(p2, la);
-            DPA_SUM(p3, lb);
-#undef DPA_SUM
-            l_t = la + lb;
-        }
-        l_run += l_t;
-#define DPA_PV(U, PU)                                                                               \
-    do {                                                                                            \
-        const char* vb_ = st + (U) * 16 * 128;                                                      \
-        const s16x4 a0_ = tr_read(vb_ + voff[0][0]);                                                \
-        const s16x4 b0_ = tr_read(vb_ + voff[1][0]);                                                \
-        const s16x4 a1_ = tr_read(vb_ + voff[0][1]);                                                \
-        const s16x4 b1_ = tr_read(vb_ + voff[1][1]);                                                \
-        const bf16x8 v0_ = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0_, b0_, 0, 1, 2, 3, 4, 5, 6, 7)); \
-        const bf16x8 v1_ = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a1_, b1_, 0, 1, 2, 3, 4, 5, 6, 7)); \
-        o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0_, PU, o0, 0, 0, 0);                          \
-        o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1_, PU, o1, 0, 0, 0);                          \
-    } while (0)
-        DPA_PV(0, p0);
-        DPA_PV(1, p1);
-        DPA_PV(2, p2);
-        DPA_PV(3, p3);
-#undef DPA_PV
-        // Tile t+3 goes into the stage tile t-1 left (every wave passed this iteration's barrier
-        // after its last read of it).  Issued after this tile's V^T reads: the compiler makes the
-        // transposing LDS reads wait for every direct-to-LDS load in flight, so loads issued
-        // earlier in the iteration would be waited for here.
-        if (it + STAGES - 1 < nt) DPA_ISSUE(t + STAGES - 1, (it + STAGES - 1) % STAGES);
     }
+#undef DPA_BLOCK
+#undef DPA_VT
+#undef DPA_SLICE
+#undef DPA_FIX
+#undef DPA_EXP
+#undef DPA_S
 #undef DPA_ISSUE
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
