@@ -76,6 +76,41 @@ def test_peaked_softmax_bf16(q_scale):
     run_case(1, 64, 64, 10, 64, 4, 1, "bf16", seed=10, q_scale=q_scale)
 
 
+@pytest.mark.parametrize("order", ["rising", "falling"])
+@pytest.mark.parametrize("i", [1, 3])
+def test_score_steps_move_offset(order, i):
+    """Scores that step by about 11.5 (in units of log2 of the softmax weight) every 24 keys: rising,
+    every step is a new maximum more than 2^8 above the kernel's running offset, so the check on
+    each 32-key half's probability sum fails and the offset moves, in first and second halves of
+    tiles alike (steps at keys 24, 48, 72, ... fall in both) and in every key split; falling, the
+    first tile holds the maximum and the offset never moves.  A missed rescale would weight an
+    earlier level 2^11 times too much."""
+    B, H, W, heads, d, P = 1, 64, 64, 2, 64, 4
+    C, N = heads * d, H * W
+    rng = np.random.default_rng(31 + i)
+    a = rng.choice([-1.0, 1.0], size=(heads, d)).astype(np.float32)      # one direction per head
+    lvl = (np.arange(N) // 24).astype(np.float32)
+    if order == "falling":
+        lvl = lvl[::-1].copy()
+    scale = 1.0 / np.sqrt(d)
+    # q ~ a, k_n = lvl_n a (integers, exact in bf16): scale * log2(e) * q.k_n ~ 11.5 * lvl_n
+    k_full = synth.to_storage((lvl[:, None, None] * a[None]).reshape(B, N, C), "bf16")
+    q_full = synth.to_storage((a[None] + 0.05 * rng.standard_normal((N, heads, d))).reshape(B, N, C), "bf16")
+    v_full = synth.to_storage(rng.standard_normal((B, N, C)), "bf16")
+    y = scale * np.log2(np.e) * np.einsum("hd,nhd->nh", a, k_full.reshape(N, heads, d).astype(np.float64))
+    if order == "rising":
+        assert np.min(np.diff(y[24::24, 0])) > 8.0        # every step exceeds the lazy margin
+    nq = (H // P) * W
+    t0 = i * nq
+    q, k, v = (x[:, t0:t0 + nq] for x in (q_full, k_full, v_full))
+    announce("attention score steps", order, "patch", i)
+    ref = oracle.attention_splice(q, k, v, k_full, v_full, H, W, P, i, heads)
+    o = dp.dp_attention_splice(dp.Patch(B, H, W, C, P, i), heads, gpu(q, "bf16"), gpu(k, "bf16"), gpu(v, "bf16"),
+                               gpu(k_full, "bf16"), gpu(v_full, "bf16"))
+    torch.cuda.synchronize()
+    assert_parity(host(o), ref, "bf16", f"attn score steps {order} i{i}")
+
+
 @pytest.mark.parametrize("d", [4, 16, 32, 64, 128])
 def test_f32_head_dims(d):
     announce("attention f32 d", d)
