@@ -113,15 +113,16 @@ __device__ __forceinline__ void ring_barrier() { asm volatile("s_waitcnt lgkmcnt
 // key (j/4) of a 4-key group at 4 consecutive dims and each lane ends up holding one dim for 4
 // keys.  Four reads (va, va + 1 KB: keys +0/+8 of dims 0..31; vb = va ^ 64: dims 32..63), waited
 // for in the same asm block.
-template <int U>
+template <int U, int SO = 0>
 __device__ __forceinline__ void lds_read_vt(uint32_t va, uint32_t vb, s16x4& r00, s16x4& r10, s16x4& r01,
                                             s16x4& r11) {
+    static_assert(SO + U * 2048 + 1024 < 65536, "LDS offset field");
     asm volatile(
         "ds_read_b64_tr_b16 %0, %4 offset:%6\n\tds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
         "ds_read_b64_tr_b16 %2, %5 offset:%6\n\tds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(r00), "=&v"(r10), "=&v"(r01), "=&v"(r11)
-        : "v"(va), "v"(vb), "i"(U * 2048), "i"(U * 2048 + 1024));
+        : "v"(va), "v"(vb), "i"(SO + U * 2048), "i"(SO + U * 2048 + 1024));
 }
 
 // ---------------------------------------------------------------------------
@@ -245,16 +246,16 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
         voff00 = (uint32_t)(8192 + row * 128 + (((d >> 3) ^ (row & 7)) * 16) + (d & 7) * 2);
     }
 
-    // Online softmax with a lazily moved offset m_run (base-2 units of scale * score):
-    // p = 2^(sc * s - m_run), the scale applied in fp32 by one FMA per score.  m_run is set to
+    // Online softmax with a lazily moved offset m (base-2 units of scale * score), kept negated
+    // as nm_run: p = 2^(sc * s - m), the scale applied in fp32 by one FMA per score.  m is set to
     // the first half tile's maximum and moved up to the running maximum only when some score
     // exceeds it by more than kLazy (p <= 2^kLazy, harmless in the fp32 sums and the bf16 P);
-    // since m_run is always a score that occurred, the largest p of a row is >= 1.
+    // since m is always a score that occurred, the largest p of a row is >= 1.
     f32x16 o0, o1;
     const f32x16 zacc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     o0 = zacc;
     o1 = zacc;
-    float m_run = 0.f;
+    float nm_run = 0.f;     // minus the offset
     float l_run = 0.f;
     bool first = true;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -268,24 +269,23 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
         S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_ld128(((SA) ^ 96) + (KO)), q3, S, 0, 0, 0); \
     } while (0)
     // Probabilities of a half (P^T operands PA: keys 16u + 4*hsel + {0..3, 8..11} of its first 16,
-    // PB: of its second 16) and their sum; the row sum adds the same bf16 values P.V uses.
+    // PB: of its second 16) and their sum, in one chain; the row sum adds the same bf16 values
+    // P.V uses.
 #define DPA_EXP(S, PA, PB, L)                                                                       \
     do {                                                                                            \
-        const float nm_ = -m_run;                                                                   \
-        _Pragma("unroll") for (int i = 0; i < 16; ++i) S[i] = __builtin_amdgcn_exp2f(fmaf(S[i], sc, nm_)); \
+        _Pragma("unroll") for (int i = 0; i < 16; ++i) S[i] = __builtin_amdgcn_exp2f(fmaf(S[i], sc, nm_run)); \
         PA = pack_probs<0>(S);                                                                      \
         PB = pack_probs<2>(S);                                                                      \
-        float la_ = 0.f, lb_ = 0.f;                                                                 \
         const uint4 wa_ = __builtin_bit_cast(uint4, PA), wb_ = __builtin_bit_cast(uint4, PB);       \
-        la_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wa_.x), ones, la_, false); \
-        la_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wa_.y), ones, la_, false); \
-        la_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wa_.z), ones, la_, false); \
-        la_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wa_.w), ones, la_, false); \
-        lb_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wb_.x), ones, lb_, false); \
-        lb_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wb_.y), ones, lb_, false); \
-        lb_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wb_.z), ones, lb_, false); \
-        lb_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wb_.w), ones, lb_, false); \
-        L = la_ + lb_;                                                                              \
+        float l_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wa_.x), ones, 0.f, false); \
+        l_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wa_.y), ones, l_, false);   \
+        l_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wa_.z), ones, l_, false);   \
+        l_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wa_.w), ones, l_, false);   \
+        l_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wb_.x), ones, l_, false);   \
+        l_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wb_.y), ones, l_, false);   \
+        l_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wb_.z), ones, l_, false);   \
+        l_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wb_.w), ones, l_, false);   \
+        L = l_;                                                                                     \
     } while (0)
     // Slow path of a half of tile T (K at SA): its raw scores again, keys >= N masked (-inf, so
     // p = 0), its maximum (both lane halves of a query), the offset moved if it is exceeded by
@@ -305,70 +305,68 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
         }                                                                                           \
         float mx_ = fmaxf(m0_, m1_) * sc;                                                           \
         mx_ = fmaxf(mx_, __shfl_xor(mx_, 32));                                                      \
-        if (first || mx_ > m_run + kLazy) {                                                         \
-            const float mnew_ = first ? mx_ : fmaxf(m_run, mx_);                                    \
-            const float alpha_ = first ? 1.f : __builtin_amdgcn_exp2f(m_run - mnew_);               \
+        if (first || mx_ > -nm_run + kLazy) {                                                       \
+            const float nmnew_ = first ? -mx_ : fminf(nm_run, -mx_);                                \
+            const float alpha_ = first ? 1.f : __builtin_amdgcn_exp2f(nmnew_ - nm_run);             \
             l_run *= alpha_;                                                                        \
             o0 *= alpha_;                                                                           \
             o1 *= alpha_;                                                                           \
-            m_run = mnew_;                                                                          \
+            nm_run = nmnew_;                                                                        \
         }                                                                                           \
         first = false;                                                                              \
         DPA_EXP(S, PA, PB, L);                                                                      \
     } while (0)
     // One slice of a half's softmax, placed after one MFMA: the exponentials of score pair J, the
     // bf16 pack of pair J-1 and the row-sum step of pair J-2 (the same operations, in the same
-    // order per value, as DPA_EXP); the fence keeps the compiler from regrouping the slices.
+    // order, as DPA_EXP); the fence keeps the compiler from regrouping the slices.
 #define DPA_SLICE(S, J)                                                                             \
     do {                                                                                            \
-        S[2 * (J)] = __builtin_amdgcn_exp2f(fmaf(S[2 * (J)], sc, nm));                              \
-        S[2 * (J) + 1] = __builtin_amdgcn_exp2f(fmaf(S[2 * (J) + 1], sc, nm));                      \
+        S[2 * (J)] = __builtin_amdgcn_exp2f(fmaf(S[2 * (J)], sc, nm_run));                          \
+        S[2 * (J) + 1] = __builtin_amdgcn_exp2f(fmaf(S[2 * (J) + 1], sc, nm_run));                  \
         if ((J) >= 1) w[(J) - 1] = pack_bf16x2(S[2 * (J) - 2], S[2 * (J) - 1]);                     \
-        if ((J) >= 2) {                                                                             \
-            if ((J) - 2 < 4) la_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[(J) - 2]), ones, la_, false); \
-            else lb_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[(J) - 2]), ones, lb_, false); \
-        }                                                                                           \
+        if ((J) == 2) l_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[0]), ones, 0.f, false); \
+        if ((J) > 2) l_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[(J) - 2]), ones, l_, false); \
         __builtin_amdgcn_sched_barrier(0);                                                          \
     } while (0)
 #define DPA_VT(A, B) __builtin_bit_cast(bf16x8, __builtin_shufflevector(A, B, 0, 1, 2, 3, 4, 5, 6, 7))
-    // One pipelined block: the scores N of half KO/4096 of the next tile (K at kn) and P.V of the
-    // current tile's 16-key groups U0, U1 (operands PIA, PIB), alternating MFMA by MFMA with the
-    // softmax of the raw scores S (into POA, POB and the sum L).
-#define DPA_BLOCK(N, KO, U0, U1, PIA, PIB, S, POA, POB, L)                                          \
+    // One pipelined block: the scores N of half KO/4096 of the next tile (its K in ring stage SN)
+    // and P.V of the current tile's 16-key groups U0, U1 (its V in stage SC; operands PIA, PIB),
+    // alternating MFMA by MFMA with the softmax of the raw scores S (into POA, POB and the sum
+    // L).  The stages are constants, so every LDS address is a lane offset plus an immediate.
+#define DPA_BLOCK(N, SN, SC, KO, U0, U1, PIA, PIB, S, POA, POB, L)                                  \
     do {                                                                                            \
-        const float nm = -m_run;                                                                    \
         uint32_t w[8];                                                                              \
-        float la_ = 0.f, lb_ = 0.f;                                                                 \
-        bf16x8 kf = lds_ld128(kn + (KO));                                                           \
+        float l_ = 0.f;                                                                             \
+        bf16x8 kf = lds_ld128(kl0 + (SN) * STAGE + (KO));                                           \
         s16x4 a0, b0, a1, b1;                                                                       \
-        lds_read_vt<U0>(va, vb, a0, b0, a1, b1);                                                    \
+        lds_read_vt<U0, (SC) * STAGE>(vl0, vl1, a0, b0, a1, b1);                                    \
         __builtin_amdgcn_sched_barrier(0);                                                          \
         N = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, q0, zacc, 0, 0, 0);                         \
-        kf = lds_ld128((kn ^ 32) + (KO));                                                           \
+        kf = lds_ld128(kl1 + (SN) * STAGE + (KO));                                                  \
         DPA_SLICE(S, 0);                                                                            \
-        o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(DPA_VT(a0, b0), PIA, o0, 0, 0, 0);              \
+        o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(DPA_VT(a0, b0), PIA, o0, 0, 0, 0);             \
         DPA_SLICE(S, 1);                                                                            \
         N = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, q1, N, 0, 0, 0);                            \
-        kf = lds_ld128((kn ^ 64) + (KO));                                                           \
+        kf = lds_ld128(kl2 + (SN) * STAGE + (KO));                                                  \
         DPA_SLICE(S, 2);                                                                            \
-        o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(DPA_VT(a1, b1), PIA, o1, 0, 0, 0);              \
-        lds_read_vt<U1>(va, vb, a0, b0, a1, b1);                                                    \
+        o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(DPA_VT(a1, b1), PIA, o1, 0, 0, 0);             \
+        lds_read_vt<U1, (SC) * STAGE>(vl0, vl1, a0, b0, a1, b1);                                    \
         DPA_SLICE(S, 3);                                                                            \
         N = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, q2, N, 0, 0, 0);                            \
-        kf = lds_ld128((kn ^ 96) + (KO));                                                           \
+        kf = lds_ld128(kl3 + (SN) * STAGE + (KO));                                                  \
         DPA_SLICE(S, 4);                                                                            \
-        o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(DPA_VT(a0, b0), PIB, o0, 0, 0, 0);              \
+        o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(DPA_VT(a0, b0), PIB, o0, 0, 0, 0);             \
         DPA_SLICE(S, 5);                                                                            \
         N = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, q3, N, 0, 0, 0);                            \
         DPA_SLICE(S, 6);                                                                            \
-        o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(DPA_VT(a1, b1), PIB, o1, 0, 0, 0);              \
+        o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(DPA_VT(a1, b1), PIB, o1, 0, 0, 0);             \
         DPA_SLICE(S, 7);                                                                            \
         w[7] = pack_bf16x2(S[14], S[15]);                                                           \
-        lb_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[6]), ones, lb_, false);  \
-        lb_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[7]), ones, lb_, false);  \
+        l_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[6]), ones, l_, false);    \
+        l_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[7]), ones, l_, false);    \
         POA = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));                       \
         POB = __builtin_bit_cast(bf16x8, make_uint4(w[4], w[5], w[6], w[7]));                       \
-        L = la_ + lb_;                                                                              \
+        L = l_;                                                                                     \
     } while (0)
 
     // Software pipeline over the key tiles, so that a wave's exponentials run between its own
@@ -397,34 +395,42 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
         DPA_FIX(s0, ka, 0, t0, p0, p1, la);     // first tile: sets the offset
         l_run = la;
     }
-    for (int it = 0; it < nt; ++it) {
-        const int t = t0 + it;
-        // this wave's loads of tile t+1 have landed (t+2's may not), then everyone's
-        if (it + 2 < nt) wait_vmcnt<LOADS>();
-        else wait_vmcnt<0>();
-        ring_barrier();
-        // every wave is done with tile t-1: tile t+3 goes into its stage
-        if (it + 3 < nt) DPA_ISSUE(t + 3, (it + 3) % STAGES);
-        const uint32_t stc = lds_addr(smem) + (uint32_t)((it % STAGES) * STAGE);
-        const uint32_t kn = lds_addr(smem) + (uint32_t)(((it + 1) % STAGES) * STAGE) + koff0;
-        const uint32_t va = stc + voff00, vb = va ^ 64u;
-
-        f32x16 n0;          // raw S0 of tile t+1
-        bf16x8 p2, p3;
-        float lb;
-        DPA_BLOCK(n0, 0, 0, 1, p0, p1, s1, p2, p3, lb);
-        if (__builtin_amdgcn_ballot_w64((t + 1) * KT > a.N || !(lb <= kLazyMax)))
-            DPA_FIX(s1, stc + koff0, 4096, t, p2, p3, lb);
-        l_run += lb;
-
-        float la;
-        DPA_BLOCK(s1, 4096, 2, 3, p2, p3, n0, p0, p1, la);
-        if (it + 1 < nt) {
-            if (__builtin_amdgcn_ballot_w64((t + 2) * KT > a.N || !(la <= kLazyMax)))
-                DPA_FIX(n0, kn, 0, t + 1, p0, p1, la);
-            l_run += la;
-        }
+    // lane offsets of the K fragments (k-steps 0..3) and of the V^T fragments; the stage is a
+    // constant offset in the unrolled loop below
+    const uint32_t kl0 = lds_addr(smem) + koff0, kl1 = kl0 ^ 32u, kl2 = kl0 ^ 64u, kl3 = kl0 ^ 96u;
+    const uint32_t vl0 = lds_addr(smem) + voff00, vl1 = vl0 ^ 64u;
+    // one iteration with tile t in stage SC (its V read), tile t+1 in stage SN (its K read)
+#define DPA_ITER(SC, SN, SI)                                                                        \
+    if (it0 + (SC) < nt) {                                                                          \
+        const int it = it0 + (SC);                                                                  \
+        const int t = t0 + it;                                                                      \
+        if (it + 2 < nt) wait_vmcnt<LOADS>();                                                       \
+        else wait_vmcnt<0>();                                                                       \
+        ring_barrier();                                                                             \
+        if (it + 3 < nt) DPA_ISSUE(t + 3, SI);                                                      \
+        f32x16 n0;                                                                                  \
+        bf16x8 p2, p3;                                                                              \
+        float lb;                                                                                   \
+        DPA_BLOCK(n0, SN, SC, 0, 0, 1, p0, p1, s1, p2, p3, lb);                                     \
+        if (__builtin_amdgcn_ballot_w64((t + 1) * KT > a.N || !(lb <= kLazyMax)))                   \
+            DPA_FIX(s1, kl0 + (SC) * STAGE, 4096, t, p2, p3, lb);                                   \
+        l_run += lb;                                                                                \
+        float la;                                                                                   \
+        DPA_BLOCK(s1, SN, SC, 4096, 2, 3, p2, p3, n0, p0, p1, la);                                  \
+        if (it + 1 < nt) {                                                                          \
+            if (__builtin_amdgcn_ballot_w64((t + 2) * KT > a.N || !(la <= kLazyMax)))               \
+                DPA_FIX(n0, kl0 + (SN) * STAGE, 0, t + 1, p0, p1, la);                              \
+            l_run += la;                                                                            \
+        }                                                                                           \
     }
+    static_assert(STAGES == 4, "the loop is unrolled by the ring depth");
+    for (int it0 = 0; it0 < nt; it0 += STAGES) {
+        DPA_ITER(0, 1, 3)
+        DPA_ITER(1, 2, 0)
+        DPA_ITER(2, 3, 1)
+        DPA_ITER(3, 0, 2)
+    }
+#undef DPA_ITER
 #undef DPA_BLOCK
 #undef DPA_VT
 #undef DPA_SLICE
@@ -457,7 +463,7 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
             *(float4*)(prow + 8 * q) = make_float4(o0[4 * q + 0], o0[4 * q + 1], o0[4 * q + 2], o0[4 * q + 3]);
             *(float4*)(prow + 32 + 8 * q) = make_float4(o1[4 * q + 0], o1[4 * q + 1], o1[4 * q + 2], o1[4 * q + 3]);
         }
-        if (hsel == 0) a.part_ml[row] = make_float2(m_run, l_tot);
+        if (hsel == 0) a.part_ml[row] = make_float2(-nm_run, l_tot);
     }
 }
 
@@ -613,9 +619,9 @@ hipError_t launch_attention(const Geom& g, const AttnPlan& plan, bool bf16, int 
         if (!grid_fits((total + 63) / 64)) return hipErrorInvalidConfiguration;
         const unsigned blocks = (unsigned)((total + 63) / 64);
         const float sc = scale * kLog2e;
-#define DP_F32_ATTN(HD)                                                                                  \
-    attn_f32_kernel<HD><<<blocks, 64, 0, stream>>>((const float*)q, (const float*)k, (const float*)v,   \
-                                                   (const float*)k_stale, (const float*)v_stale,        \
+#define DP_F32_ATTN(HD)                                                                             \
+    attn_f32_kernel<HD><<<blocks, 64, 0, stream>>>((const float*)q, (const float*)k, (const float*)v, \
+                                                   (const float*)k_stale, (const float*)v_stale,    \
                                                    (float*)o, g.B, heads, g.C, Nq, N, band0, sc)
         switch (head_dim) {
             case 4: DP_F32_ATTN(4); break;
