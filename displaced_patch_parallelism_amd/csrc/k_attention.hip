@@ -104,6 +104,15 @@ typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8;
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const lds_void*)p; }
 __device__ __forceinline__ bf16x8 lds_ld128(uint32_t addr) { return *(lds_bf16x8*)(uintptr_t)addr; }
 
+// The lane index, read so that the compiler cannot reuse an earlier copy: values derived from it on
+// rare paths (straddling tiles, the ragged last tile, the epilogue) are formed where they are used
+// instead of being kept, and spilled, across the tile loop.
+__device__ __forceinline__ int lane_now() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 // Workgroup barrier that waits only for the wave's LDS accesses: __syncthreads() would also wait
 // for the direct-to-LDS loads still in flight into the other ring stages.
 __device__ __forceinline__ void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -221,11 +230,12 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
                 __builtin_amdgcn_global_load_lds((const void*)(base_ + (uint64_t)j * 8 * row_bytes + loff0), \
                                                  (lds_void*)(st_ + (wave * LOADS + j) * 1024), 16, 0, 0); \
         } else {                                                                                    \
+            const int ln_ = lane_now();                                                             \
             _Pragma("unroll") for (int j = 0; j < LOADS; ++j) {                                     \
                 const int q_ = wave * LOADS + j;                                                    \
-                const int row_ = (q_ & 7) * 8 + sub;                                                \
+                const int row_ = (q_ & 7) * 8 + (ln_ >> 3);                                         \
                 const int n_ = n0_ + row_;                                                          \
-                const int ch_ = (slot ^ (row_ & 7)) * 8;                                            \
+                const int ch_ = ((ln_ & 7) ^ (row_ & 7)) * 8;                                       \
                 const uint16_t* g_ = n_ < a.N ? kv_row(fresh_buf, stale_buf, b, n_, a, col0 + ch_) : zero; \
                 __builtin_amdgcn_global_load_lds((const void*)g_, (lds_void*)(st_ + q_ * 1024), 16, 0, 0); \
             }                                                                                       \
@@ -259,14 +269,18 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
     float l_run = 0.f;
     bool first = true;
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    // lane offsets of the K fragments (k-steps 0..3: chunk (2 ks + hsel) ^ (row & 7), i.e. the
+    // base XOR 32 ks) and of the V^T fragments; a ring stage is a constant offset added to them
+    const uint32_t kl0 = lds_addr(smem) + koff0, kl1 = kl0 ^ 32u, kl2 = kl0 ^ 64u, kl3 = kl0 ^ 96u;
+    const uint32_t vl0 = lds_addr(smem) + voff00, vl1 = vl0 ^ 64u;
 
-    // Scores of the 32-key half KO / 4096 of the tile whose K starts at LDS address SA (+ koff0).
-#define DPA_S(S, SA, KO)                                                                            \
+    // Scores of the 32-key half KO / 4096 of the tile in ring stage SG.
+#define DPA_S(S, SG, KO)                                                                            \
     do {                                                                                            \
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_ld128((SA) + (KO)), q0, zacc, 0, 0, 0);     \
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_ld128(((SA) ^ 32) + (KO)), q1, S, 0, 0, 0); \
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_ld128(((SA) ^ 64) + (KO)), q2, S, 0, 0, 0); \
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_ld128(((SA) ^ 96) + (KO)), q3, S, 0, 0, 0); \
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_ld128(kl0 + (SG) * STAGE + (KO)), q0, zacc, 0, 0, 0); \
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_ld128(kl1 + (SG) * STAGE + (KO)), q1, S, 0, 0, 0); \
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_ld128(kl2 + (SG) * STAGE + (KO)), q2, S, 0, 0, 0); \
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_ld128(kl3 + (SG) * STAGE + (KO)), q3, S, 0, 0, 0); \
     } while (0)
     // Probabilities of a half (P^T operands PA: keys 16u + 4*hsel + {0..3, 8..11} of its first 16,
     // PB: of its second 16) and their sum, in one chain; the row sum adds the same bf16 values
@@ -287,14 +301,15 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
         l_ = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wb_.w), ones, l_, false);   \
         L = l_;                                                                                     \
     } while (0)
-    // Slow path of a half of tile T (K at SA): its raw scores again, keys >= N masked (-inf, so
-    // p = 0), its maximum (both lane halves of a query), the offset moved if it is exceeded by
-    // more than kLazy (everything accumulated so far rescaled), and the half exponentiated again.
-#define DPA_FIX(S, SA, KO, T, PA, PB, L)                                                            \
+    // Slow path of a half of tile T (in ring stage SG): its raw scores again, keys >= N masked
+    // (-inf, so p = 0), its maximum (both lane halves of a query), the offset moved if it is
+    // exceeded by more than kLazy (everything accumulated so far rescaled), and the half
+    // exponentiated again.
+#define DPA_FIX(S, SG, KO, T, PA, PB, L)                                                            \
     do {                                                                                            \
-        DPA_S(S, SA, KO);                                                                           \
+        DPA_S(S, SG, KO);                                                                           \
         if (((T) + 1) * KT > a.N) {                                                                 \
-            const int kvalid_ = a.N - ((T) * KT + 4 * hsel) - (KO) / 128;                           \
+            const int kvalid_ = a.N - ((T) * KT + 4 * (lane_now() >> 5)) - (KO) / 128;              \
             _Pragma("unroll") for (int i = 0; i < 16; ++i)                                          \
                 if (8 * (i >> 2) + (i & 3) >= kvalid_) S[i] = -INFINITY;                            \
         }                                                                                           \
@@ -388,17 +403,12 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
     f32x16 s1;          // raw S1 of the current tile
     bf16x8 p0, p1;      // P of the current tile's first half (its sum already in l_run)
     {
-        const uint32_t ka = lds_addr(smem) + koff0;
         f32x16 s0;
-        DPA_S(s1, ka, 4096);
+        DPA_S(s1, 0, 4096);
         float la;
-        DPA_FIX(s0, ka, 0, t0, p0, p1, la);     // first tile: sets the offset
+        DPA_FIX(s0, 0, 0, t0, p0, p1, la);      // first tile: sets the offset
         l_run = la;
     }
-    // lane offsets of the K fragments (k-steps 0..3) and of the V^T fragments; the stage is a
-    // constant offset in the unrolled loop below
-    const uint32_t kl0 = lds_addr(smem) + koff0, kl1 = kl0 ^ 32u, kl2 = kl0 ^ 64u, kl3 = kl0 ^ 96u;
-    const uint32_t vl0 = lds_addr(smem) + voff00, vl1 = vl0 ^ 64u;
     // one iteration with tile t in stage SC (its V read), tile t+1 in stage SN (its K read)
 #define DPA_ITER(SC, SN, SI)                                                                        \
     if (it0 + (SC) < nt) {                                                                          \
@@ -413,13 +423,13 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
         float lb;                                                                                   \
         DPA_BLOCK(n0, SN, SC, 0, 0, 1, p0, p1, s1, p2, p3, lb);                                     \
         if (__builtin_amdgcn_ballot_w64((t + 1) * KT > a.N || !(lb <= kLazyMax)))                   \
-            DPA_FIX(s1, kl0 + (SC) * STAGE, 4096, t, p2, p3, lb);                                   \
+            DPA_FIX(s1, SC, 4096, t, p2, p3, lb);                                   \
         l_run += lb;                                                                                \
         float la;                                                                                   \
         DPA_BLOCK(s1, SN, SC, 4096, 2, 3, p2, p3, n0, p0, p1, la);                                  \
         if (it + 1 < nt) {                                                                          \
             if (__builtin_amdgcn_ballot_w64((t + 2) * KT > a.N || !(la <= kLazyMax)))               \
-                DPA_FIX(n0, kl0 + (SN) * STAGE, 0, t + 1, p0, p1, la);                              \
+                DPA_FIX(n0, SN, 0, t + 1, p0, p1, la);                              \
             l_run += la;                                                                            \
         }                                                                                           \
     }
@@ -440,11 +450,13 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
 #undef DPA_ISSUE
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
-    if (!qvalid) return;
-    // O^T layout: lane owns query myq, dims db*32 + 8q + 4*hsel + r
+    const int lne = lane_now();
+    const int myq_e = qt * QTW + wave * 32 + (lne & 31), hsel_e = lne >> 5;
+    if (myq_e >= a.Nq) return;
+    // O^T layout: lane owns query myq_e, dims db*32 + 8q + 4*hsel_e + r
     if (a.kvsplit == 1) {
         const float inv = 1.0f / l_tot;
-        uint16_t* orow = a.o + ((int64_t)b * a.Nq + myq) * a.C + col0 + 4 * hsel;
+        uint16_t* orow = a.o + ((int64_t)b * a.Nq + myq_e) * a.C + col0 + 4 * hsel_e;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             uint2 w;
@@ -456,14 +468,14 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
             *(uint2*)(orow + 32 + 8 * q) = w;
         }
     } else {
-        const int64_t row = ((int64_t)split * a.B * a.heads + bh) * a.Nq + myq;
-        float* prow = a.part_o + row * D + 4 * hsel;
+        const int64_t row = ((int64_t)split * a.B * a.heads + bh) * a.Nq + myq_e;
+        float* prow = a.part_o + row * D + 4 * hsel_e;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             *(float4*)(prow + 8 * q) = make_float4(o0[4 * q + 0], o0[4 * q + 1], o0[4 * q + 2], o0[4 * q + 3]);
             *(float4*)(prow + 32 + 8 * q) = make_float4(o1[4 * q + 0], o1[4 * q + 1], o1[4 * q + 2], o1[4 * q + 3]);
         }
-        if (hsel == 0) a.part_ml[row] = make_float2(-nm_run, l_tot);
+        if (hsel_e == 0) a.part_ml[row] = make_float2(-nm_run, l_tot);
     }
 }
 
