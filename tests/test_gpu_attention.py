@@ -66,6 +66,26 @@ def test_ragged_bf16(B, H, W, heads, P, i):
     run_case(B, H, W, heads, 64, P, i, "bf16", seed=i)
 
 
+@pytest.mark.parametrize("B,H,W,heads,P,i", [
+    (1, 4, 8, 1, 2, 1),      # N = 32: one ragged key tile
+    (1, 8, 8, 1, 2, 0),      # N = 64: one full tile
+    (1, 4, 24, 2, 2, 1),     # 2 tiles, the last ragged
+    (1, 6, 32, 1, 2, 1),     # 3 tiles
+    (1, 8, 32, 1, 2, 0),     # 4 tiles: one whole pass of the loop unrolled by the ring depth
+    (1, 8, 40, 1, 4, 3),     # 5 tiles
+    (1, 12, 32, 1, 3, 1),    # 6 tiles
+    (1, 10, 44, 1, 2, 1),    # 7 tiles, the last with 56 keys
+    (2, 10, 48, 1, 2, 1),    # 8 tiles, the last ragged, batch 2
+    (1, 9, 64, 2, 3, 2),     # 9 tiles
+    (1, 12, 48, 3, 4, 2),    # 9 tiles in 4 key splits of 2, 2, 2 and 3
+])
+def test_key_tile_counts_bf16(B, H, W, heads, P, i):
+    """Every count of 64-key tiles per key split from 1 to 9, full and ragged: the tile loop's
+    prologue, its pipelined iterations and the unrolled loop's partial last pass."""
+    announce("attention tile counts", B, H, W, heads, P, i)
+    run_case(B, H, W, heads, 64, P, i, "bf16", seed=50 + H + W)
+
+
 @pytest.mark.parametrize("q_scale", [4.0, 8.0, 16.0])
 def test_peaked_softmax_bf16(q_scale):
     """Large scores (queries scaled x4, x8, x16: score standard deviations of about 4, 8 and 16,
