@@ -400,6 +400,19 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(4, 4
     else if (nt == 2) wait_vmcnt<LOADS>();
     else wait_vmcnt<0>();
     ring_barrier();
+    // A wave whose 32 queries all lie past the end of the patch (the last query tile of a band
+    // that is not a multiple of the tile) computes nothing: it only keeps loading its share of
+    // each tile and meets the workgroup at the same barriers, one per tile, leaving its SIMD's
+    // issue slots to the other waves.
+    if (qt * QTW + wave * 32 >= a.Nq) {
+        for (int it = 0; it < nt; ++it) {
+            if (it + 2 < nt) wait_vmcnt<LOADS>();
+            else wait_vmcnt<0>();
+            ring_barrier();
+            if (it + 3 < nt) DPA_ISSUE(t0 + it + 3, (it + 3) & (STAGES - 1));
+        }
+        return;
+    }
     f32x16 s1;          // raw S1 of the current tile
     bf16x8 p0, p1;      // P of the current tile's first half (its sum already in l_run)
     {
