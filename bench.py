@@ -358,11 +358,13 @@ def main():
     hbm_rates = {}
     if not args.no_hbm:
         hbm_rates["copy"] = hbm.copy_rate(3)
+        hbm_rates["splice_512MB"] = hbm.splice_ceiling(3)
         for cfg in cfgs:
             for row in hbm.call_rates(cfg, 3):
                 ent = {k: row[k] for k in ("band_bytes", "sets", "warm_us", "warm_gbs", "cold_us", "cold_gbs")}
                 ent["frac_hbm_peak_cold"] = round(row["cold_gbs"] / PEAK_HBM_GBS, 4)
                 ent["frac_copy_cold"] = round(row["cold_gbs"] / hbm_rates["copy"]["gbs"], 4)
+                ent["frac_splice_512MB_cold"] = round(row["cold_gbs"] / hbm_rates["splice_512MB"]["gbs"], 4)
                 hbm_rates[f"{cfg.name}/{row['op']}"] = ent
         log("HBM rates done")
 

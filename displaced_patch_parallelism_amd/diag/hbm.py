@@ -6,7 +6,9 @@ different buffer set, the sets together exceeding 2 x 256 MB, so each call finds
 HBM; the warm run repeats one set.  Each run is captured in one HIP graph and replayed, so the
 host's per-call dispatch cost is not timed (a bare launch loop from Python costs about 8 us a
 call, more than most of these kernels take).  Rates count one read and one write of the band (the
-algorithmic bytes); the plain copy (torch, 1 GiB) is the box's practical HBM ceiling.
+algorithmic bytes).  Two large copies give the box's practical HBM ceiling: torch's 1 GiB
+device copy, and the library's own splice kernel on a 512 MB band (a stream far larger than the
+MALL, so the launch's ramp and tail do not count).
 
     python -m displaced_patch_parallelism_amd.diag.hbm [--configs c1,c4a,c4b] [--reps 3]
 
@@ -61,6 +63,18 @@ def copy_rate(reps):
     return {"op": "copy", "bytes": 2 * n, "us": round(us, 2), "gbs": round(2 * n / us / 1e3, 1)}
 
 
+def splice_ceiling(reps):
+    """The splice kernel on one 512 MB band (1 x 2 x 262144 x 1024 bf16 map, 2 row patches)."""
+    import torch
+    import displaced_patch_parallelism_amd as dp
+    p = dp.Patch(1, 2, 262144, 1024, 2, 1)
+    x = torch.empty((1, 1, 262144, 1024), dtype=torch.bfloat16, device="cuda").fill_(1)
+    m = torch.empty((1, 2, 262144, 1024), dtype=torch.bfloat16, device="cuda")
+    n = x.numel() * 2
+    us = _time(lambda k: dp.dp_stale_update(p, x, m), range(5), reps)
+    return {"op": "splice_512MB", "bytes": 2 * n, "us": round(us, 2), "gbs": round(2 * n / us / 1e3, 1)}
+
+
 def call_rates(cfg, reps):
     import torch
     import displaced_patch_parallelism_amd as dp
@@ -108,6 +122,7 @@ def main():
     from displaced_patch_parallelism_amd.configs import CONFIGS
     dp.lib()
     print(json.dumps(copy_rate(args.reps)), flush=True)
+    print(json.dumps(splice_ceiling(args.reps)), flush=True)
     for name in args.configs.split(","):
         for row in call_rates(CONFIGS[name], args.reps):
             print(json.dumps(row), flush=True)
