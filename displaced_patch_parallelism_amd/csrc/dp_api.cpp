@@ -366,9 +366,10 @@ struct GnConvLayout {
 
 GnConvLayout gn_conv_layout(const dp::Geom& g, int G, int Cout, bool bf16, dp::GnPlan* gp, dp::ConvPlan* cp) {
     *gp = dp::plan_groupnorm(g, G, bf16);
-    *cp = dp::plan_conv(g, Cout, bf16);
+    *cp = dp::plan_conv(g, Cout, bf16, true);
     GnConvLayout l{};
     l.fused = dp::conv_gn_fusable(g, *cp, *gp, G, bf16);
+    if (!l.fused) *cp = dp::plan_conv(g, Cout, bf16);    // the three calls: the standalone conv's plan
     if (l.fused) {
         l.part_bytes = gp->ws_bytes;
     } else {

@@ -65,14 +65,16 @@ hipError_t launch_groupnorm(const Geom& g, const GnPlan& plan, bool bf16, int G,
 // ---- conv3x3 with stale halo -------------------------------------------
 struct ConvPlan {
     int kind;       // 0 = f32 direct, 1 = bf16 shared-ring 128x160 tiles, 2 = bf16 wave-split 64x80
-                    // tiles, 3 = bf16 shared-ring 256x160 tiles
+                    // tiles, 3 = bf16 shared-ring 256x160 tiles (GroupNorm folded in only)
     int bm, bn;     // output tile (pixels x output channels)
     int mtiles, ntiles;
     int ktiles;     // K stages: 32 input channels of one kernel row each (3 * Cin / 32)
     int ksplit;     // K partitions (>1: fp32 partials + ordered reduction)
     size_t ws_bytes;
 };
-ConvPlan plan_conv(const Geom& g, int Cout, bool bf16);
+// gn_fused: plan for the conv with a GroupNorm folded into its A operand (the only user of the
+// 256x160 tiles); else the standalone conv.
+ConvPlan plan_conv(const Geom& g, int Cout, bool bf16, bool gn_fused = false);
 // res: optional residual [B][h][W][Cout] added before the output is rounded.
 hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout, const void* x_patch,
                        const void* x_stale, const void* w, bool w_packed, const float* bias, const void* res,

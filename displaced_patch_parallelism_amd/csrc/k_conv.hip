@@ -264,8 +264,8 @@ __device__ __forceinline__ void tile_origin(const ConvArgs& a, int mt, int& bb, 
 // stage publishes it.  The stage's loads are dealt round-robin to the waves.
 //   TR = 4: 4 waves, 2 x 38.5 KB, two workgroups per CU (one's waits overlap the other's MFMAs).
 //   TR = 8: 8 waves, 3 x 47 KB, one workgroup per CU: the 160 channels' weights of a stage serve
-//           256 pixels instead of 128 (fewer bytes per MFMA from L2), and two stages load while
-//           one is multiplied.
+//           256 pixels instead of 128, and two stages load while one is multiplied; the
+//           GroupNorm-folding conv's tile (its lanes and parameter table take the LDS left over).
 // ---------------------------------------------------------------------------
 // Fused GroupNorm: which kernel rows ky = 0..2 read slot s of a stage from the fresh band (bit ky
 // of the mask), and, for a fresh pixel of the tile's own columns in its own rows (kernel row 1)
@@ -632,11 +632,6 @@ __global__ __launch_bounds__(256, 2) void conv3x3_bf16_halo_tile_kernel(ConvArgs
     conv_tile_body<4, 2, false>(a, smem);
 }
 
-__global__ __launch_bounds__(512, 1) void conv3x3_bf16_halo_tile8_kernel(ConvArgs a) {
-    __shared__ __attribute__((aligned(1024))) char smem[tile_smem<8, 3>()];
-    conv_tile_body<8, 3, false>(a, smem);
-}
-
 // The 256x160-tile conv whose A operand's fresh pixels are the raw GroupNorm input, normalised
 // (+ SiLU) on the fly: GroupNorm-apply fused into the conv (the statistics pass runs before it).
 // Halo rows come from the conv's stale map, already normalised by the previous step; zero padding
@@ -931,7 +926,7 @@ __global__ __launch_bounds__(256) void conv_pack_weights_kernel(const uint4* __r
     wp[o] = w[i];
 }
 
-ConvPlan plan_conv(const Geom& g, int Cout, bool bf16) {
+ConvPlan plan_conv(const Geom& g, int Cout, bool bf16, bool gn_fused) {
     ConvPlan p{};
     if (!bf16) {
         p.kind = 0;
@@ -942,9 +937,12 @@ ConvPlan plan_conv(const Geom& g, int Cout, bool bf16) {
     p.ktiles = 3 * g.C / 32;          // K stages (cc, ky)
     int ks = 1;
     const int64_t big8 = (int64_t)g.B * ((g.h + 7) / 8) * ntx * ((Cout + 159) / 160);
-    if (big >= 384 && (big8 + 255) / 256 <= (big + 511) / 512) {
+    if (gn_fused && big >= 384 && (big8 + 255) / 256 <= (big + 511) / 512) {
         // 256x160 tiles, one per CU, in no more rounds than the 128x160 tiles need at two per
-        // CU (a round of either moves the same output; the larger tile reads fewer bytes)
+        // CU: the tile the folded GroupNorm needs (its lanes and parameter table share the
+        // workgroup's LDS).  Without a GroupNorm folded in, two 128x160 workgroups per CU
+        // measured 2-5 % faster at every size tried (one workgroup's MFMAs fill the other's
+        // barrier waits; same sums in the same order, so the outputs are bitwise equal).
         p.kind = 3;
         p.bm = 256;
         p.bn = 160;
@@ -1039,9 +1037,8 @@ hipError_t launch_conv(const Geom& g, const ConvPlan& plan, bool bf16, int Cout,
     const int64_t total4 = (int64_t)a.M * Cout / 4;
     if (!grid_fits(nwg) || (plan.ksplit > 1 && !grid_fits((total4 + 255) / 256))) return hipErrorInvalidConfiguration;
     const unsigned grid = (unsigned)nwg;
-    if (plan.kind == 3)
-        conv3x3_bf16_halo_tile8_kernel<<<grid, 512, 0, stream>>>(a);
-    else if (plan.kind == 1)
+    if (plan.kind == 3) return hipErrorInvalidValue;     // only with a GroupNorm folded in
+    if (plan.kind == 1)
         conv3x3_bf16_halo_tile_kernel<<<grid, kThreads, 0, stream>>>(a);
     else
         conv3x3_bf16_halo_wave8_kernel<<<grid, 512, 0, stream>>>(a);

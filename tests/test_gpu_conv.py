@@ -88,7 +88,7 @@ def test_config_shapes(shape, seed):
     (1, 32, 64, 128, 128, 4, "conv3x3_bf16_halo_wave8_kernel"),     # 64x80 tiles, K split
     (1, 128, 128, 320, 320, 4, "conv3x3_bf16_halo_wave8_kernel"),   # the c1r ResNet block's shape
     (2, 24, 1152, 64, 320, 2, "conv3x3_bf16_halo_tile_kernel"),      # 128x160 tiles
-    (1, 124, 500, 64, 288, 2, "conv3x3_bf16_halo_tile8_kernel"),     # 256x160 tiles, N tail
+    (1, 124, 500, 64, 288, 2, "conv3x3_bf16_halo_tile_kernel"),      # 128x160 tiles, ragged rows, N tail
 ])
 def test_residual_bf16(B, H, W, cin, cout, P, kernel):
     """The skip connection is added before rounding in every kernel's epilogue (and in the
@@ -118,11 +118,10 @@ def test_ragged_bf16(B, H, W, cin, cout, P):
 
 
 @pytest.mark.parametrize("B,H,W,cin,cout,P", [
-    # 256x160 tiles (8 rows): 62 = 7*8 + 6 rows, 500 = 15*32 + 20 columns, 288 = 160 + 128
+    # 128x160 tiles (4 rows): 62 = 15*4 + 2 rows, 500 = 15*32 + 20 columns, 288 = 160 + 128
     (1, 124, 500, 64, 288, 2),
-    (2, 96, 254, 64, 320, 2),   # 256x160 tiles over two batch images, ragged columns
-    # 128x160 tiles (4 rows): 12-row bands need a second round of 8-row tiles
-    (2, 24, 1152, 64, 320, 2),
+    (2, 96, 254, 64, 320, 2),   # over two batch images, ragged columns
+    (2, 24, 1152, 64, 320, 2),  # 12-row bands, 36 column tiles
 ])
 def test_large_map_tiles_bf16(B, H, W, cin, cout, P):
     for i in range(P):
@@ -140,7 +139,7 @@ def test_f32(B, H, W, cin, cout, P):
 ONEHOT_SHAPES = [
     # (B, H, W, C, P, dtype, kernel the plan picks)
     (1, 8, 9, 64, 4, "bf16", "conv3x3_bf16_halo_wave8_kernel"),
-    (1, 240, 480, 64, 2, "bf16", "conv3x3_bf16_halo_tile8_kernel"),
+    (1, 240, 480, 64, 2, "bf16", "conv3x3_bf16_halo_tile_kernel"),
     (2, 24, 1152, 320, 2, "bf16", "conv3x3_bf16_halo_tile_kernel"),
     (1, 8, 9, 8, 4, "f32", "conv3x3_f32_direct_kernel"),
 ]
@@ -150,7 +149,9 @@ ONEHOT_SHAPES = [
 def test_onehot_halo_indexing_bit_exact(B, H, W, C, P, dtype, kernel):
     """One-hot weights copy one tap: fresh values are negative, stale positive, so
     the output names which buffer (or the zero padding) every source came from.  Run on
-    every kernel the plan can pick (the small-map, both large-map tile kernels, f32)."""
+    every kernel the plan can pick (the small-map and the large-map tile kernels, f32; the
+    256x160 tiles, used only with a GroupNorm folded in, are bitwise equal to the unfused
+    calls in test_gpu_gn_conv)."""
     assert conv_kernel(B, H, W, C, C, P, dtype) == kernel
     rng = np.random.default_rng(7)
     fresh = -rng.integers(1, 101, size=(B, H, W, C)).astype(np.float32)
@@ -170,8 +171,8 @@ def test_onehot_halo_indexing_bit_exact(B, H, W, C, P, dtype, kernel):
 
 @pytest.mark.parametrize("B,H,W,C,P,i,kernel", [
     (1, 64, 64, 640, 4, 1, "conv3x3_bf16_halo_wave8_kernel"),     # c2 (K split)
-    (1, 240, 480, 64, 2, 1, "conv3x3_bf16_halo_tile8_kernel"),
-    (1, 480, 480, 320, 8, 1, "conv3x3_bf16_halo_tile8_kernel"),   # c4a
+    (1, 240, 480, 64, 2, 1, "conv3x3_bf16_halo_tile_kernel"),
+    (1, 480, 480, 320, 8, 1, "conv3x3_bf16_halo_tile_kernel"),    # c4a
     (2, 24, 1152, 320, 2, 0, "conv3x3_bf16_halo_tile_kernel"),
 ])
 def test_determinism_and_stale_rows_only(B, H, W, C, P, i, kernel):
