@@ -662,7 +662,8 @@ __global__ __launch_bounds__(512) void conv3x3_bf16_halo_wave8_kernel(ConvArgs a
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave-uniform, so the wave's K range, stage indices and LDS buffer stay in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // logical order (channel tile, K split, pixel tile), pixel tile fastest
     const int lt = xcd_order(blockIdx.x, gridDim.x);
     const int mt = lt % a.mtiles;
