@@ -68,7 +68,8 @@ __global__ __launch_bounds__(256) void linear_bf16_kernel(LinArgs a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave-uniform, so each load's LDS destination is a scalar (no per-load readfirstlane)
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave & 1, wn = wave >> 1;
     // XCD-contiguous order, row tile slowest: consecutive workgroups on an XCD share W
     const int total = gridDim.x;
