@@ -506,8 +506,16 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
     if (idx >= rows * (D / 4)) return;
     const int d4 = (int)(idx % (D / 4));
     const int64_t row = idx / (D / 4);  // (bh, q)
-    const int q = (int)(row % Nq);
-    const int bh = (int)(row / Nq);
+    // 32-bit division when every row index fits (a uniform test): the 64-bit one is a long
+    // sequence ahead of the loads
+    int q, bh;
+    if (rows <= 0xffffffffLL) {
+        q = (int)((uint32_t)row % (uint32_t)Nq);
+        bh = (int)((uint32_t)row / (uint32_t)Nq);
+    } else {
+        q = (int)(row % Nq);
+        bh = (int)(row / Nq);
+    }
     float2 ml[kMaxSplit];
     float4 v[kMaxSplit];
 #pragma unroll

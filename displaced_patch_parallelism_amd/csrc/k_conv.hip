@@ -839,9 +839,10 @@ __global__ __launch_bounds__(256) void conv_splitk_reduce_kernel(const float* __
     const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i4 >= total4) return;
     const int64_t i = i4 * 4;
-    const int co = (int)(i % Cout);
-    const float4 bv = bias ? *(const float4*)(bias + co) : make_float4(0.f, 0.f, 0.f, 0.f);
     float4 s = *(const float4*)(part + i);
+    // 32-bit division when every element index fits (a uniform test)
+    const int co = total4 <= 0x3fffffffLL ? (int)((uint32_t)i % (uint32_t)Cout) : (int)(i % Cout);
+    const float4 bv = bias ? *(const float4*)(bias + co) : make_float4(0.f, 0.f, 0.f, 0.f);
     for (int k0 = 1; k0 < ksplit; k0 += 8) {
         float4 v[8];
 #pragma unroll
